@@ -1,0 +1,154 @@
+/*
+ * attn.h -- C ABI of the guarded BF16 FlashAttention library (gfx950).
+ *
+ * The operation is softmax attention O = softmax(alpha * Q K^T) V computed
+ * tile by tile with an online softmax and an unnormalised accumulator
+ * Ō = P̄ V, and its gradient, with the repeated-row-maximum guard of
+ *   [R] "BF16 플래시 어텐션은 왜 수천 스텝 뒤에 무너질까" (priors.kr review of
+ *       Qiu & Yao, "Why Low-Precision Transformer Training Fails: An Analysis
+ *       on Flash Attention"), and
+ *   [S] "Why Low-Precision Transformer Training Fails: An Analysis on Flash
+ *       Attention" (bud-325.pages.dev summary).
+ * Each entry point below names the passage that defines it.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major [batch][heads][seqlen][head_dim] with
+ *     head_dim contiguous; Q, O, dO, dQ have heads_q heads, K, V, dK, dV have
+ *     heads_kv heads.  Per-row vectors are [batch][heads_q][seqlen].
+ *   - Every pointer is a device pointer owned by the caller; the library
+ *     neither allocates nor frees, keeps no state between calls, never
+ *     synchronises and never prints.  Tensor pointers must be 16-byte
+ *     aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously; a device fault surfaces at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated before anything is enqueued: a bad argument
+ *     returns a negative ATTN_E_* code and enqueues nothing.
+ *   - Calls on different streams with disjoint outputs may run concurrently.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* attn_params.flags */
+#define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
+#define ATTN_GUARD_NONE 0x0u      /* shift m = row max r (plain online softmax) */
+#define ATTN_GUARD_BETA 0x2u      /* tie rows: m = beta*r if r > 0, else 0      */
+#define ATTN_GUARD_EPS 0x4u       /* tie rows: m = r + shift_eps                */
+#define ATTN_GUARD_MASK 0x6u
+#define ATTN_OBAR_FP32 0x8u       /* keep Ō in fp32 (default: bf16 per block)   */
+
+/* per-row flag bits written by attn_fwd */
+#define ATTN_ROW_TIE 0x1u           /* the row maximum recurs within tie_eps   */
+#define ATTN_ROW_ZERO_DENOM 0x2u    /* ℓ == 0 (every P̄ underflowed): O is NaN */
+#define ATTN_ROW_GUARD_APPLIED 0x4u /* a guarded shift was used for the row    */
+
+/* return codes */
+#define ATTN_OK 0
+#define ATTN_E_NULL (-1)        /* a required pointer is NULL                   */
+#define ATTN_E_SHAPE (-2)       /* non-positive size, heads_q % heads_kv != 0   */
+#define ATTN_E_UNSUPPORTED (-3) /* head_dim not 64/128, misaligned pointer      */
+#define ATTN_E_PARAM (-4)       /* bad beta/tie_eps/shift_eps/flags/scale       */
+#define ATTN_E_WORKSPACE (-5)   /* workspace missing or too small               */
+#define ATTN_E_HIP (-6)         /* the HIP runtime refused a launch             */
+
+typedef struct {
+  int32_t batch;     /* > 0                                                  */
+  int32_t heads_q;   /* > 0, multiple of heads_kv (grouped-query attention)  */
+  int32_t heads_kv;  /* > 0; query head h reads KV head h / (heads_q/heads_kv) */
+  int32_t seqlen;    /* > 0; queries and keys have the same length           */
+  int32_t head_dim;  /* 64 or 128                                            */
+  float softmax_scale; /* alpha; <= 0 selects fl32(1/sqrt(head_dim))          */
+  float beta;        /* beta-guard multiplier, > 1 (the pages use 2..8)      */
+  float tie_eps;     /* tie window, >= 0: tie iff fl32(r - r2) <= tie_eps    */
+  float shift_eps;   /* eps-guard extra shift, > 0 (the pages use 2^-5)      */
+  uint32_t flags;    /* ATTN_CAUSAL | one ATTN_GUARD_* | ATTN_OBAR_FP32      */
+} attn_params;
+
+/*
+ * attn_fwd -- guarded streaming forward.
+ * Defines: [R] "Why it matters" (tiled attention, paper §2.2) and "Core
+ * idea" equations (O = PV with P̄ = exp(S - m), paper §3.3.2); the guard:
+ * [R] "Core idea", the fix (paper §4) and [S] "Method" (Algorithm 1, one
+ * extra line in the tiling loop that detects a repeated maximum).
+ * Per query row the keys are streamed in blocks of attn_schedule()'s block_n
+ * keys.  After each block: (r, r2) = the two largest scaled logits
+ * t = fl32(alpha*s) so far; tie = fl32(r - r2) <= tie_eps; m = guard shift
+ * of r; Ō <- exp(m_old - m) Ō + sum bf16(exp(t - m)) V, accumulated in fp32
+ * and, unless ATTN_OBAR_FP32, rounded to bf16 at the end of the block;
+ * ℓ <- exp(m_old - m) ℓ + sum exp(t - m) in fp32.  Finally O = bf16(Ō/ℓ).
+ *   q [B,Hq,N,d] bf16, k/v [B,Hkv,N,d] bf16                (in)
+ *   o [B,Hq,N,d] bf16                                       (out)
+ *   row_m [B,Hq,N] fp32: the final shift m                  (out, required)
+ *   row_l [B,Hq,N] fp32: ℓ relative to row_m                (out, required)
+ *   row_flags [B,Hq,N] u8: ATTN_ROW_* bits                  (out, required)
+ *   obar_out [B,Hq,N,d]: final Ō, bf16 (or fp32 with ATTN_OBAR_FP32) (nullable)
+ *   row_max [B,Hq,N] fp32: r, the row maximum of t          (nullable)
+ * row_m and row_l are what attn_bwd needs to recompute P = exp(t - m)/ℓ.
+ */
+int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
+             void* o, float* row_m, float* row_l, uint8_t* row_flags,
+             void* obar_out, float* row_max, void* stream);
+
+/*
+ * attn_bwd -- backward of attn_fwd, the three stages below in order.
+ * Defines: [R] "Core idea", equations (paper Eq. 1-2: dS = alpha P∘(dP -
+ * delta), dQ = dS K, delta = rowsum(dO∘O)) and the summary/method sections
+ * (delta computed from the bf16 O, paper §3.2).  The guard is carried by
+ * recomputing P = exp(t - row_m) / row_l with the stored shift ([R] the fix:
+ * the backward is otherwise unchanged).
+ *   q, k, v, o (bf16), dout [B,Hq,N,d] bf16, row_m, row_l from attn_fwd (in)
+ *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d] bf16                  (out)
+ *   delta [B,Hq,N] fp32 = rowsum(dO∘O)                      (out, required)
+ *   workspace of attn_bwd_workspace_bytes(p) bytes, 256-byte aligned (scratch)
+ * dK and dV sum over the heads_q/heads_kv query heads sharing a KV head.
+ */
+size_t attn_bwd_workspace_bytes(const attn_params* p);
+int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
+             const void* o, const void* dout, const float* row_m, const float* row_l,
+             void* dq, void* dk, void* dv, float* delta, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* attn_bwd's stages, callable one by one (same arguments and rules):
+ *   attn_bwd_preprocess: delta = rowsum(dO∘O) in fp32 from the bf16 O, and
+ *     clears the fp32 dQ accumulator in the workspace
+ *     ([R] "Core idea"/method: the delta term, paper §3.2).
+ *   attn_bwd_main: per key block, recompute S and P, then dV += P^T dO,
+ *     dP = dO V^T, dS = P∘(dP - delta), dK += dS^T Q, dQ += dS K (fp32
+ *     accumulation in the workspace) ([R] "Core idea", Eq. 1-2).
+ *   attn_bwd_finalize: dQ = bf16(alpha * accumulated dQ).                 */
+int attn_bwd_preprocess(const attn_params* p, const void* o, const void* dout,
+                        float* delta, void* workspace, size_t workspace_bytes,
+                        void* stream);
+int attn_bwd_main(const attn_params* p, const void* q, const void* k, const void* v,
+                  const void* dout, const float* row_m, const float* row_l,
+                  const float* delta, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, void* stream);
+int attn_bwd_finalize(const attn_params* p, void* dq, const void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * attn_schedule -- the rounding schedule attn_fwd uses for these params, so
+ * that a reference can replay it: block_m query rows per workgroup, block_n
+ * keys per streaming step (the Ō rounding block), chunk = products per
+ * matrix instruction along each contraction.  Returns ATTN_OK or an error
+ * code for invalid params.  Pointers may be NULL.
+ */
+int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n,
+                  int32_t* chunk);
+
+const char* attn_strerror(int code);
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */

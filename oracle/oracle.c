@@ -1,0 +1,841 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU reference for guarded BF16
+ * attention.  TEST INFRASTRUCTURE ONLY (see oracle.h): never linked into, or
+ * called by, the product path.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math (oracle/build_oracle.py).  No
+ * contraction, no reassociation: every fp32 step below is one IEEE binary32
+ * operation, every fp64 step one binary64 operation.
+ *
+ * Page citations use the keys of oracle.h: [R] the priors.kr review, [S] the
+ * bud-325 summary.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_VERSION 1
+#define U24 5.9604644775390625e-08 /* 2^-24: unit roundoff of binary32 */
+
+int orc_version(void) { return ORC_VERSION; }
+
+/* ======================================================================
+ * BF16.  [R] "Why it matters" (paper §2.1): BF16 keeps FP32's 8 exponent
+ * bits and 7 mantissa bits, so values in [1,2) are spaced 1/128.
+ * [R] "Core idea", intuition (paper App. B): results are rounded to the
+ * nearest representable value, and an exact half-way case goes to the value
+ * whose last mantissa bit is even.
+ * ====================================================================== */
+
+/* Nearest bf16 to an fp32 value, written from the definition: the candidate
+ * below in magnitude is the 16-bit truncation; the discarded low half decides
+ * (more than half: away from zero; less: keep; exactly half: the even one). */
+uint16_t orc_bf16_from_f32(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+    return (uint16_t)((u >> 16) | 0x0040u); /* NaN stays NaN (quiet) */
+  uint32_t sign = u & 0x80000000u;
+  uint32_t mag = u & 0x7fffffffu;
+  uint32_t below = mag & 0xffff0000u;
+  uint32_t rest = mag & 0x0000ffffu;
+  int away;
+  if (rest > 0x8000u)
+    away = 1;
+  else if (rest < 0x8000u)
+    away = 0;
+  else
+    away = (int)((below >> 16) & 1u); /* tie: go to the even neighbour */
+  /* one step up in magnitude; a carry out of the mantissa moves to the next
+   * binade, and out of the largest finite value to infinity, as RNE requires */
+  uint32_t res = below + (away ? 0x10000u : 0u);
+  return (uint16_t)((sign | res) >> 16);
+}
+
+float orc_f32_from_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+void orc_bf16_from_f32_array(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_f32(x[i]);
+}
+
+void orc_f32_from_bf16_array(const uint16_t* h, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_from_bf16(h[i]);
+}
+
+/* Spacing of the bf16 grid in the binade of |x| (subnormal spacing below
+ * 2^-126).  bf16 has 7 stored mantissa bits, so the spacing in [2^e, 2^e+1)
+ * is 2^(e-7). */
+double orc_bf16_ulp(double x) {
+  double a = fabs(x);
+  if (a == 0.0 || !isfinite(a)) return ldexp(1.0, -133);
+  int e;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int lo = e - 1;
+  if (lo < -126) lo = -126;
+  return ldexp(1.0, lo - 7);
+}
+
+/* Direct round-to-nearest-even of a double to bf16: scale by the grid
+ * spacing (exact, a power of two), round the quotient to the nearest integer
+ * with ties to even, scale back. */
+uint16_t orc_bf16_from_f64(double x) {
+  if (isnan(x)) return (uint16_t)(signbit(x) ? 0xffc0u : 0x7fc0u);
+  if (x == 0.0) return (uint16_t)(signbit(x) ? 0x8000u : 0x0000u);
+  double a = fabs(x);
+  uint16_t sign = (uint16_t)(signbit(x) ? 0x8000u : 0u);
+  if (isinf(a)) return (uint16_t)(sign | 0x7f80u);
+  double sp = orc_bf16_ulp(a);
+  double qv = a / sp;
+  double rn = nearbyint(qv); /* default mode: nearest, ties to even */
+  double res = rn * sp;
+  if (res >= 0x1p128) return (uint16_t)(sign | 0x7f80u); /* overflow */
+  float f = (float)res; /* exact: res is on the bf16 grid */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | (u >> 16));
+}
+
+/* Distance from x to the nearest rounding boundary (half-way point between
+ * two neighbouring bf16 values).  A value whose error bound is smaller than
+ * this rounds the same way whatever the error is. */
+double orc_bf16_boundary_distance(double x) {
+  double a = fabs(x);
+  if (!isfinite(a)) return 0.0;
+  double sp = orc_bf16_ulp(a);
+  double qv = a / sp;
+  double fr = qv - floor(qv);
+  return fabs(fr - 0.5) * sp;
+}
+
+/* Error-free transformation of a + b (Knuth's TwoSum). */
+static void two_sum(double a, double b, double* s, double* e) {
+  double x = a + b;
+  double bv = x - a;
+  double av = x - bv;
+  *s = x;
+  *e = (a - av) + (b - bv);
+}
+
+/* Sum kept as an unevaluated pair hi + lo (twice double precision). */
+typedef struct {
+  double hi, lo;
+} dd_t;
+
+static void dd_add(dd_t* acc, double x) {
+  double s, e;
+  two_sum(acc->hi, x, &s, &e);
+  double lo = acc->lo + e;
+  two_sum(s, lo, &acc->hi, &acc->lo);
+}
+
+/* RNE to bf16 of hi + lo.  |lo| is below half a double ulp of hi, so it can
+ * only matter when hi sits exactly on a bf16 half-way point. */
+static uint16_t dd_to_bf16(dd_t v) {
+  if (v.lo != 0.0 && orc_bf16_boundary_distance(v.hi) == 0.0 && isfinite(v.hi)) {
+    double sp = orc_bf16_ulp(v.hi);
+    double toward = (v.lo > 0.0) ? v.hi + sp / 4 : v.hi - sp / 4;
+    return orc_bf16_from_f64(toward);
+  }
+  return orc_bf16_from_f64(v.hi);
+}
+
+/* [R] "Core idea", equations (paper §3.3.2) and [S] "Results": the
+ * unnormalised output is accumulated wider than bf16 and rounded once; the
+ * small same-sign residual survives in the accumulator and decides a
+ * half-way case.  This is that step: RNE of the exact sum. */
+uint16_t orc_bf16_round_of_sum(const double* terms, int32_t n, double* exact_out) {
+  dd_t acc = {0.0, 0.0};
+  for (int32_t i = 0; i < n; ++i) dd_add(&acc, terms[i]);
+  if (exact_out) *exact_out = acc.hi + acc.lo;
+  return dd_to_bf16(acc);
+}
+
+/* ======================================================================
+ * Shared plumbing: problem checks, head lists, a tiny thread pool.
+ * ====================================================================== */
+
+static int check_problem(const orc_problem* p) {
+  if (!p) return -1;
+  if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->seqlen <= 0 ||
+      p->head_dim <= 0)
+    return -2;
+  if (p->heads_q % p->heads_kv != 0) return -2;
+  if (p->guard < ORC_GUARD_NONE || p->guard > ORC_GUARD_EPS) return -4;
+  if (!(p->alpha > 0.0f)) return -4;
+  return 0;
+}
+
+typedef struct {
+  void (*fn)(void* ctx, int32_t item);
+  void* ctx;
+  int32_t nitems;
+  int32_t nthreads;
+  int32_t tid;
+} pool_arg;
+
+static void* pool_worker(void* a) {
+  pool_arg* pa = (pool_arg*)a;
+  for (int32_t i = pa->tid; i < pa->nitems; i += pa->nthreads) pa->fn(pa->ctx, i);
+  return NULL;
+}
+
+/* Run fn(ctx, i) for i in [0, nitems) on nthreads threads (static split). */
+static void run_pool(void (*fn)(void*, int32_t), void* ctx, int32_t nitems, int32_t nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nitems) nthreads = nitems;
+  if (nthreads <= 1) {
+    for (int32_t i = 0; i < nitems; ++i) fn(ctx, i);
+    return;
+  }
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  pool_arg* args = (pool_arg*)malloc(sizeof(pool_arg) * (size_t)nthreads);
+  for (int32_t t = 0; t < nthreads; ++t) {
+    args[t].fn = fn;
+    args[t].ctx = ctx;
+    args[t].nitems = nitems;
+    args[t].nthreads = nthreads;
+    args[t].tid = t;
+    pthread_create(&th[t], NULL, pool_worker, &args[t]);
+  }
+  for (int32_t t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(args);
+}
+
+/* Pointers to the [N][d] slabs of query head (b, h) and of its KV head.
+ * Grouped-query mapping: query head h reads KV head h / (heads_q/heads_kv). */
+static size_t q_head_offset(const orc_problem* p, int32_t qhead) {
+  return (size_t)qhead * (size_t)p->seqlen * (size_t)p->head_dim;
+}
+static size_t kv_head_offset(const orc_problem* p, int32_t qhead) {
+  int32_t b = qhead / p->heads_q, h = qhead % p->heads_q;
+  int32_t g = p->heads_q / p->heads_kv;
+  int32_t hk = h / g;
+  return ((size_t)b * (size_t)p->heads_kv + (size_t)hk) * (size_t)p->seqlen * (size_t)p->head_dim;
+}
+
+/* Keys visible to query row i. */
+static int32_t visible(const orc_problem* p, int32_t i) {
+  return p->causal ? i + 1 : p->seqlen;
+}
+
+/* s = sum_f q_f k_f in double: each product of two bf16 values is exact in
+ * double and the sum of head_dim of them stays exact for these magnitudes. */
+static double dot_bf16(const uint16_t* a, const uint16_t* b, int32_t d) {
+  double s = 0.0;
+  for (int32_t f = 0; f < d; ++f)
+    s += (double)orc_f32_from_bf16(a[f]) * (double)orc_f32_from_bf16(b[f]);
+  return s;
+}
+
+/* Error bound of a sum c0 + sum(terms) as the kernel computes it (see
+ * orc_schedule).  With chunk = 0: any order of fp32 additions.  Otherwise a
+ * chain of matrix instructions, each adding `chunk` products to the running
+ * value C.  Model of one instruction (bf16 inputs, fp32 accumulate), taken
+ * from measurements of the hardware: the products are summed in two halves,
+ * each aligned to its largest product with everything below 2^-24 of that
+ * truncated toward zero and the half-sum rounded to fp32; C is truncated the
+ * same way relative to the largest product; the three are added and the
+ * result rounded to fp32.  The bound does not need to know which products
+ * share a half: with E the exponent of the chunk's largest product, a product
+ * that is a multiple of 2^(E-24) loses nothing, any other loses less than
+ * 2^(E-24); the two half-sum roundings together cost at most u*sum|p|; C loses less than 2^(E-24) unless it is on that grid or not
+ * below 2^(E+1); the final rounding costs at most u*|result|.  chunk_err
+ * scales the whole bound (a safety factor over the measured model).        */
+static double chain_bound(const orc_schedule* sc, double c0, const double* terms, int32_t n) {
+  if (!sc || sc->chunk <= 0) {
+    double a = fabs(c0);
+    for (int32_t i = 0; i < n; ++i) a += fabs(terms[i]);
+    return (double)(n + 1) * U24 * a;
+  }
+  double err = 0.0, c = c0;
+  double factor = sc->chunk_err > 0 ? sc->chunk_err : 1.0;
+  for (int32_t i0 = 0; i0 < n; i0 += sc->chunk) {
+    int32_t i1 = i0 + sc->chunk < n ? i0 + sc->chunk : n;
+    double sa = 0.0, r = c, mx = 0.0;
+    for (int32_t i = i0; i < i1; ++i) {
+      sa += fabs(terms[i]);
+      r += terms[i];
+      if (fabs(terms[i]) > mx) mx = fabs(terms[i]);
+    }
+    double step = 0.0;
+    if (mx > 0.0) {
+      int e;
+      frexp(mx, &e); /* mx in [2^(e-1), 2^e) */
+      double grid = ldexp(1.0, (e - 1) - 24);
+      for (int32_t i = i0; i < i1; ++i)
+        if (fmod(terms[i], grid) != 0.0) step += grid;
+      step += U24 * sa;
+      if (fabs(c) < ldexp(1.0, e) && fmod(c, grid) != 0.0) step += grid;
+    }
+    step += U24 * fabs(r);
+    err += factor * step;
+    c = r;
+  }
+  return err;
+}
+
+/* Exact score and the bound on the kernel's fp32 score for one (i, j). */
+static double dot_with_bound(const orc_schedule* sc, const uint16_t* a, const uint16_t* b,
+                             int32_t d, double* tmp, double* bound) {
+  double s = 0.0;
+  for (int32_t f = 0; f < d; ++f) {
+    tmp[f] = (double)orc_f32_from_bf16(a[f]) * (double)orc_f32_from_bf16(b[f]);
+    s += tmp[f];
+  }
+  *bound = chain_bound(sc, 0.0, tmp, d);
+  return s;
+}
+
+/* ======================================================================
+ * FP64 reference forward: O = softmax(alpha * Q K^T) V.
+ * [R] "Core idea", equations: S = QK^T with P = softmax and O = PV; the
+ * score scale alpha = 1/sqrt(d) ([S] "Method", Eqn. 2's 1/sqrt(d)).
+ * ====================================================================== */
+
+typedef struct {
+  const orc_problem* p;
+  const uint16_t *q, *k, *v;
+  const int32_t* heads;
+  double *o, *lse;
+} fwd64_ctx;
+
+static void fwd64_head(void* c, int32_t item) {
+  fwd64_ctx* x = (fwd64_ctx*)c;
+  const orc_problem* p = x->p;
+  int32_t qh = x->heads ? x->heads[item] : item;
+  int32_t N = p->seqlen, d = p->head_dim;
+  const uint16_t* Q = x->q + q_head_offset(p, qh);
+  const uint16_t* K = x->k + kv_head_offset(p, qh);
+  const uint16_t* V = x->v + kv_head_offset(p, qh);
+  double* t = (double*)malloc(sizeof(double) * (size_t)N);
+  double alpha = (double)p->alpha;
+  for (int32_t i = 0; i < N; ++i) {
+    int32_t n = visible(p, i);
+    double mx = -INFINITY;
+    for (int32_t j = 0; j < n; ++j) {
+      t[j] = alpha * dot_bf16(Q + (size_t)i * d, K + (size_t)j * d, d);
+      if (t[j] > mx) mx = t[j];
+    }
+    double z = 0.0;
+    for (int32_t j = 0; j < n; ++j) {
+      t[j] = exp(t[j] - mx); /* now the unnormalised probability */
+      z += t[j];
+    }
+    double* orow = x->o ? x->o + q_head_offset(p, qh) + (size_t)i * d : NULL;
+    if (orow) {
+      for (int32_t f = 0; f < d; ++f) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < n; ++j) acc += t[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+        orow[f] = acc / z;
+      }
+    }
+    if (x->lse) x->lse[(size_t)qh * N + i] = mx + log(z);
+  }
+  free(t);
+}
+
+int orc_fwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, const int32_t* heads, int32_t nheads,
+                double* o, double* lse, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v) return -1;
+  fwd64_ctx c = {p, q, k, v, heads, o, lse};
+  int32_t n = heads ? nheads : p->batch * p->heads_q;
+  run_pool(fwd64_head, &c, n, nthreads);
+  return 0;
+}
+
+/* ======================================================================
+ * FP64 reference backward.
+ * [R] "Core idea", equations (paper Eq. 1-2): dS = alpha P∘(dP - delta),
+ * dQ = dS K, with delta = rowsum(dO∘O) ([R] summary and "method", paper §3.2).
+ * dP = dO V^T, dK = dS^T Q, dV = P^T dO complete the gradient of O = PV.
+ * Here dS is kept without alpha and alpha is applied in dQ and dK, which is
+ * the same product.
+ * ====================================================================== */
+
+typedef struct {
+  const orc_problem* p;
+  const uint16_t *q, *k, *v, *dout;
+  const int32_t* kv_heads;
+  double *o, *delta, *dq, *dk, *dv;
+} bwd64_ctx;
+
+static void bwd64_kvhead(void* c, int32_t item) {
+  bwd64_ctx* x = (bwd64_ctx*)c;
+  const orc_problem* p = x->p;
+  int32_t kvh = x->kv_heads ? x->kv_heads[item] : item;
+  int32_t N = p->seqlen, d = p->head_dim;
+  int32_t g = p->heads_q / p->heads_kv;
+  int32_t b = kvh / p->heads_kv, hk = kvh % p->heads_kv;
+  size_t kvoff = (size_t)kvh * (size_t)N * (size_t)d;
+  const uint16_t* K = x->k + kvoff;
+  const uint16_t* V = x->v + kvoff;
+  double* dK = x->dk ? x->dk + kvoff : NULL;
+  double* dV = x->dv ? x->dv + kvoff : NULL;
+  if (dK) memset(dK, 0, sizeof(double) * (size_t)N * d);
+  if (dV) memset(dV, 0, sizeof(double) * (size_t)N * d);
+  double* P = (double*)malloc(sizeof(double) * (size_t)N);
+  double* orow = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dqrow = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dorow = (double*)malloc(sizeof(double) * (size_t)d);
+  double alpha = (double)p->alpha;
+  for (int32_t hh = 0; hh < g; ++hh) {
+    int32_t qh = b * p->heads_q + hk * g + hh;
+    const uint16_t* Q = x->q + q_head_offset(p, qh);
+    const uint16_t* dO = x->dout + q_head_offset(p, qh);
+    for (int32_t i = 0; i < N; ++i) {
+      int32_t n = visible(p, i);
+      const uint16_t* qi = Q + (size_t)i * d;
+      double mx = -INFINITY;
+      for (int32_t j = 0; j < n; ++j) {
+        P[j] = alpha * dot_bf16(qi, K + (size_t)j * d, d);
+        if (P[j] > mx) mx = P[j];
+      }
+      double z = 0.0;
+      for (int32_t j = 0; j < n; ++j) {
+        P[j] = exp(P[j] - mx);
+        z += P[j];
+      }
+      for (int32_t j = 0; j < n; ++j) P[j] /= z;
+      for (int32_t f = 0; f < d; ++f) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < n; ++j) acc += P[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+        orow[f] = acc;
+        dorow[f] = (double)orc_f32_from_bf16(dO[(size_t)i * d + f]);
+      }
+      double delta = 0.0;
+      for (int32_t f = 0; f < d; ++f) delta += dorow[f] * orow[f];
+      memset(dqrow, 0, sizeof(double) * (size_t)d);
+      for (int32_t j = 0; j < n; ++j) {
+        const uint16_t* kj = K + (size_t)j * d;
+        const uint16_t* vj = V + (size_t)j * d;
+        double dp = 0.0;
+        for (int32_t f = 0; f < d; ++f) dp += dorow[f] * (double)orc_f32_from_bf16(vj[f]);
+        double ds = P[j] * (dp - delta);
+        for (int32_t f = 0; f < d; ++f) dqrow[f] += alpha * ds * (double)orc_f32_from_bf16(kj[f]);
+        if (dK)
+          for (int32_t f = 0; f < d; ++f)
+            dK[(size_t)j * d + f] += alpha * ds * (double)orc_f32_from_bf16(qi[f]);
+        if (dV)
+          for (int32_t f = 0; f < d; ++f) dV[(size_t)j * d + f] += P[j] * dorow[f];
+      }
+      size_t ro = q_head_offset(p, qh) + (size_t)i * d;
+      if (x->o) memcpy(x->o + ro, orow, sizeof(double) * (size_t)d);
+      if (x->dq) memcpy(x->dq + ro, dqrow, sizeof(double) * (size_t)d);
+      if (x->delta) x->delta[(size_t)qh * N + i] = delta;
+    }
+  }
+  free(P);
+  free(orow);
+  free(dqrow);
+  free(dorow);
+}
+
+int orc_bwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, const uint16_t* dout, const int32_t* kv_heads,
+                int32_t nkv, double* o, double* delta, double* dq, double* dk,
+                double* dv, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout) return -1;
+  bwd64_ctx c = {p, q, k, v, dout, kv_heads, o, delta, dq, dk, dv};
+  int32_t n = kv_heads ? nkv : p->batch * p->heads_kv;
+  run_pool(bwd64_kvhead, &c, n, nthreads);
+  return 0;
+}
+
+/* ======================================================================
+ * The repeated-maximum guard.
+ * [R] "Core idea", the fix (paper §4): a row whose maximum r recurs (within
+ * the tie window) takes the shift m = beta*r when r > 0 and m = 0 otherwise;
+ * every other row takes m = r.  r = 0 is not covered by the page's two cases;
+ * it is read as the "otherwise" branch (m = 0).
+ * [S] "Key claims" / "Method" (Algorithm 1): the variant that subtracts an
+ * extra eps = 2^-5 from the shift of such rows, m = r + eps.
+ * ====================================================================== */
+
+static float guard_shift(const orc_problem* p, float r, int tie) {
+  if (!tie || p->guard == ORC_GUARD_NONE) return r;
+  if (p->guard == ORC_GUARD_BETA) return (r > 0.0f) ? p->beta * r : 0.0f;
+  return r + p->shift_eps;
+}
+
+/* Tie test on the running top two: count >= 2 within the window <=>
+ * r2 >= r - eps, decided as fl32(r - r2) <= eps. */
+static int tie_test(const orc_problem* p, float r, float r2) {
+  if (r2 == -INFINITY) return 0;
+  return (r - r2) <= p->tie_eps;
+}
+
+/* Fp32 scaled logit of the definition: t = fl32(alpha * fl32(s)). */
+static float scaled_logit(const orc_problem* p, double s) {
+  float sf = (float)s;
+  return p->alpha * sf;
+}
+
+/* ======================================================================
+ * Row statistics (r, r2, tie flag, final m) with certification.
+ * The kernel's scaled logits differ from the oracle's by at most delta_j per
+ * key; the maximum and the second maximum of a set move by at most the
+ * largest such delta, so the tie decision is certain when
+ * |fl32(r - r2) - eps| exceeds twice that plus the rounding of t itself.
+ * ====================================================================== */
+
+typedef struct {
+  const orc_problem* p;
+  const orc_schedule* s;
+  const uint16_t *q, *k;
+  const int32_t* heads;
+  float *r, *r2, *m;
+  uint8_t *flags, *cert;
+} stats_ctx;
+
+/* Bound on |t_kernel - t| for one key: alpha times the score bound, plus the
+ * fp32 roundings of s and of alpha*s on either side. */
+static double logit_error(const orc_problem* p, double sv, double sbound) {
+  double a = (double)p->alpha;
+  return a * sbound + 3.0 * U24 * fabs(a * sv);
+}
+
+static int tie_certain(const orc_problem* p, float r, float r2, double dmax) {
+  if (r2 == -INFINITY) return 1;
+  double gap = (double)(r - r2) - (double)p->tie_eps;
+  double margin = 2.0 * dmax + 2.0 * U24 * (fabs((double)r) + fabs((double)r2));
+  return fabs(gap) > margin;
+}
+
+static void stats_head(void* c, int32_t item) {
+  stats_ctx* x = (stats_ctx*)c;
+  const orc_problem* p = x->p;
+  int32_t qh = x->heads ? x->heads[item] : item;
+  int32_t N = p->seqlen, d = p->head_dim;
+  const uint16_t* Q = x->q + q_head_offset(p, qh);
+  const uint16_t* K = x->k + kv_head_offset(p, qh);
+  double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int32_t i = 0; i < N; ++i) {
+    int32_t n = visible(p, i);
+    float r = -INFINITY, r2 = -INFINITY;
+    double dmax = 0.0;
+    for (int32_t j = 0; j < n; ++j) {
+      double sb;
+      double sv = dot_with_bound(x->s, Q + (size_t)i * d, K + (size_t)j * d, d, tmp, &sb);
+      float t = scaled_logit(p, sv);
+      if (t > r) {
+        r2 = r;
+        r = t;
+      } else if (t > r2) {
+        r2 = t;
+      }
+      double e = logit_error(p, sv, sb);
+      if (e > dmax) dmax = e;
+    }
+    int tie = tie_test(p, r, r2);
+    size_t ro = (size_t)qh * N + i;
+    if (x->r) x->r[ro] = r;
+    if (x->r2) x->r2[ro] = r2;
+    if (x->m) x->m[ro] = guard_shift(p, r, tie);
+    if (x->flags)
+      x->flags[ro] = (uint8_t)((tie ? ORC_ROW_TIE : 0) |
+                               ((tie && p->guard != ORC_GUARD_NONE) ? ORC_ROW_GUARD_APPLIED : 0));
+    if (x->cert) x->cert[ro] = (uint8_t)tie_certain(p, r, r2, dmax);
+  }
+  free(tmp);
+}
+
+int orc_row_stats(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
+                  const uint16_t* k, const int32_t* heads, int32_t nheads,
+                  float* r, float* r2, float* m, uint8_t* flags,
+                  uint8_t* flag_cert, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k) return -1;
+  stats_ctx c = {p, s, q, k, heads, r, r2, m, flags, flag_cert};
+  int32_t n = heads ? nheads : p->batch * p->heads_q;
+  run_pool(stats_head, &c, n, nthreads);
+  return 0;
+}
+
+/* ======================================================================
+ * Unnormalised output for a given shift, in double (signed-error metric).
+ * ====================================================================== */
+
+typedef struct {
+  const orc_problem* p;
+  const uint16_t *q, *k, *v;
+  const float* m;
+  const int32_t* heads;
+  double *obar, *l;
+} obar_ctx;
+
+static void obar_head(void* c, int32_t item) {
+  obar_ctx* x = (obar_ctx*)c;
+  const orc_problem* p = x->p;
+  int32_t qh = x->heads ? x->heads[item] : item;
+  int32_t N = p->seqlen, d = p->head_dim;
+  const uint16_t* Q = x->q + q_head_offset(p, qh);
+  const uint16_t* K = x->k + kv_head_offset(p, qh);
+  const uint16_t* V = x->v + kv_head_offset(p, qh);
+  double* e = (double*)malloc(sizeof(double) * (size_t)N);
+  double alpha = (double)p->alpha;
+  for (int32_t i = 0; i < N; ++i) {
+    int32_t n = visible(p, i);
+    size_t ro = (size_t)qh * N + i;
+    double mi = (double)x->m[ro];
+    double l = 0.0;
+    for (int32_t j = 0; j < n; ++j) {
+      e[j] = exp(alpha * dot_bf16(Q + (size_t)i * d, K + (size_t)j * d, d) - mi);
+      l += e[j];
+    }
+    if (x->obar)
+      for (int32_t f = 0; f < d; ++f) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < n; ++j) acc += e[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+        x->obar[ro * d + f] = acc;
+      }
+    if (x->l) x->l[ro] = l;
+  }
+  free(e);
+}
+
+int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                 const uint16_t* v, const float* m, const int32_t* heads,
+                 int32_t nheads, double* obar, double* l, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !m) return -1;
+  obar_ctx c = {p, q, k, v, m, heads, obar, l};
+  int32_t n = heads ? nheads : p->batch * p->heads_q;
+  run_pool(obar_head, &c, n, nthreads);
+  return 0;
+}
+
+/* ======================================================================
+ * Streaming BF16 emulation of the guarded forward.
+ *
+ * The steps follow the FlashAttention-2 tiling the pages analyse ([R] "Why
+ * it matters", paper §2.2; "Points to doubt": the analysed implementation
+ * keeps P̄V in bf16) with the guard placed inside the tile loop ([S]
+ * "Method": one extra line in the standard tiling that detects a repeated
+ * maximum as the row is streamed).  For each key block of the schedule:
+ *   1. merge the block's scaled logits into the running (r, r2);
+ *   2. decide the tie and the shift m (guard_shift);
+ *   3. rescale by c = exp(m_old - m) and add P̄ = exp(t - m), with P̄ rounded
+ *      to bf16 as a matrix-core operand: Ō <- c Ō + sum P̄_bf16 V,
+ *      accumulated in fp32; in bf16 mode Ō is then rounded to bf16
+ *      ([R] "Core idea", equations: the sum lives in a wider accumulator and
+ *      is rounded once, which is what the worked addition shows);
+ *   4. ℓ <- c ℓ + sum P̄ in fp32.
+ * At the end O = RNE_bf16(Ō/ℓ).
+ *
+ * Every rounding whose input is known only up to the kernel's arithmetic
+ * error (the fp32 dot products, the hardware exp, the fp32 sums) is
+ * certified: the emulated value is declared certain only if the exact
+ * pre-rounding value lies farther from a bf16 rounding boundary than that
+ * error bound.  An uncertain step makes the rest of the row uncertain.
+ * ====================================================================== */
+
+typedef struct {
+  const orc_problem* p;
+  const orc_schedule* s;
+  const uint16_t *q, *k, *v;
+  const int32_t* heads;
+  double *obar, *o;
+  uint8_t* obar_cert;
+  float *m, *l;
+  uint8_t *flags, *flag_cert, *ex;
+} emu_ctx;
+
+static void emu_head(void* c, int32_t item) {
+  emu_ctx* x = (emu_ctx*)c;
+  const orc_problem* p = x->p;
+  const orc_schedule* sc = x->s;
+  int32_t qh = x->heads ? x->heads[item] : item;
+  int32_t N = p->seqlen, d = p->head_dim;
+  int32_t bn = sc->block_n > 0 ? sc->block_n : N;
+  const uint16_t* Q = x->q + q_head_offset(p, qh);
+  const uint16_t* K = x->k + kv_head_offset(p, qh);
+  const uint16_t* V = x->v + kv_head_offset(p, qh);
+  const double alpha = (double)p->alpha;
+  const double log2e = 1.4426950408889634;
+  const double exp_err = sc->exp_rel_err > 0 ? sc->exp_rel_err : 4.0 * U24;
+  /* smallest nonzero result of the kernel's exp */
+  const double under = sc->ftz ? 0x1p-126 : 0x1p-149;
+
+  double* sv = (double*)malloc(sizeof(double) * (size_t)N);  /* exact scores  */
+  double* sb = (double*)malloc(sizeof(double) * (size_t)N);  /* their bounds  */
+  float* tv = (float*)malloc(sizeof(float) * (size_t)N);     /* fp32 logits   */
+  double* pb = (double*)malloc(sizeof(double) * (size_t)bn); /* bf16 P̄ values */
+  double* ob = (double*)malloc(sizeof(double) * (size_t)d);  /* running Ō     */
+  double* obb = (double*)malloc(sizeof(double) * (size_t)d); /* bound on cŌ   */
+  double* terms = (double*)malloc(sizeof(double) * (size_t)(bn > d ? bn : d));
+  uint8_t* oc = (uint8_t*)malloc((size_t)d);
+
+  for (int32_t i = 0; i < N; ++i) {
+    int32_t n = visible(p, i);
+    const uint16_t* qi = Q + (size_t)i * d;
+    for (int32_t j = 0; j < n; ++j) {
+      sv[j] = dot_with_bound(sc, qi, K + (size_t)j * d, d, terms, &sb[j]);
+      tv[j] = scaled_logit(p, sv[j]);
+    }
+    float r = -INFINITY, r2 = -INFINITY, m = 0.0f, l32 = 0.0f;
+    int have_m = 0, row_cert = 1, tie = 0, zero_ambig = 0;
+    uint8_t exb = 0;
+    double dmax = 0.0;
+    for (int32_t f = 0; f < d; ++f) {
+      ob[f] = 0.0;
+      oc[f] = 1;
+    }
+    for (int32_t j0 = 0; j0 < n; j0 += bn) {
+      int32_t j1 = j0 + bn < n ? j0 + bn : n;
+      int32_t nt = j1 - j0;
+      /* 1. running top two of the scaled logits */
+      for (int32_t j = j0; j < j1; ++j) {
+        float t = tv[j];
+        if (t > r) {
+          r2 = r;
+          r = t;
+        } else if (t > r2) {
+          r2 = t;
+        }
+        double e = logit_error(p, sv[j], sb[j]);
+        if (e > dmax) dmax = e;
+      }
+      /* 2. tie decision and shift for this block */
+      tie = tie_test(p, r, r2);
+      if (!tie_certain(p, r, r2, dmax)) row_cert = 0;
+      float mn = guard_shift(p, r, tie);
+      if (tie && p->guard == ORC_GUARD_BETA && r == 0.0f) exb |= ORC_EX_ZERO_MAX_TIE;
+      /* 3a. rescale the running sums by c = exp(m_old - m_new) */
+      if (have_m && mn != m) {
+        if (mn < m) exb |= ORC_EX_SHIFT_DECREASED;
+        double cexact = exp((double)m - (double)mn);
+        float c32 = (float)cexact;
+        if (isinf(c32)) exb |= ORC_EX_RESCALE_OVERFLOW;
+        /* kernel: c = exp2(fl32(fl32(m_old - m_new) * log2e)), then fl32(c * Ō) */
+        double dm2 = fabs((double)m - (double)mn) * log2e;
+        double rho_c = log(2.0) * (2.0 * U24 * dm2) + exp_err;
+        for (int32_t f = 0; f < d; ++f) {
+          ob[f] = cexact * ob[f];
+          obb[f] = fabs(ob[f]) * (rho_c + U24);
+        }
+        l32 = c32 * l32;
+      } else {
+        for (int32_t f = 0; f < d; ++f) obb[f] = 0.0;
+      }
+      m = mn;
+      have_m = 1;
+      /* 3b. P̄ = exp(t - m), rounded to bf16 as the matrix operand */
+      double flush_slack = 0.0; /* total size of P̄ that may flush to zero */
+      for (int32_t j = j0; j < j1; ++j) {
+        double xe = alpha * sv[j] - (double)m;
+        double pbar = exp(xe);
+        /* kernel: P̄ = exp2(fma(s, fl32(alpha log2e), -fl32(m log2e))) */
+        double x2 = xe * log2e;
+        double err_x2 = log2e * alpha * sb[j] * (1.0 + U24) +
+                        U24 * (fabs(alpha * sv[j] * log2e) + fabs((double)m * log2e) + fabs(x2));
+        double rho = log(2.0) * err_x2 + exp_err;
+        double pbv;
+        if (pbar <= under * (1.0 + 4.0 * rho)) {
+          /* at or below the flush threshold: the kernel gives 0 or a tiny
+           * value; take 0 and count the whole size as uncertainty */
+          pbv = 0.0;
+          if (pbar >= under * (1.0 - 4.0 * rho)) zero_ambig = 1;
+          flush_slack += 2.0 * pbar;
+        } else {
+          pbv = (double)orc_f32_from_bf16(orc_bf16_from_f64(pbar));
+          if (orc_bf16_boundary_distance(pbar) <= (rho + 2.0 * U24) * pbar) row_cert = 0;
+        }
+        if (pbv == 1.0) {
+          if (tie) exb |= ORC_EX_PBAR_ONE_TIED;
+          if (!tie) exb |= ORC_EX_PBAR_ONE_PRE_TIE;
+        }
+        pb[j - j0] = pbv;
+        /* 4. fp32 denominator: sum of the fp32 P̄ (sequential order here) */
+        float p32 = (pbar < under) ? 0.0f : (float)pbar;
+        l32 = l32 + p32;
+      }
+      /* 3c. Ō <- cŌ + sum P̄_bf16 V, one rounding per block in bf16 mode */
+      for (int32_t f = 0; f < d; ++f) {
+        double vmax = 0.0;
+        for (int32_t j = j0; j < j1; ++j) {
+          double vv = (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+          terms[j - j0] = pb[j - j0] * vv; /* exact: 8-bit x 8-bit mantissas */
+          vmax = fmax(vmax, fabs(vv));
+        }
+        double exact;
+        double c0 = ob[f];
+        double bound = obb[f] + chain_bound(sc, c0, terms, nt) + flush_slack * vmax;
+        /* RNE of the exact c0 + sum(terms) */
+        uint16_t hb;
+        {
+          dd_t acc = {0.0, 0.0};
+          dd_add(&acc, c0);
+          for (int32_t j = 0; j < nt; ++j) dd_add(&acc, terms[j]);
+          exact = acc.hi + acc.lo;
+          hb = dd_to_bf16(acc);
+        }
+        if (sc->obar_fp32) {
+          ob[f] = exact;
+          oc[f] = 0; /* no bit claim in fp32 mode */
+        } else {
+          ob[f] = (double)orc_f32_from_bf16(hb);
+          if (!row_cert || orc_bf16_boundary_distance(exact) <= bound) oc[f] = 0;
+        }
+      }
+    }
+    /* end of row: flags and O = RNE_bf16(fl32(Ō / ℓ)) */
+    size_t ro = (size_t)qh * N + i;
+    uint8_t fl = 0;
+    if (tie) fl |= ORC_ROW_TIE;
+    if (tie && p->guard != ORC_GUARD_NONE) fl |= ORC_ROW_GUARD_APPLIED;
+    if (l32 == 0.0f) fl |= ORC_ROW_ZERO_DENOM;
+    if (x->flags) x->flags[ro] = fl;
+    if (x->flag_cert) x->flag_cert[ro] = (uint8_t)(row_cert && !zero_ambig);
+    if (x->ex) x->ex[ro] = exb;
+    if (x->m) x->m[ro] = m;
+    if (x->l) x->l[ro] = l32;
+    for (int32_t f = 0; f < d; ++f) {
+      size_t eo = ro * (size_t)d + f;
+      if (x->obar) x->obar[eo] = ob[f];
+      if (x->obar_cert) x->obar_cert[eo] = oc[f];
+      if (x->o) {
+        float q32 = (float)ob[f] / l32;
+        x->o[eo] = (double)orc_f32_from_bf16(orc_bf16_from_f32(q32));
+      }
+    }
+  }
+  free(sv);
+  free(sb);
+  free(tv);
+  free(pb);
+  free(ob);
+  free(obb);
+  free(terms);
+  free(oc);
+}
+
+int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
+                const uint16_t* k, const uint16_t* v, const int32_t* heads,
+                int32_t nheads, double* obar, uint8_t* obar_cert, double* o,
+                float* m, float* l, uint8_t* flags, uint8_t* flag_cert,
+                uint8_t* ex, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!s || !q || !k || !v) return -1;
+  if (s->block_n < 0) return -4;
+  emu_ctx c = {p, s, q, k, v, heads, obar, o, obar_cert, m, l, flags, flag_cert, ex};
+  int32_t n = heads ? nheads : p->batch * p->heads_q;
+  run_pool(emu_head, &c, n, nthreads);
+  return 0;
+}

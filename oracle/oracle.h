@@ -1,0 +1,133 @@
+/*
+ * oracle.h -- plain, slow, CPU-only reference for guarded BF16 attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this library: only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark load it.  It shares no code, header, table or helper with
+ * the HIP library; the two meet only in the tests.
+ *
+ * Sources (cited by title and section; the pages are prior art, not code):
+ *   [R] "BF16 플래시 어텐션은 왜 수천 스텝 뒤에 무너질까" -- priors.kr review of
+ *       Qiu & Yao, "Why Low-Precision Transformer Training Fails: An Analysis
+ *       on Flash Attention" (ICLR 2026).  Sections used: "Why it matters"
+ *       (BF16 format, paper §2.1-2.2), "Core idea" -> intuition / method /
+ *       equations (paper §3.2, §3.3.2, Eq. 1-3), the fix (paper §4, App. C),
+ *       "Points to doubt" (public PyTorch-ops implementation, App. G) and the
+ *       comprehension quiz.
+ *   [S] "Why Low-Precision Transformer Training Fails: An Analysis on Flash
+ *       Attention" -- bud-325.pages.dev summary.  Sections used: "Key claims",
+ *       "Method" (Algorithm 1), "Results" (second addition trace).
+ *
+ * All tensors are row-major [batch][heads][seqlen][head_dim] with head_dim
+ * contiguous.  bf16 values are passed as their 16-bit patterns.  Every entry
+ * point returns 0 on success and a negative number on a bad argument.
+ */
+#ifndef ORACLE_H
+#define ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_GUARD_NONE = 0, ORC_GUARD_BETA = 1, ORC_GUARD_EPS = 2 };
+enum { ORC_ROW_TIE = 1, ORC_ROW_ZERO_DENOM = 2, ORC_ROW_GUARD_APPLIED = 4 };
+/* per-row exception bits reported by the emulation (not part of the method) */
+enum {
+  ORC_EX_PBAR_ONE_TIED = 1,   /* bf16(P̄) == 1 in a block that saw the tie  */
+  ORC_EX_ZERO_MAX_TIE = 2,     /* tie row with r == 0: m = 0 and P̄_max = 1     */
+  ORC_EX_SHIFT_DECREASED = 4,  /* running tie broken later: m went down         */
+  ORC_EX_RESCALE_OVERFLOW = 8, /* exp(m_old - m_new) overflowed fp32            */
+  ORC_EX_PBAR_ONE_PRE_TIE = 16 /* P̄ == 1 at a first occurrence, before the tie  */
+};
+
+typedef struct {
+  int32_t batch, heads_q, heads_kv, seqlen, head_dim;
+  int32_t causal;     /* 1: key j visible to query i iff j <= i (top-left)    */
+  int32_t guard;      /* ORC_GUARD_*                                           */
+  float alpha;        /* softmax scale applied to QK^T, as an fp32 value       */
+  float beta;         /* beta-guard multiplier (> 1)                           */
+  float tie_eps;      /* tie window: repeated max iff r - r2 <= tie_eps        */
+  float shift_eps;    /* extra shift of the eps-guard                          */
+} orc_problem;
+
+/* How the kernel under test rounds; used only to decide which emulated values
+ * are certain (far enough from a rounding boundary) -- never to change them. */
+typedef struct {
+  int32_t block_n;        /* keys per streaming step = Ō rounding block       */
+  int32_t obar_fp32;      /* 0: Ō rounded to bf16 after every block; 1: fp32   */
+  int32_t ftz;            /* 1: exp results below 2^-126 flush to zero         */
+  /* Sums computed by the kernel's matrix instructions: a chain of steps, each
+   * adding `chunk` terms to the running value C, with the per-step error
+   * model of chain_bound() in oracle.c scaled by chunk_err (a safety factor).
+   * chunk = 0 means "any order of fp32 additions": n*u*sum|terms|.         */
+  int32_t chunk;
+  double chunk_err;
+  double exp_rel_err;     /* bound on the relative error of the kernel's exp   */
+} orc_schedule;
+
+int orc_version(void);
+
+/* ---- BF16 (bfloat16: 8 exponent bits, 7 stored mantissa bits) ---------- */
+uint16_t orc_bf16_from_f32(float x);       /* round to nearest, ties to even */
+uint16_t orc_bf16_from_f64(double x);      /* direct RNE of a double         */
+float orc_f32_from_bf16(uint16_t h);
+void orc_bf16_from_f32_array(const float* x, uint16_t* out, int64_t n);
+void orc_f32_from_bf16_array(const uint16_t* h, float* out, int64_t n);
+double orc_bf16_ulp(double x);             /* spacing of the bf16 grid at |x| */
+double orc_bf16_boundary_distance(double x); /* |x - nearest rounding midpoint| */
+/* RNE to bf16 of the exact sum of n doubles (the accumulate-then-round step).
+ * *exact_out (nullable) receives the exact sum rounded to double.           */
+uint16_t orc_bf16_round_of_sum(const double* terms, int32_t n, double* exact_out);
+
+/* ---- FP64 reference (the plain definition) ----------------------------- */
+/* O = softmax(alpha QK^T) V in double.  lse[i] = log sum_j exp(alpha s_ij).
+ * heads: list of flattened (b*heads_q + h) query heads, or NULL for all.    */
+int orc_fwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, const int32_t* heads, int32_t nheads,
+                double* o, double* lse, int32_t nthreads);
+
+/* Backward of softmax attention in double: delta = rowsum(dO∘O),
+ * dS = P∘(dP - delta), dQ = alpha dS K, dK = alpha dS^T Q, dV = P^T dO,
+ * dK/dV summed over the query heads that share a KV head.
+ * kv_heads: list of flattened (b*heads_kv + hk), or NULL for all.  Only the
+ * query heads of the listed KV heads are written in o/delta/dq.             */
+int orc_bwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, const uint16_t* dout, const int32_t* kv_heads,
+                int32_t nkv, double* o, double* delta, double* dq, double* dk,
+                double* dv, int32_t nthreads);
+
+/* Row statistics on the fp32 scaled logits t = fl32(alpha * fl32(s)):
+ * r = max, r2 = second largest (multiset), tie flag, final shift m.
+ * flag_cert[i] = 1 when the kernel's score error (orc_schedule's model of
+ * its matrix-instruction sums) cannot change the tie decision.             */
+int orc_row_stats(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
+                  const uint16_t* k, const int32_t* heads, int32_t nheads,
+                  float* r, float* r2, float* m, uint8_t* flags,
+                  uint8_t* flag_cert, int32_t nthreads);
+
+/* Unnormalised output for a given per-row shift m, in double:
+ * obar[i,f] = sum_j exp(t_ij - m_i) v_jf and l[i] = sum_j exp(t_ij - m_i),
+ * with t the exact scaled logit alpha*s.                                    */
+int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                 const uint16_t* v, const float* m, const int32_t* heads,
+                 int32_t nheads, double* obar, double* l, int32_t nthreads);
+
+/* Tile-by-tile emulation of the guarded streaming forward with the rounding
+ * points of the schedule, plus certification of every bf16 rounding.
+ * Outputs (per query row of the listed heads, in [B,Hq,N(,d)] layout):
+ *   obar      final Ō (bf16-valued in bf16 mode), obar_cert 1 = certain
+ *   o         RNE_bf16(Ō/ℓ) as double
+ *   m, l      final shift and fp32 denominator; flags = ORC_ROW_* bits
+ *   flag_cert 1 = every streaming tie decision of the row is certain
+ *   ex        ORC_EX_* bits                                                 */
+int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
+                const uint16_t* k, const uint16_t* v, const int32_t* heads,
+                int32_t nheads, double* obar, uint8_t* obar_cert, double* o,
+                float* m, float* l, uint8_t* flags, uint8_t* flag_cert,
+                uint8_t* ex, int32_t nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

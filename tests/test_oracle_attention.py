@@ -1,0 +1,253 @@
+"""Pins of the oracle's attention functions against things other than
+itself: torch float64 materialised attention and its autograd (library
+routines), closed forms, invariants the pages state, special cases and
+brute-force counting on tiny inputs."""
+import numpy as np
+import pytest
+import torch
+
+from flashattention_fa_fwd_amd import workloads as W
+
+
+def _rand_problem(orc, seed, B=1, Hq=2, Hkv=1, N=40, d=64, causal=True, scale=1.0, guard=0):
+    rng = np.random.default_rng(seed)
+    q = W.to_bf16_bits(rng.standard_normal((B, Hq, N, d)).astype(np.float32) * scale)
+    k = W.to_bf16_bits(rng.standard_normal((B, Hkv, N, d)).astype(np.float32) * scale)
+    v = W.to_bf16_bits(rng.standard_normal((B, Hkv, N, d)).astype(np.float32) - 0.3)
+    do = W.to_bf16_bits(rng.standard_normal((B, Hq, N, d)).astype(np.float32))
+    p = orc.Problem(B, Hq, Hkv, N, d, causal, guard)
+    return p, q, k, v, do
+
+
+def _t64(bits):
+    return torch.from_numpy(W.bits_to_f32(bits).astype(np.float64))
+
+
+def _torch_attention(p, q, k, v):
+    """Materialised softmax attention in torch float64 (CPU)."""
+    Q, K, V = _t64(q), _t64(k), _t64(v)
+    g = p.heads_q // p.heads_kv
+    K = K.repeat_interleave(g, dim=1)
+    V = V.repeat_interleave(g, dim=1)
+    alpha = float(np.float32(1 / np.sqrt(p.head_dim)))
+    S = alpha * (Q @ K.transpose(-1, -2))
+    if p.causal:
+        N = p.seqlen
+        S = S.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    return torch.softmax(S, dim=-1), V
+
+
+@pytest.mark.parametrize("causal,Hq,Hkv,N,d", [(True, 2, 1, 40, 64), (False, 4, 2, 33, 64),
+                                                (True, 2, 2, 65, 128), (False, 1, 1, 1, 64)])
+def test_fwd_f64_matches_torch_materialised(orc, causal, Hq, Hkv, N, d):
+    p, q, k, v, _ = _rand_problem(orc, 3, 2, Hq, Hkv, N, d, causal)
+    o, lse = orc.fwd_f64(p, q, k, v)
+    P, V = _torch_attention(p, q, k, v)
+    ref = (P @ V).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("causal,Hq,Hkv,N,d", [(True, 2, 1, 24, 64), (False, 4, 2, 17, 64),
+                                                (True, 1, 1, 9, 128)])
+def test_bwd_f64_matches_torch_autograd(orc, causal, Hq, Hkv, N, d):
+    p, q, k, v, do = _rand_problem(orc, 4, 2, Hq, Hkv, N, d, causal)
+    Q, K, V = (_t64(x).requires_grad_(True) for x in (q, k, v))
+    g = Hq // Hkv
+    alpha = float(np.float32(1 / np.sqrt(d)))
+    S = alpha * (Q @ K.repeat_interleave(g, 1).transpose(-1, -2))
+    if causal:
+        S = S.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    O = torch.softmax(S, -1) @ V.repeat_interleave(g, 1)
+    O.backward(_t64(do))
+    r = orc.bwd_f64(p, q, k, v, do)
+    for name, ref in (("o", O.detach()), ("dq", Q.grad), ("dk", K.grad), ("dv", V.grad)):
+        ref = ref.numpy()
+        err = np.max(np.abs(r[name] - ref)) / max(1e-30, np.max(np.abs(ref)))
+        assert err < 1e-11, (name, err)
+
+
+def test_delta_identity(orc):
+    """delta = rowsum(dO∘O) equals rowsum(dP∘P) ([R] method, paper §3.2)."""
+    p, q, k, v, do = _rand_problem(orc, 5, 1, 2, 2, 48, 64, True)
+    r = orc.bwd_f64(p, q, k, v, do)
+    P, V = _torch_attention(p, q, k, v)
+    dP = _t64(do) @ V.transpose(-1, -2)
+    alt = (dP * P).sum(-1).numpy()
+    assert np.max(np.abs(r["delta"] - alt)) < 1e-12 * np.max(np.abs(alt))
+
+
+def test_gradient_structure(orc):
+    """Softmax shift invariance makes every row of dS sum to zero, so the key
+    gradients of a head sum to zero; rows of P sum to one, so sum_j dV_j =
+    sum_i dO_i (per KV head, over its query heads)."""
+    p, q, k, v, do = _rand_problem(orc, 6, 2, 4, 2, 37, 64, False)
+    r = orc.bwd_f64(p, q, k, v, do)
+    dk_sum = r["dk"].sum(axis=2)
+    assert np.max(np.abs(dk_sum)) < 1e-11 * np.max(np.abs(r["dk"])) * p.seqlen
+    dO = W.bits_to_f32(do).astype(np.float64).reshape(2, 2, 2, 37, 64).sum(axis=(2, 3))
+    assert np.allclose(r["dv"].sum(axis=2), dO, rtol=1e-12, atol=1e-10)
+
+
+def test_special_cases(orc):
+    # causal row 0 sees only key 0: O_0 = V_0 and dQ_0 = 0
+    p, q, k, v, do = _rand_problem(orc, 7, 1, 1, 1, 16, 64, True)
+    r = orc.bwd_f64(p, q, k, v, do)
+    assert np.array_equal(r["o"][0, 0, 0], W.bits_to_f32(v[0, 0, 0]).astype(np.float64))
+    assert np.all(r["dq"][0, 0, 0] == 0)
+    # a single key: P = 1, so dK = 0 and dV = dO
+    p1, q1, k1, v1, do1 = _rand_problem(orc, 8, 1, 1, 1, 1, 64, False)
+    r1 = orc.bwd_f64(p1, q1, k1, v1, do1)
+    assert np.all(r1["dk"] == 0)
+    assert np.array_equal(r1["dv"], W.bits_to_f32(do1).astype(np.float64))
+
+
+def _count_tie(t_row, eps):
+    """Brute force: the maximum recurs iff at least two logits lie within eps
+    of it (counted, not via a second maximum)."""
+    mx = np.max(t_row)
+    return int(np.sum(t_row >= np.float32(mx - np.float32(eps)))) >= 2 if t_row.size > 1 else False
+
+
+def test_row_stats_against_counting(orc):
+    x = W.make("tiny")
+    wl = x["workload"]
+    p = orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True, orc.GUARD_BETA)
+    st = orc.row_stats(p, x["q"], x["k"])
+    Q = W.bits_to_f32(x["q"][0, 0]).astype(np.float64)
+    K = W.bits_to_f32(x["k"][0, 0]).astype(np.float64)
+    S = Q @ K.T
+    alpha = np.float32(wl.alpha)
+    n_tie = 0
+    for i in range(wl.seqlen):
+        t = (alpha * S[i, : i + 1].astype(np.float32)).astype(np.float32)
+        tie = _count_tie(t, 1e-3)
+        n_tie += tie
+        assert bool(st["flags"][0, 0, i] & orc.ROW_TIE) == tie, i
+        assert st["r"][0, 0, i] == np.max(t)
+        r = np.max(t)
+        m = (np.float32(2.0) * r if r > 0 else np.float32(0.0)) if tie else r
+        assert st["m"][0, 0, i] == m
+    assert n_tie >= 13  # the planted ties (10%) are found
+
+
+def test_shift_invariance(orc):
+    """Every shift gives the same O in exact arithmetic ([R] the fix: softmax
+    is unchanged by a per-row constant; [S] key claims)."""
+    x = W.make("tiny")
+    wl = x["workload"]
+    o64, _ = orc.fwd_f64(orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True), x["q"], x["k"], x["v"])
+    for guard in (orc.GUARD_NONE, orc.GUARD_BETA, orc.GUARD_EPS):
+        for beta in (2.0, 8.0):
+            p = orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True, guard, beta=beta)
+            st = orc.row_stats(p, x["q"], x["k"])
+            ob, l = orc.obar_f64(p, x["q"], x["k"], x["v"], st["m"])
+            o = ob / l[..., None]
+            assert np.max(np.abs(o - o64)) < 1e-12 * np.max(np.abs(o64))
+
+
+def test_beta_guard_underflow_closed_form(orc):
+    """[R] the fix / App. C: the guarded maximum term is exp(-(beta-1) r),
+    so a tie row's denominator underflows iff (beta-1) r exceeds the exp
+    underflow threshold (126 ln 2 with results below 2^-126 flushed)."""
+    d, N = 64, 4
+    thr = 126 * np.log(2.0)
+    # r = 87.0 and 87.5 are exact (q = 8r is a bf16 value) and straddle 126 ln 2 = 87.34
+    for r_target, want_zero in ((87.0, False), (87.5, True)):
+        # keys 0 and 1 identical, query aligned with them: r = alpha*q.k
+        beta = 2.0
+        alpha = 1 / 8
+        kvec = np.zeros(d, np.float32); kvec[0] = 1.0
+        q = np.zeros((1, 1, N, d), np.float32); q[0, 0, :, 0] = r_target / alpha
+        k = np.zeros((1, 1, N, d), np.float32); k[0, 0, 0] = kvec; k[0, 0, 1] = kvec
+        k[0, 0, 2:, 0] = -1.0
+        qb, kb = W.to_bf16_bits(q), W.to_bf16_bits(k)
+        vb = W.to_bf16_bits(np.ones((1, 1, N, d), np.float32))
+        p = orc.Problem(1, 1, 1, N, d, False, orc.GUARD_BETA, beta=beta)
+        e = orc.fwd_emu(p, orc.Schedule(block_n=64, ftz=True), qb, kb, vb)
+        r = float(W.bits_to_f32(qb[0, 0, 0, 0])) * alpha
+        pred = (beta - 1) * r > thr
+        assert pred == want_zero
+        for i in range(N):
+            assert bool(e["flags"][0, 0, i] & orc.ROW_ZERO_DENOM) == pred
+            assert bool(e["flags"][0, 0, i] & orc.ROW_TIE)
+
+
+def test_guard_keeps_pbar_below_one(orc):
+    """[R] the fix: under a guarded shift no P̄ reaches 1 (apart from the two
+    documented exceptions: r = 0, and a shift too small to move bf16(P̄)
+    off 1); an unguarded tie row has bf16(P̄) = 1 at every maximum."""
+    x = W.make("tiny")
+    wl = x["workload"]
+    sched = orc.Schedule(block_n=64)
+    for guard in (orc.GUARD_BETA, orc.GUARD_EPS):
+        p = orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True, guard)
+        e = orc.fwd_emu(p, sched, x["q"], x["k"], x["v"])
+        tie = (e["flags"] & orc.ROW_TIE) != 0
+        st = orc.row_stats(p, x["q"], x["k"])
+        small = np.abs(st["r"]) * (p.beta - 1 if guard == orc.GUARD_BETA else 0) < 2 ** -9
+        exempt = (st["r"] == 0) | (small if guard == orc.GUARD_BETA else False)
+        bad = tie & ((e["ex"] & orc.EX_PBAR_ONE_TIED) != 0) & ~exempt
+        assert not bad.any()
+    p = orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True, orc.GUARD_NONE)
+    e = orc.fwd_emu(p, sched, x["q"], x["k"], x["v"])
+    tie = (e["flags"] & orc.ROW_TIE) != 0
+    assert np.all((e["ex"][tie] & orc.EX_PBAR_ONE_TIED) != 0)
+
+
+def test_emulation_fp32_mode_matches_definition(orc):
+    """With Ō kept in fp32 the emulated output is the exact output up to the
+    bf16 roundings of P̄ and of O itself."""
+    x = W.make("tiny")
+    wl = x["workload"]
+    p = orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True, orc.GUARD_BETA)
+    e = orc.fwd_emu(p, orc.Schedule(block_n=64, obar_fp32=True), x["q"], x["k"], x["v"])
+    o64, _ = orc.fwd_f64(p, x["q"], x["k"], x["v"])
+    assert np.max(np.abs(e["o"] - o64)) < 2 ** -7 * np.max(np.abs(o64))
+    ob, l = orc.obar_f64(p, x["q"], x["k"], x["v"], e["m"])
+    assert np.max(np.abs(e["obar"] - ob) / np.maximum(l[..., None], 1e-30)) < 2 ** -7
+
+
+def test_emulation_single_block_is_final_shift(orc):
+    """With one block covering the whole row (no tiling), the streaming shift
+    is the per-row rule of the final maximum."""
+    x = W.make("tiny")
+    wl = x["workload"]
+    for guard in (orc.GUARD_NONE, orc.GUARD_BETA, orc.GUARD_EPS):
+        p = orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True, guard)
+        e = orc.fwd_emu(p, orc.Schedule(block_n=wl.seqlen), x["q"], x["k"], x["v"])
+        st = orc.row_stats(p, x["q"], x["k"])
+        assert np.array_equal(e["m"], st["m"])
+        assert np.array_equal(e["flags"] & orc.ROW_TIE, st["flags"] & orc.ROW_TIE)
+        assert not np.any(e["ex"] & orc.EX_SHIFT_DECREASED)
+
+
+def _signed_error(orc, x, guard, obar_fp32=False, block_n=64):
+    wl = x["workload"]
+    p = orc.Problem(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim, wl.causal, guard)
+    e = orc.fwd_emu(p, orc.Schedule(block_n=block_n, obar_fp32=obar_fp32), x["q"], x["k"], x["v"])
+    ob, l = orc.obar_f64(p, x["q"], x["k"], x["v"], e["m"])
+    err = (e["obar"] - ob) / l[..., None]
+    tie = (e["flags"] & orc.ROW_TIE) != 0
+    return err, tie
+
+
+def test_emulated_bias_reproduces_the_pages_finding(orc):
+    """[R] 'Core idea' (paper §3.3.2) / [S] key claims: in bf16 Ō mode, tie
+    rows of an unguarded pass get a negative mean error on negative-dominated
+    features; the beta guard removes it; fp32 Ō removes it too.  The eps
+    variant leaves a consistent-direction error: its P̄ at the maximum is
+    always bf16(exp(-2^-5)) = 0.96875, rounded down ([R] the fix: a fixed
+    small constant brings the bias back)."""
+    errs = {}
+    for seed in range(1001, 1031):
+        x = W.make("tiny", seed=seed)
+        for key, guard, f32 in (("none", orc.GUARD_NONE, False), ("beta", orc.GUARD_BETA, False),
+                                ("eps", orc.GUARD_EPS, False), ("none32", orc.GUARD_NONE, True)):
+            err, tie = _signed_error(orc, x, guard, f32)
+            errs.setdefault(key, []).append(err[0, 0][tie[0, 0]][:, :32].ravel())
+    m = {k: np.concatenate(v) for k, v in errs.items()}
+    se = {k: v.std() / np.sqrt(v.size) for k, v in m.items()}
+    assert m["none"].mean() < -3 * se["none"]
+    assert abs(m["beta"].mean()) < 1e-4
+    assert abs(m["none32"].mean()) < 1e-4
+    assert abs(m["eps"].mean()) > 3 * se["eps"]
