@@ -1,0 +1,211 @@
+"""Guarded BF16 FlashAttention for MI355X (gfx950): Python binding.
+
+Argument marshalling for the C ABI in ``include/attn.h`` (``libattn.so``):
+every step of the computation runs in the library's HIP kernels.  PyTorch is
+used only to own device memory and to name the current HIP stream.  There is
+no fallback: if the library is missing or fails to load, every call raises.
+
+The functions carry the C ABI's names: attn_fwd, attn_bwd (and its stages
+attn_bwd_preprocess / attn_bwd_main / attn_bwd_finalize), attn_schedule,
+attn_bwd_workspace_bytes, attn_strerror, attn_abi_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+CAUSAL = 0x1
+GUARD_NONE, GUARD_BETA, GUARD_EPS = 0x0, 0x2, 0x4
+OBAR_FP32 = 0x8
+ROW_TIE, ROW_ZERO_DENOM, ROW_GUARD_APPLIED = 0x1, 0x2, 0x4
+_GUARDS = {"none": GUARD_NONE, "beta": GUARD_BETA, "eps": GUARD_EPS}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {attn_strerror(code)} (code {code})")
+        self.code = code
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("beta", ctypes.c_float), ("tie_eps", ctypes.c_float),
+        ("shift_eps", ctypes.c_float), ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libattn.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run flashattention_fa_fwd_amd/build_lib.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, fp, pp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(Params)
+        u8p, i32p = ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_int32)
+        L.attn_abi_version.restype = ctypes.c_int
+        L.attn_strerror.argtypes = [ctypes.c_int]
+        L.attn_strerror.restype = ctypes.c_char_p
+        L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p]
+        L.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd_workspace_bytes.argtypes = [pp]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_bwd_main.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_bwd_finalize.argtypes = [pp, vp, vp, ctypes.c_size_t, vp]
+        for n in ("attn_schedule", "attn_fwd", "attn_bwd", "attn_bwd_preprocess",
+                  "attn_bwd_main", "attn_bwd_finalize"):
+            getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def attn_abi_version() -> int:
+    return lib().attn_abi_version()
+
+
+def attn_strerror(code: int) -> str:
+    return lib().attn_strerror(int(code)).decode()
+
+
+def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guard="beta",
+                beta=2.0, tie_eps=1e-3, shift_eps=2.0 ** -5, obar_fp32=False,
+                softmax_scale=None) -> Params:
+    flags = (CAUSAL if causal else 0) | _GUARDS[guard] | (OBAR_FP32 if obar_fp32 else 0)
+    return Params(batch, heads_q, heads_kv, seqlen, head_dim,
+                  0.0 if softmax_scale is None else float(softmax_scale),
+                  float(beta), float(tie_eps), float(shift_eps), flags)
+
+
+def _params_from(q, k, **kw) -> Params:
+    B, Hq, N, d = q.shape
+    return make_params(B, Hq, k.shape[1], N, d, **kw)
+
+
+def _check_bf16(name, t, shape=None):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 tensor on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous ([batch, heads, seqlen, head_dim])")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _call(name, rc):
+    if rc != 0:
+        raise AttnError(rc, name)
+
+
+def attn_schedule(p: Params):
+    bm, bn, rn, ch = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _call("attn_schedule", lib().attn_schedule(ctypes.byref(p), ctypes.byref(bm), ctypes.byref(bn),
+                                               ctypes.byref(rn), ctypes.byref(ch)))
+    return dict(block_m=bm.value, block_n=bn.value, round_n=rn.value, chunk=ch.value)
+
+
+def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
+             shift_eps=2.0 ** -5, obar_fp32=False, softmax_scale=None,
+             return_obar=False, return_row_max=False, out=None, stream=None):
+    """Guarded streaming forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16.
+    Returns a dict: o, row_m, row_l, row_flags (+ obar, row_max on request)."""
+    _check_bf16("q", q)
+    B, Hq, N, d = q.shape
+    _check_bf16("k", k, (B, k.shape[1], N, d))
+    _check_bf16("v", v, k.shape)
+    p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
+                     shift_eps=shift_eps, obar_fp32=obar_fp32, softmax_scale=softmax_scale)
+    dev = q.device
+    res = out if out is not None else {}
+    if "o" not in res:
+        res["o"] = torch.empty_like(q)
+        res["row_m"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        res["row_l"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        res["row_flags"] = torch.empty((B, Hq, N), dtype=torch.uint8, device=dev)
+        if return_obar:
+            res["obar"] = torch.empty(q.shape, dtype=torch.float32 if obar_fp32 else torch.bfloat16, device=dev)
+        if return_row_max:
+            res["row_max"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    _call("attn_fwd", lib().attn_fwd(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(res["o"]), _ptr(res["row_m"]),
+        _ptr(res["row_l"]), _ptr(res["row_flags"]), _ptr(res.get("obar")), _ptr(res.get("row_max")),
+        _stream(stream)))
+    return res
+
+
+def attn_bwd_workspace_bytes(p: Params) -> int:
+    return int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def alloc_workspace(p: Params, device) -> torch.Tensor:
+    n = attn_bwd_workspace_bytes(p)
+    # torch's caching allocator hands out 512-byte aligned blocks
+    return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=device)
+
+
+def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=2.0,
+             tie_eps=1e-3, shift_eps=2.0 ** -5, softmax_scale=None, workspace=None,
+             out=None, stream=None):
+    """Backward.  Returns a dict: dq, dk, dv (bf16) and delta (fp32)."""
+    for n_, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_bf16(n_, t)
+    B, Hq, N, d = q.shape
+    p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
+                     shift_eps=shift_eps, softmax_scale=softmax_scale)
+    ws = workspace if workspace is not None else alloc_workspace(p, q.device)
+    res = out if out is not None else {}
+    if "dq" not in res:
+        res["dq"] = torch.empty_like(q)
+        res["dk"] = torch.empty_like(k)
+        res["dv"] = torch.empty_like(v)
+        res["delta"] = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _call("attn_bwd", lib().attn_bwd(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
+        _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["delta"]), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return res
+
+
+def attn_bwd_preprocess(p: Params, o, dout, delta, workspace, stream=None):
+    _call("attn_bwd_preprocess", lib().attn_bwd_preprocess(
+        ctypes.byref(p), _ptr(o), _ptr(dout), _ptr(delta), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_bwd_main(p: Params, q, k, v, dout, row_m, row_l, delta, dk, dv, workspace, stream=None):
+    _call("attn_bwd_main", lib().attn_bwd_main(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(row_m), _ptr(row_l),
+        _ptr(delta), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_bwd_finalize(p: Params, dq, workspace, stream=None):
+    _call("attn_bwd_finalize", lib().attn_bwd_finalize(
+        ctypes.byref(p), _ptr(dq), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def default_scale(head_dim: int) -> float:
+    """fl32(1/sqrt(head_dim)), the scale the library uses when none is given."""
+    return float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))

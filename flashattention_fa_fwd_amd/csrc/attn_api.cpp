@@ -1,0 +1,221 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h: argument checks,
+// kernel selection and launches on the caller's stream.  No allocation, no
+// synchronisation, no global state.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float scale_of(const attn_params* p) {
+  if (p->softmax_scale > 0.0f) return p->softmax_scale;
+  return (float)(1.0 / std::sqrt((double)p->head_dim));
+}
+
+int check_params(const attn_params* p) {
+  if (!p) return ATTN_E_NULL;
+  if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->seqlen <= 0 ||
+      p->head_dim <= 0)
+    return ATTN_E_SHAPE;
+  if (p->heads_q % p->heads_kv != 0) return ATTN_E_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return ATTN_E_UNSUPPORTED;
+  const uint32_t known = ATTN_CAUSAL | ATTN_GUARD_MASK | ATTN_OBAR_FP32;
+  if (p->flags & ~known) return ATTN_E_PARAM;
+  const uint32_t g = p->flags & ATTN_GUARD_MASK;
+  if (g == ATTN_GUARD_MASK) return ATTN_E_PARAM;  // two guards at once
+  if (!std::isfinite(p->softmax_scale)) return ATTN_E_PARAM;
+  if (g == ATTN_GUARD_BETA && !(p->beta > 1.0f && std::isfinite(p->beta))) return ATTN_E_PARAM;
+  if (!(p->tie_eps >= 0.0f && std::isfinite(p->tie_eps))) return ATTN_E_PARAM;
+  if (g == ATTN_GUARD_EPS && !(p->shift_eps > 0.0f && std::isfinite(p->shift_eps))) return ATTN_E_PARAM;
+  // rows * head_dim must fit the kernels' index arithmetic
+  const double elems = (double)p->batch * p->heads_q * p->seqlen * p->head_dim;
+  if (elems > 9.0e15) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+int guard_of(uint32_t flags) {
+  switch (flags & ATTN_GUARD_MASK) {
+    case ATTN_GUARD_BETA: return attn::kGuardBeta;
+    case ATTN_GUARD_EPS: return attn::kGuardEps;
+    default: return attn::kGuardNone;
+  }
+}
+
+size_t ws_bytes(const attn_params* p) {
+  return (size_t)p->batch * p->heads_q * p->seqlen * p->head_dim * sizeof(float);
+}
+
+attn::BwdArgs bwd_args(const attn_params* p, const void* q, const void* k, const void* v,
+                       const void* o, const void* dout, const float* row_m, const float* row_l,
+                       void* dq, void* dk, void* dv, float* delta, void* ws) {
+  attn::BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)dout;
+  a.row_m = row_m;
+  a.row_l = row_l;
+  a.delta = delta;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.dq_acc = (float*)ws;
+  a.B = p->batch;
+  a.Hq = p->heads_q;
+  a.Hkv = p->heads_kv;
+  a.N = p->seqlen;
+  a.group = p->heads_q / p->heads_kv;
+  a.alpha = scale_of(p);
+  a.c1 = a.alpha * attn::kLog2e;
+  return a;
+}
+
+int check_ws(const attn_params* p, const void* ws, size_t bytes) {
+  if (!ws) return ATTN_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ATTN_E_WORKSPACE;
+  if (bytes < ws_bytes(p)) return ATTN_E_WORKSPACE;
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "invalid shape (non-positive size or heads_q not a multiple of heads_kv)";
+    case ATTN_E_UNSUPPORTED: return "unsupported head_dim (64 or 128) or misaligned tensor pointer";
+    case ATTN_E_PARAM: return "invalid parameter (beta, tie_eps, shift_eps, scale or flags)";
+    case ATTN_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ATTN_E_HIP: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown error code";
+  }
+}
+
+int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n, int32_t* round_n,
+                  int32_t* chunk) {
+  const int rc = check_params(p);
+  if (rc) return rc;
+  if (block_m) *block_m = attn::kFwdBlockM;
+  if (block_n) *block_n = attn::kFwdBlockN;
+  if (round_n) *round_n = attn::kFwdRoundN;
+  if (chunk) *chunk = attn::kMfmaK;
+  return ATTN_OK;
+}
+
+int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o,
+             float* row_m, float* row_l, uint8_t* row_flags, void* obar_out, float* row_max,
+             void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !o || !row_m || !row_l || !row_flags) return ATTN_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (obar_out && !aligned16(obar_out)))
+    return ATTN_E_UNSUPPORTED;
+  attn::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.row_m = row_m;
+  a.row_l = row_l;
+  a.row_flags = row_flags;
+  a.obar = obar_out;
+  a.row_max = row_max;
+  a.B = p->batch;
+  a.Hq = p->heads_q;
+  a.Hkv = p->heads_kv;
+  a.N = p->seqlen;
+  a.group = p->heads_q / p->heads_kv;
+  a.alpha = scale_of(p);
+  a.c1 = a.alpha * attn::kLog2e;
+  a.beta = p->beta;
+  a.tie_eps = p->tie_eps;
+  a.shift_eps = p->shift_eps;
+  return hip_status(attn::launch_fwd(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
+                                     guard_of(p->flags), (p->flags & ATTN_OBAR_FP32) != 0,
+                                     (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_bytes(const attn_params* p) {
+  if (check_params(p) != ATTN_OK) return 0;
+  return ws_bytes(p);
+}
+
+int attn_bwd_preprocess(const attn_params* p, const void* o, const void* dout, float* delta,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!o || !dout || !delta) return ATTN_E_NULL;
+  if (!aligned16(o) || !aligned16(dout)) return ATTN_E_UNSUPPORTED;
+  rc = check_ws(p, workspace, workspace_bytes);
+  if (rc) return rc;
+  const attn::BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr,
+                                   nullptr, nullptr, nullptr, delta, workspace);
+  return hip_status(attn::launch_bwd_pre(a, p->head_dim, (hipStream_t)stream));
+}
+
+int attn_bwd_main(const attn_params* p, const void* q, const void* k, const void* v,
+                  const void* dout, const float* row_m, const float* row_l, const float* delta,
+                  void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout || !row_m || !row_l || !delta || !dk || !dv) return ATTN_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dk) ||
+      !aligned16(dv))
+    return ATTN_E_UNSUPPORTED;
+  rc = check_ws(p, workspace, workspace_bytes);
+  if (rc) return rc;
+  const attn::BwdArgs a = bwd_args(p, q, k, v, nullptr, dout, row_m, row_l, nullptr, dk, dv,
+                                   const_cast<float*>(delta), workspace);
+  return hip_status(attn::launch_bwd_main(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
+                                          (hipStream_t)stream));
+}
+
+int attn_bwd_finalize(const attn_params* p, void* dq, const void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!dq) return ATTN_E_NULL;
+  if (!aligned16(dq)) return ATTN_E_UNSUPPORTED;
+  rc = check_ws(p, workspace, workspace_bytes);
+  if (rc) return rc;
+  const attn::BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, dq, nullptr, nullptr, nullptr,
+                                   const_cast<void*>(workspace));
+  return hip_status(attn::launch_bwd_post(a, p->head_dim, (hipStream_t)stream));
+}
+
+int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* row_m, const float* row_l, void* dq, void* dk,
+             void* dv, float* delta, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !o || !dout || !row_m || !row_l || !dq || !dk || !dv || !delta)
+    return ATTN_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_E_UNSUPPORTED;
+  rc = check_ws(p, workspace, workspace_bytes);
+  if (rc) return rc;
+  rc = attn_bwd_preprocess(p, o, dout, delta, workspace, workspace_bytes, stream);
+  if (rc) return rc;
+  rc = attn_bwd_main(p, q, k, v, dout, row_m, row_l, delta, dk, dv, workspace, workspace_bytes,
+                     stream);
+  if (rc) return rc;
+  return attn_bwd_finalize(p, dq, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,306 @@
+// attn_fwd.hip -- guarded streaming FlashAttention forward for gfx950.
+//
+// What it computes ([R] = the priors.kr review "BF16 플래시 어텐션은 왜 수천
+// 스텝 뒤에 무너질까", [S] = the bud-325 summary "Why Low-Precision
+// Transformer Training Fails: An Analysis on Flash Attention"):
+//   * tiled attention with an online softmax and an unnormalised output
+//     Ō = P̄ V, P̄ = exp(t - m), normalised once at the end ([R] "Why it
+//     matters", paper §2.2; "Core idea", equations, paper §3.3.2);
+//   * the repeated-maximum guard: a row whose maximum r recurs within
+//     tie_eps takes the shift beta*r (r > 0) or 0, or r + shift_eps in the
+//     eps variant; other rows take r ([R] the fix, paper §4; [S] "Method",
+//     Algorithm 1: one extra step inside the tiling loop);
+//   * Ō accumulated in fp32 and rounded to bf16 after every 512 keys (the
+//     block size of the analysed code, which keeps P̄V in bf16: [R] "Points
+//     to doubt") and after the row's last key, or kept in fp32 throughout
+//     ([S] "Key claims" and the QK-Guard abstract: fp32 accumulation repairs
+//     it).
+//
+// Mapping to CDNA4 (not from the pages):
+//   * one workgroup = 4 wave64s = 128 query rows of one (batch, head); a
+//     wave owns 32 rows;
+//   * per step of 64 keys the block's K rows are staged in LDS row-major
+//     and its V rows transposed (feature-major), shared by the 4 waves;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: lane l of a wave owns query
+//     row l%32 and holds 32 of that row's 64 scores (the other 32 sit in lane
+//     l^32), so the row max, the top-two merge and the row sum are in-lane
+//     plus one exchange between the two lane halves;
+//   * P̄ goes to bf16 in registers and is used directly as the B operand of
+//     O^T = V^T P̄^T, whose accumulator has the same lane-to-row ownership,
+//     so the rescale by exp(m_old - m) is a per-lane scalar.
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Top-two merge of (a, a2) and (b, b2), each with first >= second; the
+// result keeps multiset semantics (equal maxima give r2 == r).
+__device__ __forceinline__ void top2_merge(float& a, float& a2, float b, float b2) {
+  float lo = fminf(a, b);
+  a = fmaxf(a, b);
+  a2 = fmaxf(lo, fmaxf(a2, b2));
+}
+
+template <int D, bool CAUSAL, int GUARD, bool OBAR_F32>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+  constexpr int BN = kFwdBlockN;
+  constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
+  constexpr int VSTR = BN + 4;   // LDS row stride of the transposed V tile
+  constexpr int NT = D / kMfmaK; // matrix steps along d for S
+  constexpr int FB = D / 32;     // 32-feature blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int N = a.N;
+  const int nmb = gridDim.x;
+  const int mb = CAUSAL ? (nmb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // heavy blocks first
+  const int hq = blockIdx.y, b = blockIdx.z;
+  const int hk = hq / a.group;
+  const int q0 = mb * kFwdBlockM + wave * 32;
+  const int qrow = q0 + l32;
+
+  const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
+  const size_t kvoff = ((size_t)(b * a.Hkv + hk) * N) * D;
+  const uint16_t* __restrict__ Q = a.q + qoff;
+  const uint16_t* __restrict__ K = a.k + kvoff;
+  const uint16_t* __restrict__ V = a.v + kvoff;
+
+  // Q fragment as the B operand: lane holds Q[qrow][16t + 8*half + 0..7]
+  bf16x8 qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (qrow < N) raw = *(const uint4*)(Q + (size_t)qrow * D + 16 * t + 8 * half);
+    qf[t] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  f32x16 oacc[FB];
+#pragma unroll
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[f][i] = 0.0f;
+
+  float R = -INFINITY, R2 = -INFINITY;  // running top two of the raw scores s
+  float m = 0.0f, m2 = 0.0f, rt = -INFINITY;
+  float lsum = 0.0f;
+  bool tie = false;
+
+  const int kend = CAUSAL ? min(N, (mb + 1) * kFwdBlockM) : N;
+  const bool wave_live = q0 < N;
+
+  for (int j0 = 0; j0 < kend; j0 += BN) {
+    __syncthreads();  // the previous step's readers are done with the tiles
+    // ---- stage K (row-major) and V (transposed) of keys j0 .. j0+63
+    constexpr int KCH = BN * D / 8;  // 16-byte chunks
+#pragma unroll
+    for (int c = tid; c < KCH; c += kThreads) {
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int key = j0 + row;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (key < N) val = *(const uint4*)(K + (size_t)key * D + col);
+      *(uint4*)(&Ks[row * KSTR + col]) = val;
+    }
+    // V: a thread takes two consecutive keys and 8 features and writes
+    // 8 dwords (key pair) of the feature-major tile
+    constexpr int VCH = (BN / 2) * (D / 8);
+#pragma unroll
+    for (int c = tid; c < VCH; c += kThreads) {
+      const int pr = c % (BN / 2), col = (c / (BN / 2)) * 8;
+      const int key = j0 + 2 * pr;
+      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+      if (key < N) v0 = *(const uint4*)(V + (size_t)key * D + col);
+      if (key + 1 < N) v1 = *(const uint4*)(V + (size_t)(key + 1) * D + col);
+      const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
+      const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // features col+2e (low halves) and col+2e+1 (high halves)
+        uint32_t lo = (w0[e] & 0xffffu) | (w1[e] << 16);
+        uint32_t hi = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+        *(uint32_t*)(&Vt[(col + 2 * e) * VSTR + 2 * pr]) = lo;
+        *(uint32_t*)(&Vt[(col + 2 * e + 1) * VSTR + 2 * pr]) = hi;
+      }
+    }
+    __syncthreads();
+
+    // a wave whose rows all lie above this block's first key has nothing here
+    if (!wave_live || (CAUSAL && j0 > q0 + 31)) continue;
+
+    // ---- S^T = K Q^T for the 64 keys: two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 kf =
+            *(const bf16x8*)(&Ks[(32 * kb + l32) * KSTR + 16 * t + 8 * half]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
+      }
+    }
+    // key of s[kb][i] in this lane: j0 + 32kb + 8(i/4) + 4*half + i%4
+    const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > q0);
+    if (edge) {
+      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (key > lim) s[kb][i] = -INFINITY;
+        }
+    }
+
+    // ---- running top two (repeated-maximum detection)
+    float tr = -INFINITY, tr2 = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = s[kb][i];
+        tr2 = __builtin_amdgcn_fmed3f(tr, tr2, x);  // = max(tr2, min(tr, x))
+        tr = fmaxf(tr, x);
+      }
+    top2_merge(tr, tr2, __shfl_xor(tr, 32), __shfl_xor(tr2, 32));
+    top2_merge(R, R2, tr, tr2);
+
+    // ---- tie decision and shift on the scaled logits t = alpha * s
+    rt = a.alpha * R;
+    const float r2t = a.alpha * R2;
+    tie = (rt - r2t) <= a.tie_eps;  // false when r2 is -inf (a single key)
+    float mn = rt;
+    if (GUARD == kGuardBeta && tie) mn = (rt > 0.0f) ? a.beta * rt : 0.0f;
+    if (GUARD == kGuardEps && tie) mn = rt + a.shift_eps;
+
+    // ---- rescale by c = exp(m_old - m_new) where the shift moved
+    if (j0 == 0) {
+      m = mn;
+    } else if (__any(mn != m)) {
+      const float c = (mn != m) ? __builtin_amdgcn_exp2f((m - mn) * kLog2e) : 1.0f;
+      lsum *= c;
+#pragma unroll
+      for (int f = 0; f < FB; ++f)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[f][i] *= c;
+      m = mn;
+    }
+    m2 = m * kLog2e;
+
+    // ---- P̄ = exp(t - m) = exp2(s * alpha*log2e - m*log2e); row sum; bf16
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], a.c1, -m2));
+        lsum += p;
+        pf[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+      }
+
+    // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      const uint16_t* vrow = &Vt[(32 * f + l32) * VSTR];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint2 lo = *(const uint2*)(vrow + 16 * t + 4 * half);
+        const uint2 hi = *(const uint2*)(vrow + 16 * t + 8 + 4 * half);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[f], 0, 0, 0);
+      }
+    }
+    // bf16 mode: round the accumulator after every kFwdRoundN keys and
+    // after this wave's last step (which holds the last key of its rows)
+    const bool last = CAUSAL ? (j0 + BN > q0 + 31) : (j0 + BN >= kend);
+    if (!OBAR_F32 && (((j0 + BN) % kFwdRoundN) == 0 || last)) {
+#pragma unroll
+      for (int f = 0; f < FB; ++f)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[f][i] = bf16_round(oacc[f][i]);
+    }
+  }
+
+  if (!wave_live) return;
+  // ---- epilogue: O = bf16(Ō / ℓ); row outputs
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (qrow >= N) return;
+  uint16_t* orow = a.o + qoff + (size_t)qrow * D;
+#pragma unroll
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = 32 * f + 8 * g + 4 * half;
+      uint16_t e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = bf16_bits(oacc[f][4 * g + u] / ltot);
+      *(uint2*)(orow + col) = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+      if (a.obar) {
+        if (OBAR_F32) {
+          float* ob = (float*)a.obar + qoff + (size_t)qrow * D + col;
+          *(f32x4*)ob = f32x4{oacc[f][4 * g], oacc[f][4 * g + 1], oacc[f][4 * g + 2], oacc[f][4 * g + 3]};
+        } else {
+          uint16_t* ob = (uint16_t*)a.obar + qoff + (size_t)qrow * D + col;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) e[u] = bf16_bits(oacc[f][4 * g + u]);
+          *(uint2*)ob = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+        }
+      }
+    }
+  if (half == 0) {
+    const size_t ridx = (size_t)(b * a.Hq + hq) * N + qrow;
+    a.row_m[ridx] = m;
+    a.row_l[ridx] = ltot;
+    uint8_t fl = 0;
+    if (tie) fl |= 1u;
+    if (ltot == 0.0f) fl |= 2u;
+    if (tie && GUARD != kGuardNone) fl |= 4u;
+    a.row_flags[ridx] = fl;
+    if (a.row_max) a.row_max[ridx] = rt;
+  }
+}
+
+template <int D, bool CAUSAL, int GUARD, bool OBAR_F32>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+  const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
+  dim3 grid(nmb, a.Hq, a.B);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, GUARD, OBAR_F32>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, int GUARD>
+hipError_t launch_o(const FwdArgs& a, bool obar_f32, hipStream_t s) {
+  return obar_f32 ? launch_t<D, CAUSAL, GUARD, true>(a, s) : launch_t<D, CAUSAL, GUARD, false>(a, s);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_g(const FwdArgs& a, int guard, bool obar_f32, hipStream_t s) {
+  switch (guard) {
+    case kGuardBeta: return launch_o<D, CAUSAL, kGuardBeta>(a, obar_f32, s);
+    case kGuardEps: return launch_o<D, CAUSAL, kGuardEps>(a, obar_f32, s);
+    default: return launch_o<D, CAUSAL, kGuardNone>(a, obar_f32, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
+                      hipStream_t s) {
+  if (d == 64)
+    return causal ? launch_g<64, true>(a, guard, obar_f32, s) : launch_g<64, false>(a, guard, obar_f32, s);
+  return causal ? launch_g<128, true>(a, guard, obar_f32, s) : launch_g<128, false>(a, guard, obar_f32, s);
+}
+
+}  // namespace attn

@@ -1,0 +1,70 @@
+// attn_internal.h -- device types and launcher declarations shared by the
+// HIP translation units of the library (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+enum Guard { kGuardNone = 0, kGuardBeta = 1, kGuardEps = 2 };
+
+// Tile shape of the streaming forward: 4 waves x 32 query rows per
+// workgroup, 64 keys per streaming step (tie decision and shift).  In bf16
+// mode Ō is rounded to bf16 after every kFwdRoundN keys and after a row's
+// last step.
+constexpr int kFwdBlockM = 128;
+constexpr int kFwdBlockN = 64;
+constexpr int kFwdRoundN = 512;
+// Products per matrix instruction along every contraction.
+constexpr int kMfmaK = 16;
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* row_m;
+  float* row_l;
+  uint8_t* row_flags;
+  void* obar;      // nullable
+  float* row_max;  // nullable
+  int B, Hq, Hkv, N, group;
+  float alpha;     // softmax scale (fp32)
+  float c1;        // fl32(alpha * log2(e))
+  float beta, tie_eps, shift_eps;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* row_m;
+  const float* row_l;
+  float* delta;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dq_acc;   // workspace: fp32 [B, Hq, N, d]
+  int B, Hq, Hkv, N, group;
+  float alpha, c1;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
+                      hipStream_t s);
+hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_post(const BwdArgs& a, int d, hipStream_t s);
+
+// Keys per workgroup and query rows per inner step of the backward.
+constexpr int kBwdBlockN = 64;
+constexpr int kBwdBlockM = 32;
+
+}  // namespace attn

@@ -82,9 +82,10 @@ typedef struct {
  * Per query row the keys are streamed in blocks of attn_schedule()'s block_n
  * keys.  After each block: (r, r2) = the two largest scaled logits
  * t = fl32(alpha*s) so far; tie = fl32(r - r2) <= tie_eps; m = guard shift
- * of r; Ō <- exp(m_old - m) Ō + sum bf16(exp(t - m)) V, accumulated in fp32
- * and, unless ATTN_OBAR_FP32, rounded to bf16 at the end of the block;
- * ℓ <- exp(m_old - m) ℓ + sum exp(t - m) in fp32.  Finally O = bf16(Ō/ℓ).
+ * of r; Ō <- exp(m_old - m) Ō + sum bf16(exp(t - m)) V, accumulated in fp32;
+ * ℓ <- exp(m_old - m) ℓ + sum exp(t - m) in fp32.  Unless ATTN_OBAR_FP32, Ō
+ * is rounded to bf16 after every round_n keys and after the row's last
+ * block.  Finally O = bf16(Ō/ℓ).
  *   q [B,Hq,N,d] bf16, k/v [B,Hkv,N,d] bf16                (in)
  *   o [B,Hq,N,d] bf16                                       (out)
  *   row_m [B,Hq,N] fp32: the final shift m                  (out, required)
@@ -138,12 +139,13 @@ int attn_bwd_finalize(const attn_params* p, void* dq, const void* workspace,
 /*
  * attn_schedule -- the rounding schedule attn_fwd uses for these params, so
  * that a reference can replay it: block_m query rows per workgroup, block_n
- * keys per streaming step (the Ō rounding block), chunk = products per
- * matrix instruction along each contraction.  Returns ATTN_OK or an error
- * code for invalid params.  Pointers may be NULL.
+ * keys per streaming step (tie decision and shift), round_n keys per bf16
+ * rounding of Ō (bf16 mode), chunk = products per matrix instruction along
+ * each contraction.  Returns ATTN_OK or an error code for invalid params.
+ * Pointers may be NULL.
  */
 int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n,
-                  int32_t* chunk);
+                  int32_t* round_n, int32_t* chunk);
 
 const char* attn_strerror(int code);
 int attn_abi_version(void);

@@ -39,7 +39,8 @@ class _Problem(ctypes.Structure):
 
 class _Schedule(ctypes.Structure):
     _fields_ = [
-        ("block_n", ctypes.c_int32), ("obar_fp32", ctypes.c_int32),
+        ("block_n", ctypes.c_int32), ("round_n", ctypes.c_int32),
+        ("obar_fp32", ctypes.c_int32), ("certify", ctypes.c_int32),
         ("ftz", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("chunk_err", ctypes.c_double), ("exp_rel_err", ctypes.c_double),
     ]
@@ -74,7 +75,9 @@ class Problem:
 class Schedule:
     """Rounding points and error model of the kernel under test.
 
-    block_n: keys per streaming step (= where Ō is rounded in bf16 mode).
+    block_n: keys per streaming step (tie decision and shift).
+    round_n: bf16 mode rounds Ō after every round_n keys (0: block_n).
+    certify: compute the certification (slow); False leaves every cert 0.
     ftz: the kernel's exp flushes results below 2^-126 to zero.
     chunk/chunk_err: sums run as chains of matrix instructions of `chunk`
     terms (error model in oracle.c, chain_bound), scaled by the safety factor
@@ -82,14 +85,17 @@ class Schedule:
     exp_rel_err: relative error bound of the kernel's exp.
     """
     block_n: int = 64
+    round_n: int = 0
     obar_fp32: bool = False
+    certify: bool = True
     ftz: bool = True
     chunk: int = 16
     chunk_err: float = 2.0
     exp_rel_err: float = 2.0 ** -22
 
     def c(self) -> _Schedule:
-        return _Schedule(self.block_n, int(bool(self.obar_fp32)), int(bool(self.ftz)),
+        return _Schedule(self.block_n, self.round_n, int(bool(self.obar_fp32)),
+                         int(bool(self.certify)), int(bool(self.ftz)),
                          self.chunk, self.chunk_err, self.exp_rel_err)
 
 

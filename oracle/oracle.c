@@ -271,10 +271,15 @@ static double chain_bound(const orc_schedule* sc, double c0, const double* terms
       int e;
       frexp(mx, &e); /* mx in [2^(e-1), 2^e) */
       double grid = ldexp(1.0, (e - 1) - 24);
-      for (int32_t i = i0; i < i1; ++i)
-        if (fmod(terms[i], grid) != 0.0) step += grid;
+      for (int32_t i = i0; i < i1; ++i) {
+        double qv = terms[i] / grid; /* exact: grid is a power of two */
+        if (qv != floor(qv)) step += grid;
+      }
       step += U24 * sa;
-      if (fabs(c) < ldexp(1.0, e) && fmod(c, grid) != 0.0) step += grid;
+      if (fabs(c) < ldexp(1.0, e)) {
+        double qc = c / grid;
+        if (qc != floor(qc)) step += grid;
+      }
     }
     step += U24 * fabs(r);
     err += factor * step;
@@ -632,9 +637,11 @@ int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
  *   2. decide the tie and the shift m (guard_shift);
  *   3. rescale by c = exp(m_old - m) and add P̄ = exp(t - m), with P̄ rounded
  *      to bf16 as a matrix-core operand: Ō <- c Ō + sum P̄_bf16 V,
- *      accumulated in fp32; in bf16 mode Ō is then rounded to bf16
- *      ([R] "Core idea", equations: the sum lives in a wider accumulator and
- *      is rounded once, which is what the worked addition shows);
+ *      accumulated in fp32; in bf16 mode the accumulator is rounded to bf16
+ *      after every round_n keys (the analysed code used 512-key blocks) and
+ *      after the row's last block ([R] "Core idea", equations: the sum lives
+ *      in a wider accumulator and is rounded once, which is what the worked
+ *      addition shows);
  *   4. ℓ <- c ℓ + sum P̄ in fp32.
  * At the end O = RNE_bf16(Ō/ℓ).
  *
@@ -663,6 +670,8 @@ static void emu_head(void* c, int32_t item) {
   int32_t qh = x->heads ? x->heads[item] : item;
   int32_t N = p->seqlen, d = p->head_dim;
   int32_t bn = sc->block_n > 0 ? sc->block_n : N;
+  int32_t rn = sc->round_n > 0 ? sc->round_n : bn;
+  const int cert_on = sc->certify != 0;
   const uint16_t* Q = x->q + q_head_offset(p, qh);
   const uint16_t* K = x->k + kv_head_offset(p, qh);
   const uint16_t* V = x->v + kv_head_offset(p, qh);
@@ -672,12 +681,12 @@ static void emu_head(void* c, int32_t item) {
   /* smallest nonzero result of the kernel's exp */
   const double under = sc->ftz ? 0x1p-126 : 0x1p-149;
 
-  double* sv = (double*)malloc(sizeof(double) * (size_t)N);  /* exact scores  */
-  double* sb = (double*)malloc(sizeof(double) * (size_t)N);  /* their bounds  */
-  float* tv = (float*)malloc(sizeof(float) * (size_t)N);     /* fp32 logits   */
-  double* pb = (double*)malloc(sizeof(double) * (size_t)bn); /* bf16 P̄ values */
-  double* ob = (double*)malloc(sizeof(double) * (size_t)d);  /* running Ō     */
-  double* obb = (double*)malloc(sizeof(double) * (size_t)d); /* bound on cŌ   */
+  double* sv = (double*)malloc(sizeof(double) * (size_t)N);  /* exact scores   */
+  double* sb = (double*)malloc(sizeof(double) * (size_t)N);  /* their bounds   */
+  float* tv = (float*)malloc(sizeof(float) * (size_t)N);     /* fp32 logits    */
+  double* pb = (double*)malloc(sizeof(double) * (size_t)bn); /* bf16 P̄ values  */
+  double* ob = (double*)malloc(sizeof(double) * (size_t)d);  /* accumulator Ō  */
+  double* obb = (double*)malloc(sizeof(double) * (size_t)d); /* its error bound */
   double* terms = (double*)malloc(sizeof(double) * (size_t)(bn > d ? bn : d));
   uint8_t* oc = (uint8_t*)malloc((size_t)d);
 
@@ -685,16 +694,22 @@ static void emu_head(void* c, int32_t item) {
     int32_t n = visible(p, i);
     const uint16_t* qi = Q + (size_t)i * d;
     for (int32_t j = 0; j < n; ++j) {
-      sv[j] = dot_with_bound(sc, qi, K + (size_t)j * d, d, terms, &sb[j]);
+      if (cert_on) {
+        sv[j] = dot_with_bound(sc, qi, K + (size_t)j * d, d, terms, &sb[j]);
+      } else {
+        sv[j] = dot_bf16(qi, K + (size_t)j * d, d);
+        sb[j] = 0.0;
+      }
       tv[j] = scaled_logit(p, sv[j]);
     }
     float r = -INFINITY, r2 = -INFINITY, m = 0.0f, l32 = 0.0f;
-    int have_m = 0, row_cert = 1, tie = 0, zero_ambig = 0;
+    int have_m = 0, dec_cert = cert_on, val_cert = cert_on, tie = 0, zero_ambig = 0;
     uint8_t exb = 0;
     double dmax = 0.0;
     for (int32_t f = 0; f < d; ++f) {
       ob[f] = 0.0;
-      oc[f] = 1;
+      obb[f] = 0.0;
+      oc[f] = (uint8_t)cert_on;
     }
     for (int32_t j0 = 0; j0 < n; j0 += bn) {
       int32_t j1 = j0 + bn < n ? j0 + bn : n;
@@ -713,25 +728,28 @@ static void emu_head(void* c, int32_t item) {
       }
       /* 2. tie decision and shift for this block */
       tie = tie_test(p, r, r2);
-      if (!tie_certain(p, r, r2, dmax)) row_cert = 0;
+      if (cert_on && !tie_certain(p, r, r2, dmax)) dec_cert = 0;
       float mn = guard_shift(p, r, tie);
       if (tie && p->guard == ORC_GUARD_BETA && r == 0.0f) exb |= ORC_EX_ZERO_MAX_TIE;
       /* 3a. rescale the running sums by c = exp(m_old - m_new) */
       if (have_m && mn != m) {
         if (mn < m) exb |= ORC_EX_SHIFT_DECREASED;
         double cexact = exp((double)m - (double)mn);
-        float c32 = (float)cexact;
-        if (isinf(c32)) exb |= ORC_EX_RESCALE_OVERFLOW;
         /* kernel: c = exp2(fl32(fl32(m_old - m_new) * log2e)), then fl32(c * Ō) */
         double dm2 = fabs((double)m - (double)mn) * log2e;
         double rho_c = log(2.0) * (2.0 * U24 * dm2) + exp_err;
+        /* the same exp flushes a result below the threshold to zero */
+        if (cexact <= under * (1.0 + 4.0 * rho_c)) {
+          if (cexact >= under * (1.0 - 4.0 * rho_c)) zero_ambig = 1;
+          cexact = (cexact < under) ? 0.0 : cexact;
+        }
+        float c32 = (float)cexact;
+        if (isinf(c32)) exb |= ORC_EX_RESCALE_OVERFLOW;
         for (int32_t f = 0; f < d; ++f) {
           ob[f] = cexact * ob[f];
-          obb[f] = fabs(ob[f]) * (rho_c + U24);
+          obb[f] = obb[f] * cexact * (1.0 + rho_c) + fabs(ob[f]) * (rho_c + U24);
         }
         l32 = c32 * l32;
-      } else {
-        for (int32_t f = 0; f < d; ++f) obb[f] = 0.0;
       }
       m = mn;
       have_m = 1;
@@ -754,7 +772,7 @@ static void emu_head(void* c, int32_t item) {
           flush_slack += 2.0 * pbar;
         } else {
           pbv = (double)orc_f32_from_bf16(orc_bf16_from_f64(pbar));
-          if (orc_bf16_boundary_distance(pbar) <= (rho + 2.0 * U24) * pbar) row_cert = 0;
+          if (cert_on && orc_bf16_boundary_distance(pbar) <= (rho + 2.0 * U24) * pbar) val_cert = 0;
         }
         if (pbv == 1.0) {
           if (tie) exb |= ORC_EX_PBAR_ONE_TIED;
@@ -765,7 +783,10 @@ static void emu_head(void* c, int32_t item) {
         float p32 = (pbar < under) ? 0.0f : (float)pbar;
         l32 = l32 + p32;
       }
-      /* 3c. Ō <- cŌ + sum P̄_bf16 V, one rounding per block in bf16 mode */
+      /* 3c. Ō <- cŌ + sum P̄_bf16 V in an fp32 accumulator; in bf16 mode the
+       * accumulator is rounded to bf16 after every round_n keys and after the
+       * row's last block */
+      const int round_here = !sc->obar_fp32 && ((j1 % rn) == 0 || j1 == n);
       for (int32_t f = 0; f < d; ++f) {
         double vmax = 0.0;
         for (int32_t j = j0; j < j1; ++j) {
@@ -773,24 +794,20 @@ static void emu_head(void* c, int32_t item) {
           terms[j - j0] = pb[j - j0] * vv; /* exact: 8-bit x 8-bit mantissas */
           vmax = fmax(vmax, fabs(vv));
         }
-        double exact;
-        double c0 = ob[f];
-        double bound = obb[f] + chain_bound(sc, c0, terms, nt) + flush_slack * vmax;
-        /* RNE of the exact c0 + sum(terms) */
-        uint16_t hb;
-        {
-          dd_t acc = {0.0, 0.0};
-          dd_add(&acc, c0);
-          for (int32_t j = 0; j < nt; ++j) dd_add(&acc, terms[j]);
-          exact = acc.hi + acc.lo;
-          hb = dd_to_bf16(acc);
-        }
-        if (sc->obar_fp32) {
-          ob[f] = exact;
-          oc[f] = 0; /* no bit claim in fp32 mode */
-        } else {
+        if (cert_on) obb[f] += chain_bound(sc, ob[f], terms, nt) + flush_slack * vmax;
+        dd_t acc = {0.0, 0.0};
+        dd_add(&acc, ob[f]);
+        for (int32_t j = 0; j < nt; ++j) dd_add(&acc, terms[j]);
+        double exact = acc.hi + acc.lo;
+        if (round_here) {
+          uint16_t hb = dd_to_bf16(acc);
+          if (!dec_cert || !val_cert || orc_bf16_boundary_distance(exact) <= obb[f]) oc[f] = 0;
           ob[f] = (double)orc_f32_from_bf16(hb);
-          if (!row_cert || orc_bf16_boundary_distance(exact) <= bound) oc[f] = 0;
+          obb[f] = 0.0;
+        } else {
+          ob[f] = exact;
+          obb[f] += 0x1p-52 * fabs(exact);
+          if (sc->obar_fp32) oc[f] = 0; /* no bit claim in fp32 mode */
         }
       }
     }
@@ -801,7 +818,7 @@ static void emu_head(void* c, int32_t item) {
     if (tie && p->guard != ORC_GUARD_NONE) fl |= ORC_ROW_GUARD_APPLIED;
     if (l32 == 0.0f) fl |= ORC_ROW_ZERO_DENOM;
     if (x->flags) x->flags[ro] = fl;
-    if (x->flag_cert) x->flag_cert[ro] = (uint8_t)(row_cert && !zero_ambig);
+    if (x->flag_cert) x->flag_cert[ro] = (uint8_t)(dec_cert && !zero_ambig);
     if (x->ex) x->ex[ro] = exb;
     if (x->m) x->m[ro] = m;
     if (x->l) x->l[ro] = l32;
@@ -833,7 +850,8 @@ int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
   int rc = check_problem(p);
   if (rc) return rc;
   if (!s || !q || !k || !v) return -1;
-  if (s->block_n < 0) return -4;
+  if (s->block_n < 0 || s->round_n < 0) return -4;
+  if (s->block_n > 0 && s->round_n > 0 && s->round_n % s->block_n != 0) return -4;
   emu_ctx c = {p, s, q, k, v, heads, obar, o, obar_cert, m, l, flags, flag_cert, ex};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
   run_pool(emu_head, &c, n, nthreads);

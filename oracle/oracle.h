@@ -51,11 +51,16 @@ typedef struct {
   float shift_eps;    /* extra shift of the eps-guard                          */
 } orc_problem;
 
-/* How the kernel under test rounds; used only to decide which emulated values
- * are certain (far enough from a rounding boundary) -- never to change them. */
+/* The rounding schedule to replay (block_n, round_n, obar_fp32) and the error
+ * model of the kernel under test (the other fields), which only decides which
+ * emulated values are certain -- never changes them. */
 typedef struct {
-  int32_t block_n;        /* keys per streaming step = Ō rounding block       */
-  int32_t obar_fp32;      /* 0: Ō rounded to bf16 after every block; 1: fp32   */
+  int32_t block_n;        /* keys per streaming step (tie decision and shift)  */
+  int32_t round_n;        /* bf16 mode: Ō is rounded to bf16 after every
+                             round_n keys (a multiple of block_n; 0 = block_n)
+                             and after the row's last block                  */
+  int32_t obar_fp32;      /* 0: Ō rounded to bf16 (see round_n); 1: fp32      */
+  int32_t certify;        /* 0: skip the certification (fast; all cert = 0)   */
   int32_t ftz;            /* 1: exp results below 2^-126 flush to zero         */
   /* Sums computed by the kernel's matrix instructions: a chain of steps, each
    * adding `chunk` terms to the running value C, with the per-step error
@@ -119,7 +124,8 @@ int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
  *   obar      final Ō (bf16-valued in bf16 mode), obar_cert 1 = certain
  *   o         RNE_bf16(Ō/ℓ) as double
  *   m, l      final shift and fp32 denominator; flags = ORC_ROW_* bits
- *   flag_cert 1 = every streaming tie decision of the row is certain
+ *   flag_cert 1 = every streaming tie decision of the row (and its zero-
+ *             denominator outcome) is certain
  *   ex        ORC_EX_* bits                                                 */
 int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
                 const uint16_t* k, const uint16_t* v, const int32_t* heads,

@@ -1,0 +1,119 @@
+"""The C-ABI library loads on the CPU host, exports every function that
+include/attn.h declares, and rejects bad arguments before touching a GPU
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_fa_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        from flashattention_fa_fwd_amd import build_lib
+        build_lib.build()
+    return fa.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*(attn_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert {"attn_fwd", "attn_bwd", "attn_schedule", "attn_bwd_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(L):
+    assert fa.attn_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
+    assert fa.attn_strerror(-99) == "unknown error code"
+
+
+def test_schedule(L):
+    p = fa.make_params(1, 1, 1, 128, 64)
+    assert fa.attn_schedule(p) == dict(block_m=128, block_n=64, round_n=512, chunk=16)
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced
+
+
+def _fwd(L, p, ptrs=None, obar=None):
+    ptrs = ptrs or [FAKE] * 7
+    vp = [ctypes.c_void_p(x) for x in ptrs]
+    return L.attn_fwd(ctypes.byref(p), *vp, ctypes.c_void_p(obar), None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -2), (dict(heads_q=3, heads_kv=2), -2), (dict(seqlen=0), -2),
+    (dict(head_dim=96), -3), (dict(head_dim=32), -3),
+])
+def test_shape_errors(L, kw, code):
+    args = dict(batch=1, heads_q=2, heads_kv=1, seqlen=64, head_dim=64)
+    args.update(kw)
+    p = fa.make_params(args["batch"], args["heads_q"], args["heads_kv"], args["seqlen"], args["head_dim"])
+    assert _fwd(L, p) == code
+
+
+def test_param_errors(L):
+    p = fa.make_params(1, 1, 1, 64, 64, guard="beta", beta=1.0)
+    assert _fwd(L, p) == -4
+    p = fa.make_params(1, 1, 1, 64, 64, guard="eps", shift_eps=0.0)
+    assert _fwd(L, p) == -4
+    p = fa.make_params(1, 1, 1, 64, 64, tie_eps=-1.0)
+    assert _fwd(L, p) == -4
+    p = fa.make_params(1, 1, 1, 64, 64)
+    p.flags = fa.GUARD_BETA | fa.GUARD_EPS
+    assert _fwd(L, p) == -4
+    p.flags = 0x100
+    assert _fwd(L, p) == -4
+    p = fa.make_params(1, 1, 1, 64, 64, softmax_scale=float("nan"))
+    assert _fwd(L, p) == -4
+    # beta is only checked when the beta guard is on
+    p = fa.make_params(1, 1, 1, 64, 64, guard="none", beta=0.5)
+    assert fa.attn_schedule(p)["block_n"] == 64
+
+
+def test_null_and_alignment_errors(L):
+    p = fa.make_params(1, 1, 1, 64, 64)
+    assert L.attn_fwd(None, *([ctypes.c_void_p(FAKE)] * 7), None, None, None) == -1
+    ptrs = [FAKE] * 7
+    ptrs[0] = 0
+    assert _fwd(L, p, ptrs) == -1
+    ptrs = [FAKE] * 7
+    ptrs[1] = FAKE + 2
+    assert _fwd(L, p, ptrs) == -3
+    assert _fwd(L, p, obar=FAKE + 8) == -3
+
+
+def test_workspace_errors(L):
+    p = fa.make_params(2, 4, 2, 100, 64)
+    need = fa.attn_bwd_workspace_bytes(p)
+    assert need == 2 * 4 * 100 * 64 * 4
+    vp = ctypes.c_void_p
+    args = [vp(FAKE)] * 11
+    assert L.attn_bwd(ctypes.byref(p), *args, None, need, None) == -5          # no workspace
+    assert L.attn_bwd(ctypes.byref(p), *args, vp(FAKE), need - 4, None) == -5  # too small
+    assert L.attn_bwd(ctypes.byref(p), *args, vp(FAKE + 16), need, None) == -5  # misaligned
+    assert L.attn_bwd_finalize(ctypes.byref(p), vp(FAKE), None, need, None) == -5
+    bad = fa.make_params(1, 3, 2, 10, 64)
+    assert fa.attn_bwd_workspace_bytes(bad) == 0
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    """Without the library the binding raises instead of computing anything."""
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(ImportError):
+        fa.lib()
