@@ -1,0 +1,198 @@
+"""Benchmark: guarded BF16 attention forward+backward at the GPT-2 Small
+attention shape (B=16, H=12, N=1024, d=64, causal, beta = 2 guard, bf16 Ō)
+on one MI355X.
+
+One step = attn_fwd + attn_bwd (every stage of the path) over one batch of
+synthetic inputs that are resident in device memory before timing starts.
+Prints one JSON line (see the keys below).  The CPU oracle's FP64
+forward+backward is timed on a bounded sample of heads as a baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload gpt2s]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2s")
+    ap.add_argument("--guard", default="beta", choices=["none", "beta", "eps"])
+    ap.add_argument("--obar-fp32", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="KV heads in the CPU oracle's bounded sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import flashattention_fa_fwd_amd as fa
+    from flashattention_fa_fwd_amd import workloads as W
+
+    fa.lib()  # fails loudly when the HIP library is not built
+    x = W.make(args.workload)
+    wl = x["workload"]
+    dev = "cuda"
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["do"])
+    kw = dict(causal=wl.causal, guard=args.guard)
+    p = fa.make_params(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim,
+                       obar_fp32=args.obar_fp32, **kw)
+    ws = fa.alloc_workspace(p, q.device)
+    fout, bout = {}, {}
+    fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
+    fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], workspace=ws, out=bout, **kw)
+    torch.cuda.synchronize()
+
+    def step():
+        fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
+        fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], workspace=ws, out=bout, **kw)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, iters, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters  # ms
+
+    # ---- the timed region: exactly K steps, synchronised on both sides
+    ms_step = timed(step, args.steps, args.warmup)
+    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations (HIP events on the launch stream)
+    n_rep = max(20, args.steps)
+    ms_fwd = timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw), n_rep, 3)
+    delta = bout["delta"]
+    ms_pre = timed(lambda: fa.attn_bwd_preprocess(p, fout["o"], do, delta, ws), n_rep, 3)
+    ms_main = timed(lambda: fa.attn_bwd_main(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
+                                             bout["dk"], bout["dv"], ws), n_rep, 3)
+    ms_fin = timed(lambda: fa.attn_bwd_finalize(p, bout["dq"], ws), n_rep, 3)
+    other = "none" if args.guard != "none" else "beta"
+    fo2 = {}
+    ms_fwd_other = timed(lambda: fa.attn_fwd(q, k, v, causal=wl.causal, guard=other, out=fo2), n_rep, 3)
+    print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_pre {ms_pre:.4f}, bwd_main {ms_main:.4f}, "
+          f"bwd_post {ms_fin:.4f}; fwd with guard={other}: {ms_fwd_other:.4f}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    fl_fwd = wl.flops_fwd()
+    fl_bwd = 2.5 * fl_fwd
+    fl_step = fl_fwd + fl_bwd
+    value = fl_step / (ms_step * 1e-3) / 1e12
+    kernels = {
+        "attn_fwd": (ms_fwd, fl_fwd),
+        "bwd_main": (ms_main, fl_bwd),
+    }
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dms, dfl = kernels[dom]
+    achieved = dfl / (dms * 1e-3) / 1e12
+    rec = {
+        "metric": "attn fwd+bwd TFLOP/s (BF16, guarded) at GPT-2 shape; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.description,
+            "batch": wl.batch, "heads_q": wl.heads_q, "heads_kv": wl.heads_kv,
+            "seq_len": wl.seqlen, "head_dim": wl.head_dim, "causal": wl.causal,
+            "guard": args.guard, "beta": 2.0, "obar": "fp32" if args.obar_fp32 else "bf16",
+            "flops_per_step": fl_step,
+        },
+        "pct_of_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "fwd_tflops": round(fl_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(fl_bwd / ((ms_pre + ms_main + ms_fin) * 1e-3) / 1e12, 2),
+        "kernel_ms": {"attn_fwd": round(ms_fwd, 5), "bwd_pre": round(ms_pre, 5),
+                      "bwd_main": round(ms_main, 5), "bwd_post": round(ms_fin, 5)},
+        "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, wl, args)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(x, wl, args):
+    """The FP64 oracle (forward+backward of softmax attention) on a bounded
+    sample: the first --cpu-heads KV heads of the same workload, all host
+    threads.  Scaled to TFLOP/s with the same counted work per head."""
+    import oracle as orc
+
+    nthreads = os.cpu_count() or 1
+    heads = list(range(min(args.cpu_heads, wl.batch * wl.heads_kv)))
+    p = orc.Problem(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim, wl.causal,
+                    {"none": 0, "beta": 1, "eps": 2}[args.guard])
+    t0 = time.perf_counter()
+    orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], kv_heads=heads, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    g = wl.heads_q // wl.heads_kv
+    frac = len(heads) * g / (wl.batch * wl.heads_q)
+    flops = 3.5 * wl.flops_fwd() * frac
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": min(nthreads, len(heads)),
+        "kind": "oracle",
+        "sample": f"FP64 forward+backward of {len(heads)} of {wl.batch * wl.heads_kv} KV heads "
+                  f"({len(heads) * g} query heads) of the {wl.name} workload, {dt:.2f} s wall",
+    }
+
+
+if __name__ == "__main__":
+    main()

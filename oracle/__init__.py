@@ -132,12 +132,22 @@ def lib():
         L.orc_fwd_f64.argtypes = [pp, u16p, u16p, u16p, i32p, ctypes.c_int32, f64p, f64p, ctypes.c_int32]
         L.orc_bwd_f64.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, ctypes.c_int32,
                                   f64p, f64p, f64p, f64p, f64p, ctypes.c_int32]
+        L.orc_bwd_rows_f64.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
+                                       f64p, f64p, f64p, ctypes.c_int32]
+        L.orc_bwd_emu.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, ctypes.c_int32, f64p,
+                                  ctypes.c_int32, f64p, f64p, f64p, f64p, ctypes.c_int32]
+        L.orc_bwd_rows_emu.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
+                                       f64p, ctypes.c_int32, f64p, f64p, ctypes.c_int32]
+        L.orc_fwd_emu_rows.argtypes = [pp, sp, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
+                                       f64p, f32p, f32p, u8p, ctypes.c_int32]
         L.orc_row_stats.argtypes = [pp, sp, u16p, u16p, i32p, ctypes.c_int32,
                                     f32p, f32p, f32p, u8p, u8p, ctypes.c_int32]
         L.orc_obar_f64.argtypes = [pp, u16p, u16p, u16p, f32p, i32p, ctypes.c_int32, f64p, f64p, ctypes.c_int32]
         L.orc_fwd_emu.argtypes = [pp, sp, u16p, u16p, u16p, i32p, ctypes.c_int32,
                                   f64p, u8p, f64p, f32p, f32p, u8p, u8p, u8p, ctypes.c_int32]
-        for name in ("orc_fwd_f64", "orc_bwd_f64", "orc_row_stats", "orc_obar_f64", "orc_fwd_emu"):
+        for name in ("orc_fwd_f64", "orc_bwd_f64", "orc_bwd_rows_f64", "orc_row_stats",
+                     "orc_obar_f64", "orc_fwd_emu", "orc_bwd_emu", "orc_bwd_rows_emu",
+                     "orc_fwd_emu_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -244,6 +254,79 @@ def bwd_f64(p: Problem, q, k, v, dout, kv_heads=None, nthreads=None):
                              _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double), _threads(nthreads)),
            "orc_bwd_f64")
     return dict(o=o, delta=delta, dq=dq, dk=dk, dv=dv)
+
+
+def bwd_rows_f64(p: Problem, q, k, v, dout, qheads, rows, nthreads=None):
+    """o, delta, dq (double) for single rows: row rows[i] of query head qheads[i]."""
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    qh = np.ascontiguousarray(np.asarray(qheads, dtype=np.int32))
+    rw = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    n = int(qh.size)
+    d = q.shape[-1]
+    o = np.zeros((n, d), np.float64); delta = np.zeros(n, np.float64); dq = np.zeros((n, d), np.float64)
+    pc = p.c()
+    _check(lib().orc_bwd_rows_f64(ctypes.byref(pc), _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                  _ptr(v, ctypes.c_uint16), _ptr(dout, ctypes.c_uint16),
+                                  _ptr(qh, ctypes.c_int32), _ptr(rw, ctypes.c_int32), n,
+                                  _ptr(o, ctypes.c_double), _ptr(delta, ctypes.c_double),
+                                  _ptr(dq, ctypes.c_double), _threads(nthreads)), "orc_bwd_rows_f64")
+    return dict(o=o, delta=delta, dq=dq)
+
+
+def bwd_emu(p: Problem, q, k, v, dout, o_in=None, round_ops=True, kv_heads=None, nthreads=None):
+    """Backward replayed at the method's rounding points (see oracle.h):
+    delta from o_in (None = exact O), bf16 P/dS operands when round_ops."""
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    oi = None if o_in is None else np.ascontiguousarray(np.asarray(o_in, np.float64))
+    if oi is not None:
+        assert oi.shape == q.shape
+    delta = np.zeros(q.shape[:-1], np.float64)
+    dq = np.zeros(q.shape, np.float64); dk = np.zeros(k.shape, np.float64); dv = np.zeros(v.shape, np.float64)
+    h, nh = _heads_arg(kv_heads)
+    pc = p.c()
+    _check(lib().orc_bwd_emu(ctypes.byref(pc), _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                             _ptr(v, ctypes.c_uint16), _ptr(dout, ctypes.c_uint16), _ptr(h, ctypes.c_int32),
+                             nh, _ptr(oi, ctypes.c_double), int(bool(round_ops)),
+                             _ptr(delta, ctypes.c_double), _ptr(dq, ctypes.c_double),
+                             _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double), _threads(nthreads)),
+           "orc_bwd_emu")
+    return dict(delta=delta, dq=dq, dk=dk, dv=dv)
+
+
+def bwd_rows_emu(p: Problem, q, k, v, dout, qheads, rows, o_in=None, round_ops=True, nthreads=None):
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    qh = np.ascontiguousarray(np.asarray(qheads, dtype=np.int32))
+    rw = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    n, d = int(qh.size), q.shape[-1]
+    oi = None if o_in is None else np.ascontiguousarray(np.asarray(o_in, np.float64))
+    if oi is not None:
+        assert oi.shape == (n, d)
+    delta = np.zeros(n, np.float64); dq = np.zeros((n, d), np.float64)
+    pc = p.c()
+    _check(lib().orc_bwd_rows_emu(ctypes.byref(pc), _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                  _ptr(v, ctypes.c_uint16), _ptr(dout, ctypes.c_uint16),
+                                  _ptr(qh, ctypes.c_int32), _ptr(rw, ctypes.c_int32), n,
+                                  _ptr(oi, ctypes.c_double), int(bool(round_ops)),
+                                  _ptr(delta, ctypes.c_double), _ptr(dq, ctypes.c_double),
+                                  _threads(nthreads)), "orc_bwd_rows_emu")
+    return dict(delta=delta, dq=dq)
+
+
+def fwd_emu_rows(p: Problem, sched: Schedule, q, k, v, qheads, rows, nthreads=None):
+    """Streaming emulation of listed rows only (no certification)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    qh = np.ascontiguousarray(np.asarray(qheads, dtype=np.int32))
+    rw = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    n, d = int(qh.size), q.shape[-1]
+    o = np.zeros((n, d), np.float64); m = np.zeros(n, np.float32); l = np.zeros(n, np.float32)
+    fl = np.zeros(n, np.uint8)
+    pc, sc = p.c(), sched.c()
+    _check(lib().orc_fwd_emu_rows(ctypes.byref(pc), ctypes.byref(sc), _ptr(q, ctypes.c_uint16),
+                                  _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+                                  _ptr(qh, ctypes.c_int32), _ptr(rw, ctypes.c_int32), n,
+                                  _ptr(o, ctypes.c_double), _ptr(m, ctypes.c_float), _ptr(l, ctypes.c_float),
+                                  _ptr(fl, ctypes.c_uint8), _threads(nthreads)), "orc_fwd_emu_rows")
+    return dict(o=o, m=m, l=l, flags=fl)
 
 
 def row_stats(p: Problem, q, k, sched: Schedule | None = None, heads=None, nthreads=None):

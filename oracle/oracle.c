@@ -374,7 +374,12 @@ typedef struct {
   const uint16_t *q, *k, *v, *dout;
   const int32_t* kv_heads;
   double *o, *delta, *dq, *dk, *dv;
+  const double* o_in; /* nullable: the O that delta is computed from       */
+  int round_ops;      /* 1: P and dS rounded to bf16 as matrix operands      */
 } bwd64_ctx;
+
+/* bf16 value of x (RNE), as a double: the matrix-operand rounding. */
+static double bf16_round_d(double x) { return (double)orc_f32_from_bf16(orc_bf16_from_f64(x)); }
 
 static void bwd64_kvhead(void* c, int32_t item) {
   bwd64_ctx* x = (bwd64_ctx*)c;
@@ -419,8 +424,10 @@ static void bwd64_kvhead(void* c, int32_t item) {
         orow[f] = acc;
         dorow[f] = (double)orc_f32_from_bf16(dO[(size_t)i * d + f]);
       }
+      size_t rbase = q_head_offset(p, qh) + (size_t)i * d;
+      const double* odelta = x->o_in ? x->o_in + rbase : orow;
       double delta = 0.0;
-      for (int32_t f = 0; f < d; ++f) delta += dorow[f] * orow[f];
+      for (int32_t f = 0; f < d; ++f) delta += dorow[f] * odelta[f];
       memset(dqrow, 0, sizeof(double) * (size_t)d);
       for (int32_t j = 0; j < n; ++j) {
         const uint16_t* kj = K + (size_t)j * d;
@@ -428,12 +435,17 @@ static void bwd64_kvhead(void* c, int32_t item) {
         double dp = 0.0;
         for (int32_t f = 0; f < d; ++f) dp += dorow[f] * (double)orc_f32_from_bf16(vj[f]);
         double ds = P[j] * (dp - delta);
+        double pj = P[j];
+        if (x->round_ops) {
+          ds = bf16_round_d(ds);
+          pj = bf16_round_d(pj);
+        }
         for (int32_t f = 0; f < d; ++f) dqrow[f] += alpha * ds * (double)orc_f32_from_bf16(kj[f]);
         if (dK)
           for (int32_t f = 0; f < d; ++f)
             dK[(size_t)j * d + f] += alpha * ds * (double)orc_f32_from_bf16(qi[f]);
         if (dV)
-          for (int32_t f = 0; f < d; ++f) dV[(size_t)j * d + f] += P[j] * dorow[f];
+          for (int32_t f = 0; f < d; ++f) dV[(size_t)j * d + f] += pj * dorow[f];
       }
       size_t ro = q_head_offset(p, qh) + (size_t)i * d;
       if (x->o) memcpy(x->o + ro, orow, sizeof(double) * (size_t)d);
@@ -454,9 +466,117 @@ int orc_bwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   int rc = check_problem(p);
   if (rc) return rc;
   if (!q || !k || !v || !dout) return -1;
-  bwd64_ctx c = {p, q, k, v, dout, kv_heads, o, delta, dq, dk, dv};
+  bwd64_ctx c = {p, q, k, v, dout, kv_heads, o, delta, dq, dk, dv, NULL, 0};
   int32_t n = kv_heads ? nkv : p->batch * p->heads_kv;
   run_pool(bwd64_kvhead, &c, n, nthreads);
+  return 0;
+}
+
+/* The same backward replayed at the method's rounding points: delta from a
+ * given O (the bf16 output of the forward), and P (for dV) and dS (for dK,
+ * dQ) rounded to bf16 as the operands of the products; everything else in
+ * double.  Used to measure the method's own error against the definition. */
+int orc_bwd_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, const uint16_t* dout, const int32_t* kv_heads,
+                int32_t nkv, const double* o_in, int32_t round_ops, double* delta,
+                double* dq, double* dk, double* dv, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout) return -1;
+  bwd64_ctx c = {p, q, k, v, dout, kv_heads, NULL, delta, dq, dk, dv, o_in, round_ops};
+  int32_t n = kv_heads ? nkv : p->batch * p->heads_kv;
+  run_pool(bwd64_kvhead, &c, n, nthreads);
+  return 0;
+}
+
+typedef struct {
+  const orc_problem* p;
+  const uint16_t *q, *k, *v, *dout;
+  const int32_t *qheads, *rows;
+  double *o, *delta, *dq;
+  const double* o_in; /* nullable: [n, d] O rows that delta is computed from */
+  int round_ops;      /* 1: dS rounded to bf16 as the dQ operand            */
+} bwdrow_ctx;
+
+/* One query row of the backward above, written out the same way. */
+static void bwdrow_item(void* c, int32_t item) {
+  bwdrow_ctx* x = (bwdrow_ctx*)c;
+  const orc_problem* p = x->p;
+  int32_t qh = x->qheads[item], i = x->rows[item];
+  int32_t d = p->head_dim;
+  const uint16_t* qi = x->q + q_head_offset(p, qh) + (size_t)i * d;
+  const uint16_t* doi = x->dout + q_head_offset(p, qh) + (size_t)i * d;
+  const uint16_t* K = x->k + kv_head_offset(p, qh);
+  const uint16_t* V = x->v + kv_head_offset(p, qh);
+  double alpha = (double)p->alpha;
+  int32_t n = visible(p, i);
+  double* P = (double*)malloc(sizeof(double) * (size_t)n);
+  double mx = -INFINITY;
+  for (int32_t j = 0; j < n; ++j) {
+    P[j] = alpha * dot_bf16(qi, K + (size_t)j * d, d);
+    if (P[j] > mx) mx = P[j];
+  }
+  double z = 0.0;
+  for (int32_t j = 0; j < n; ++j) {
+    P[j] = exp(P[j] - mx);
+    z += P[j];
+  }
+  for (int32_t j = 0; j < n; ++j) P[j] /= z;
+  double* orow = x->o + (size_t)item * d;
+  double* dqrow = x->dq + (size_t)item * d;
+  for (int32_t f = 0; f < d; ++f) {
+    double acc = 0.0;
+    for (int32_t j = 0; j < n; ++j) acc += P[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+    orow[f] = acc;
+    dqrow[f] = 0.0;
+  }
+  const double* odelta = x->o_in ? x->o_in + (size_t)item * d : orow;
+  double delta = 0.0;
+  for (int32_t f = 0; f < d; ++f) delta += (double)orc_f32_from_bf16(doi[f]) * odelta[f];
+  for (int32_t j = 0; j < n; ++j) {
+    double dp = 0.0;
+    for (int32_t f = 0; f < d; ++f)
+      dp += (double)orc_f32_from_bf16(doi[f]) * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+    double ds = P[j] * (dp - delta);
+    if (x->round_ops) ds = bf16_round_d(ds);
+    for (int32_t f = 0; f < d; ++f) dqrow[f] += alpha * ds * (double)orc_f32_from_bf16(K[(size_t)j * d + f]);
+  }
+  x->delta[item] = delta;
+  free(P);
+}
+
+int orc_bwd_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                     const int32_t* rows, int32_t n, double* o, double* delta, double* dq,
+                     int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout || !qheads || !rows || !o || !delta || !dq) return -1;
+  for (int32_t i = 0; i < n; ++i) {
+    if (qheads[i] < 0 || qheads[i] >= p->batch * p->heads_q) return -2;
+    if (rows[i] < 0 || rows[i] >= p->seqlen) return -2;
+  }
+  bwdrow_ctx c = {p, q, k, v, dout, qheads, rows, o, delta, dq, NULL, 0};
+  run_pool(bwdrow_item, &c, n, nthreads);
+  return 0;
+}
+
+/* Single rows replayed at the method's rounding points (see orc_bwd_emu). */
+int orc_bwd_rows_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                     const int32_t* rows, int32_t n, const double* o_in, int32_t round_ops,
+                     double* delta, double* dq, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout || !qheads || !rows || !delta || !dq) return -1;
+  for (int32_t i = 0; i < n; ++i) {
+    if (qheads[i] < 0 || qheads[i] >= p->batch * p->heads_q) return -2;
+    if (rows[i] < 0 || rows[i] >= p->seqlen) return -2;
+  }
+  double* otmp = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)p->head_dim);
+  bwdrow_ctx c = {p, q, k, v, dout, qheads, rows, otmp, delta, dq, o_in, round_ops};
+  run_pool(bwdrow_item, &c, n, nthreads);
+  free(otmp);
   return 0;
 }
 
@@ -661,6 +781,7 @@ typedef struct {
   uint8_t* obar_cert;
   float *m, *l;
   uint8_t *flags, *flag_cert, *ex;
+  const int32_t *rows_qh, *rows_i; /* row list mode: item = one (head, row) */
 } emu_ctx;
 
 static void emu_head(void* c, int32_t item) {
@@ -669,6 +790,12 @@ static void emu_head(void* c, int32_t item) {
   const orc_schedule* sc = x->s;
   int32_t qh = x->heads ? x->heads[item] : item;
   int32_t N = p->seqlen, d = p->head_dim;
+  int32_t i_begin = 0, i_end = N;
+  if (x->rows_qh) { /* one listed row; outputs indexed by the list position */
+    qh = x->rows_qh[item];
+    i_begin = x->rows_i[item];
+    i_end = i_begin + 1;
+  }
   int32_t bn = sc->block_n > 0 ? sc->block_n : N;
   int32_t rn = sc->round_n > 0 ? sc->round_n : bn;
   const int cert_on = sc->certify != 0;
@@ -690,7 +817,7 @@ static void emu_head(void* c, int32_t item) {
   double* terms = (double*)malloc(sizeof(double) * (size_t)(bn > d ? bn : d));
   uint8_t* oc = (uint8_t*)malloc((size_t)d);
 
-  for (int32_t i = 0; i < N; ++i) {
+  for (int32_t i = i_begin; i < i_end; ++i) {
     int32_t n = visible(p, i);
     const uint16_t* qi = Q + (size_t)i * d;
     for (int32_t j = 0; j < n; ++j) {
@@ -812,7 +939,7 @@ static void emu_head(void* c, int32_t item) {
       }
     }
     /* end of row: flags and O = RNE_bf16(fl32(Ō / ℓ)) */
-    size_t ro = (size_t)qh * N + i;
+    size_t ro = x->rows_qh ? (size_t)item : (size_t)qh * N + i;
     uint8_t fl = 0;
     if (tie) fl |= ORC_ROW_TIE;
     if (tie && p->guard != ORC_GUARD_NONE) fl |= ORC_ROW_GUARD_APPLIED;
@@ -852,8 +979,28 @@ int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
   if (!s || !q || !k || !v) return -1;
   if (s->block_n < 0 || s->round_n < 0) return -4;
   if (s->block_n > 0 && s->round_n > 0 && s->round_n % s->block_n != 0) return -4;
-  emu_ctx c = {p, s, q, k, v, heads, obar, o, obar_cert, m, l, flags, flag_cert, ex};
+  emu_ctx c = {p, s, q, k, v, heads, obar, o, obar_cert, m, l, flags, flag_cert, ex, NULL, NULL};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
+  run_pool(emu_head, &c, n, nthreads);
+  return 0;
+}
+
+int orc_fwd_emu_rows(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
+                     const uint16_t* k, const uint16_t* v, const int32_t* qheads,
+                     const int32_t* rows, int32_t n, double* o, float* m, float* l,
+                     uint8_t* flags, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!s || !q || !k || !v || !qheads || !rows) return -1;
+  if (s->block_n < 0 || s->round_n < 0) return -4;
+  if (s->block_n > 0 && s->round_n > 0 && s->round_n % s->block_n != 0) return -4;
+  for (int32_t i = 0; i < n; ++i) {
+    if (qheads[i] < 0 || qheads[i] >= p->batch * p->heads_q) return -2;
+    if (rows[i] < 0 || rows[i] >= p->seqlen) return -2;
+  }
+  orc_schedule s2 = *s;
+  s2.certify = 0;
+  emu_ctx c = {p, &s2, q, k, v, NULL, NULL, o, NULL, m, l, flags, NULL, NULL, qheads, rows};
   run_pool(emu_head, &c, n, nthreads);
   return 0;
 }

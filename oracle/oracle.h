@@ -102,6 +102,29 @@ int orc_bwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
                 int32_t nkv, double* o, double* delta, double* dq, double* dk,
                 double* dv, int32_t nthreads);
 
+/* The same backward for single query rows: o, delta and dq of row rows[i]
+ * of query head qheads[i] (each row's dQ needs only that row).  Outputs are
+ * [n, head_dim], [n], [n, head_dim].                                       */
+int orc_bwd_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                     const int32_t* rows, int32_t n, double* o, double* delta, double* dq,
+                     int32_t nthreads);
+
+/* The backward replayed at the method's rounding points: delta computed from
+ * o_in (the forward's bf16 output, [B,Hq,N,d]; NULL = exact O) and, with
+ * round_ops, P (for dV) and dS (for dK, dQ) rounded to bf16 as the products'
+ * operands; all else in double.  Measures the method's own deviation from
+ * orc_bwd_f64 (its floor), not the kernel's.                               */
+int orc_bwd_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                const uint16_t* v, const uint16_t* dout, const int32_t* kv_heads,
+                int32_t nkv, const double* o_in, int32_t round_ops, double* delta,
+                double* dq, double* dk, double* dv, int32_t nthreads);
+/* Single-row version: o_in is [n, head_dim] (the rows' O), outputs [n], [n,d]. */
+int orc_bwd_rows_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                     const int32_t* rows, int32_t n, const double* o_in, int32_t round_ops,
+                     double* delta, double* dq, int32_t nthreads);
+
 /* Row statistics on the fp32 scaled logits t = fl32(alpha * fl32(s)):
  * r = max, r2 = second largest (multiset), tie flag, final shift m.
  * flag_cert[i] = 1 when the kernel's score error (orc_schedule's model of
@@ -132,6 +155,14 @@ int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
                 int32_t nheads, double* obar, uint8_t* obar_cert, double* o,
                 float* m, float* l, uint8_t* flags, uint8_t* flag_cert,
                 uint8_t* ex, int32_t nthreads);
+
+/* The same emulation for listed rows only (row rows[i] of query head
+ * qheads[i]), without certification; outputs indexed by list position:
+ * o [n, head_dim], m, l, flags [n] (each nullable).                        */
+int orc_fwd_emu_rows(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
+                     const uint16_t* k, const uint16_t* v, const int32_t* qheads,
+                     const int32_t* rows, int32_t n, double* o, float* m, float* l,
+                     uint8_t* flags, int32_t nthreads);
 
 #ifdef __cplusplus
 }

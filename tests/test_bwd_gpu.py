@@ -1,0 +1,197 @@
+"""Backward parity on the GPU: attn_fwd followed by attn_bwd (through the C
+ABI) against the FP64 oracle's gradient of softmax attention."""
+import numpy as np
+import pytest
+import torch
+
+import flashattention_fa_fwd_amd as fa
+import oracle as orc
+from flashattention_fa_fwd_amd import workloads as W
+
+from _util import (MAX_REL, MEAN_EXCESS, MEAN_REL, dev, f32, make, problem, rel_errors, report,
+                   schedule, threads)
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd_bwd(x, guard, beta=2.0, obar_fp32=False):
+    wl = x["workload"]
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"])
+    f = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard, beta=beta, obar_fp32=obar_fp32)
+    b = fa.attn_bwd(q, k, v, f["o"], do, f["row_m"], f["row_l"], causal=wl.causal, guard=guard,
+                    beta=beta)
+    torch.cuda.synchronize()
+    return f, b
+
+
+def _check(name, gpu, ref, floor=None):
+    """Against FP64: max rel <= 1e-2 and mean rel <= 2e-3.  Where the
+    method's own rounding points (delta from the bf16 O, bf16 P and dS as
+    matrix operands) already put its exact replay above that, the bound is
+    that replay's error (floor, from the oracle) plus a small allowance for
+    the kernel's fp32 accumulation."""
+    mx, mean = rel_errors(gpu, ref)
+    bmax, bmean = MAX_REL, MEAN_REL
+    if floor is not None:
+        bmax = max(MAX_REL, 1.25 * floor[0])
+        bmean = max(MEAN_REL, 1.1 * floor[1] + MEAN_EXCESS)
+    assert mx <= bmax, (name, "max rel", mx, "bound", bmax, "floor", floor)
+    assert mean <= bmean, (name, "mean rel", mean, "bound", bmean, "floor", floor)
+    out = {f"{name}_max": f"{mx:.2e}", f"{name}_mean": f"{mean:.2e}"}
+    if floor is not None:
+        out[f"{name}_floor"] = f"{floor[0]:.2e}/{floor[1]:.2e}"
+    return out
+
+
+def _floors(p, x, ref, obar_fp32=False, kv_heads=None, qheads=None, kvsel=None):
+    """The method's own deviation from FP64 for dq, dk, dv, delta: the
+    oracle's backward replay with delta from the oracle's emulated bf16 O."""
+    e = orc.fwd_emu(p, schedule(p, obar_fp32, certify=False), x["q"], x["k"], x["v"], heads=qheads,
+                    nthreads=threads())
+    rep = orc.bwd_emu(p, x["q"], x["k"], x["v"], x["do"], o_in=e["o"], round_ops=True,
+                      kv_heads=kv_heads, nthreads=threads())
+    wl = x["workload"]
+    qs = (-1, wl.seqlen, wl.head_dim)
+    out = {}
+    for key in ("dq", "dk", "dv", "delta"):
+        a, r = rep[key], ref[key]
+        if qheads is not None:
+            sel = qheads if key in ("dq", "delta") else kvsel
+            a = a.reshape(qs[:2] if key == "delta" else qs)[sel]
+            r = r.reshape(qs[:2] if key == "delta" else qs)[sel]
+        out[key] = rel_errors(a, r)
+    return out
+
+
+@pytest.mark.parametrize("obar_fp32", [False, True])
+@pytest.mark.parametrize("guard", ["none", "beta", "eps"])
+def test_tiny_gradients(guard, obar_fp32):
+    x = make("tiny")
+    wl = x["workload"]
+    p = problem(wl, guard)
+    ref = orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], nthreads=threads())
+    fl = _floors(p, x, ref, obar_fp32)
+    _, b = _fwd_bwd(x, guard, obar_fp32=obar_fp32)
+    out = {}
+    out.update(_check("dq", f32(b["dq"]), ref["dq"], fl["dq"]))
+    out.update(_check("dk", f32(b["dk"]), ref["dk"], fl["dk"]))
+    out.update(_check("dv", f32(b["dv"]), ref["dv"], fl["dv"]))
+    out.update(_check("delta", b["delta"].cpu().numpy(), ref["delta"], fl["delta"]))
+    report(f"bwd tiny {guard} {'fp32' if obar_fp32 else 'bf16'}", **out)
+
+
+SHAPES = [  # B, Hq, Hkv, N, d, causal
+    (1, 1, 1, 1, 64, True), (1, 2, 1, 63, 64, True), (2, 4, 2, 65, 64, False),
+    (1, 2, 2, 200, 64, True), (1, 4, 1, 257, 128, True), (2, 2, 1, 129, 128, False),
+    (1, 1, 1, 384, 64, False), (1, 8, 2, 96, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_ragged_and_grouped(shape):
+    B, Hq, Hkv, N, d, causal = shape
+    wl = W.Workload("ragged", B, Hq, Hkv, N, d, causal, 1.0, 1.0, "const", -0.3,
+                    4.0 if N > 2 else 0.0, 0.1, 0.0, 16.0, 78)
+    x = W.make_custom(wl)
+    p = problem(wl, "beta")
+    ref = orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], nthreads=threads())
+    fl = _floors(p, x, ref)
+    _, b = _fwd_bwd(x, "beta")
+    out = {}
+    if N > 1:  # N = 1: dQ = dK = 0 exactly
+        out.update(_check("dq", f32(b["dq"]), ref["dq"], fl["dq"]))
+        out.update(_check("dk", f32(b["dk"]), ref["dk"], fl["dk"]))
+    else:
+        assert not f32(b["dq"]).any() and not f32(b["dk"]).any()
+    out.update(_check("dv", f32(b["dv"]), ref["dv"], fl["dv"]))
+    out.update(_check("delta", b["delta"].cpu().numpy(), ref["delta"], fl["delta"]))
+    report(f"bwd ragged {shape}", **out)
+
+
+@pytest.mark.parametrize("name,guard,kv_heads", [
+    ("gpt2s", "beta", [0, 100]), ("gpt2s", "none", [191]), ("gpt2m", "beta", [5]),
+    ("stress", "eps", [3]),
+])
+def test_full_size_sampled_heads(name, guard, kv_heads):
+    """Full workload, the benchmark's launches; whole KV heads checked."""
+    x = make(name)
+    wl = x["workload"]
+    p = problem(wl, guard)
+    g = wl.heads_q // wl.heads_kv
+    qheads = [kh // wl.heads_kv * wl.heads_q + (kh % wl.heads_kv) * g + i for kh in kv_heads for i in range(g)]
+    ref = orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], kv_heads=kv_heads, nthreads=threads())
+    fl = _floors(p, x, ref, False, kv_heads=kv_heads, qheads=qheads, kvsel=kv_heads)
+    qs = (-1, wl.seqlen, wl.head_dim)
+    _, b = _fwd_bwd(x, guard)
+    out = {}
+    out.update(_check("dq", f32(b["dq"]).reshape(qs)[qheads], ref["dq"].reshape(qs)[qheads], fl["dq"]))
+    out.update(_check("dk", f32(b["dk"]).reshape(qs)[kv_heads], ref["dk"].reshape(qs)[kv_heads], fl["dk"]))
+    out.update(_check("dv", f32(b["dv"]).reshape(qs)[kv_heads], ref["dv"].reshape(qs)[kv_heads], fl["dv"]))
+    out.update(_check("delta", b["delta"].cpu().numpy().reshape(-1, wl.seqlen)[qheads],
+                      ref["delta"].reshape(-1, wl.seqlen)[qheads], fl["delta"]))
+    report(f"bwd {name} {guard}", **out)
+
+
+def test_llama8b_sampled_rows_and_sums():
+    """N = 8192, d = 128, grouped heads: dQ and delta of sampled rows against
+    the single-row FP64 backward; dV through the exact identity
+    sum_j dV_j = sum_i dO_i (rows of P sum to one), per KV head."""
+    x = make("llama8b")
+    wl = x["workload"]
+    p = problem(wl, "beta")
+    _, b = _fwd_bwd(x, "beta")
+    rng = np.random.default_rng(3)
+    qheads = rng.integers(0, wl.heads_q, 48)
+    rows = np.concatenate([rng.integers(0, wl.seqlen, 40), [0, 1, 63, 64, 4095, 8190, 8191, 5000]])
+    ref = orc.bwd_rows_f64(p, x["q"], x["k"], x["v"], x["do"], qheads, rows, nthreads=threads())
+    em = orc.fwd_emu_rows(p, schedule(p, certify=False), x["q"], x["k"], x["v"], qheads, rows,
+                          nthreads=threads())
+    rep = orc.bwd_rows_emu(p, x["q"], x["k"], x["v"], x["do"], qheads, rows, o_in=em["o"],
+                           round_ops=True, nthreads=threads())
+    dq = f32(b["dq"]).reshape(-1, wl.seqlen, wl.head_dim)[qheads, rows]
+    de = b["delta"].cpu().numpy().reshape(-1, wl.seqlen)[qheads, rows]
+    out = {}
+    out.update(_check("dq", dq, ref["dq"], rel_errors(rep["dq"], ref["dq"])))
+    out.update(_check("delta", de, ref["delta"], rel_errors(rep["delta"], ref["delta"])))
+    g = wl.heads_q // wl.heads_kv
+    dv = f32(b["dv"]).astype(np.float64).reshape(wl.heads_kv, wl.seqlen, wl.head_dim).sum(1)
+    do = W.bits_to_f32(x["do"]).astype(np.float64).reshape(wl.heads_kv, g * wl.seqlen, wl.head_dim).sum(1)
+    out.update(_check("sum_dv", dv, do))
+    report("bwd llama8b", **out)
+
+
+def test_zero_denominator_rows_propagate_nan():
+    """Rows whose denominator underflowed (beta = 8 on the large-logit
+    workload) give NaN O; the backward propagates it by IEEE arithmetic:
+    NaN in dQ of those rows and in dK/dV of the heads they attend to."""
+    x = make("stress")
+    wl = x["workload"]
+    f, b = _fwd_bwd(x, "beta", beta=8.0)
+    zd = ((f["row_flags"] & 2) != 0).cpu().numpy()
+    assert zd.any()
+    dq = f32(b["dq"])
+    assert np.isnan(dq[zd]).all()
+    heads_with_zd = zd.reshape(-1, wl.seqlen).any(-1)
+    dk = f32(b["dk"]).reshape(-1, wl.seqlen, wl.head_dim)
+    assert np.isnan(dk[heads_with_zd]).all()  # non-causal: every key is visible to the NaN rows
+
+
+def test_stages_equal_fused_and_dkdv_deterministic():
+    x = make("gpt2s")
+    wl = x["workload"]
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"])
+    f = fa.attn_fwd(q, k, v, causal=True, guard="beta")
+    b1 = fa.attn_bwd(q, k, v, f["o"], do, f["row_m"], f["row_l"], causal=True, guard="beta")
+    p = fa.make_params(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim, causal=True)
+    ws = fa.alloc_workspace(p, q.device)
+    delta = torch.empty_like(b1["delta"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.attn_bwd_preprocess(p, f["o"], do, delta, ws)
+    fa.attn_bwd_main(p, q, k, v, do, f["row_m"], f["row_l"], delta, dk, dv, ws)
+    fa.attn_bwd_finalize(p, dq, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(delta, b1["delta"])
+    assert torch.equal(dk, b1["dk"]) and torch.equal(dv, b1["dv"])  # no atomics: bitwise
+    # dQ is accumulated with fp32 atomics: order-dependent in the last bits
+    mx, mean = rel_errors(f32(dq), f32(b1["dq"]))
+    assert mx < 1e-2 and mean < 1e-3

@@ -251,3 +251,53 @@ def test_emulated_bias_reproduces_the_pages_finding(orc):
     assert abs(m["beta"].mean()) < 1e-4
     assert abs(m["none32"].mean()) < 1e-4
     assert abs(m["eps"].mean()) > 3 * se["eps"]
+
+
+def test_bwd_rows_match_full_backward(orc):
+    """The single-row backward gives the same o, delta, dq as the whole-head one."""
+    p, q, k, v, do = _rand_problem(orc, 9, 2, 4, 2, 45, 64, True)
+    full = orc.bwd_f64(p, q, k, v, do)
+    rng = np.random.default_rng(0)
+    qh = rng.integers(0, 8, 20)
+    rows = rng.integers(0, 45, 20)
+    r = orc.bwd_rows_f64(p, q, k, v, do, qh, rows)
+    b, h = qh // 4, qh % 4
+    assert np.array_equal(r["o"], full["o"][b, h, rows])
+    assert np.array_equal(r["delta"], full["delta"][b, h, rows])
+    assert np.allclose(r["dq"], full["dq"][b, h, rows], rtol=1e-13, atol=1e-15)
+
+
+def test_backward_replay_options(orc):
+    """The replay with exact O and no operand rounding is the definition; with
+    the rounding points on it stays within a few bf16 steps of it."""
+    p, q, k, v, do = _rand_problem(orc, 10, 1, 4, 2, 50, 64, True)
+    full = orc.bwd_f64(p, q, k, v, do)
+    plain = orc.bwd_emu(p, q, k, v, do, o_in=None, round_ops=False)
+    for key in ("delta", "dq", "dk", "dv"):
+        assert np.allclose(plain[key], full[key], rtol=1e-13, atol=1e-14), key
+    # delta from a given O is rowsum(dO * that O)
+    o_bf = W.bits_to_f32(W.to_bf16_bits(full["o"].astype(np.float32))).astype(np.float64)
+    lp = orc.bwd_emu(p, q, k, v, do, o_in=o_bf, round_ops=True)
+    dO = W.bits_to_f32(do).astype(np.float64)
+    assert np.allclose(lp["delta"], (dO * o_bf).sum(-1), rtol=1e-14, atol=1e-14)
+    for key in ("dq", "dk", "dv"):
+        err = np.abs(lp[key] - full[key]).max() / np.abs(full[key]).max()
+        assert 0 < err < 2 ** -5, key
+    # single rows agree with the whole-head replay
+    rows = np.array([0, 1, 17, 49]); qh = np.array([0, 3, 2, 1])
+    b, h = qh // 4, qh % 4
+    r = orc.bwd_rows_emu(p, q, k, v, do, qh, rows, o_in=o_bf[b, h, rows], round_ops=True)
+    assert np.allclose(r["delta"], lp["delta"][b, h, rows], rtol=1e-14)
+    assert np.allclose(r["dq"], lp["dq"][b, h, rows], rtol=1e-12, atol=1e-14)
+
+
+def test_emulation_rows_match_heads(orc):
+    x = W.make("tiny")
+    wl = x["workload"]
+    p = orc.Problem(1, 1, 1, wl.seqlen, wl.head_dim, True, orc.GUARD_BETA)
+    sc = orc.Schedule(block_n=64, round_n=512, certify=False)
+    e = orc.fwd_emu(p, sc, x["q"], x["k"], x["v"])
+    rows = np.array([0, 5, 64, 100, 127])
+    r = orc.fwd_emu_rows(p, sc, x["q"], x["k"], x["v"], np.zeros(5, np.int32), rows)
+    assert np.array_equal(r["o"], e["o"][0, 0, rows])
+    assert np.array_equal(r["m"], e["m"][0, 0, rows]) and np.array_equal(r["flags"], e["flags"][0, 0, rows])
