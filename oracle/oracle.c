@@ -448,11 +448,18 @@ static void bwd64_kvhead(void* c, int32_t item) {
           for (int32_t f = 0; f < d; ++f) dV[(size_t)j * d + f] += pj * dorow[f];
       }
       size_t ro = q_head_offset(p, qh) + (size_t)i * d;
+      if (x->round_ops) /* dQ leaves in bf16 */
+        for (int32_t f = 0; f < d; ++f) dqrow[f] = bf16_round_d(dqrow[f]);
       if (x->o) memcpy(x->o + ro, orow, sizeof(double) * (size_t)d);
       if (x->dq) memcpy(x->dq + ro, dqrow, sizeof(double) * (size_t)d);
       if (x->delta) x->delta[(size_t)qh * N + i] = delta;
     }
   }
+  if (x->round_ops) /* dK and dV leave in bf16 */
+    for (size_t e = 0; e < (size_t)N * d; ++e) {
+      if (dK) dK[e] = bf16_round_d(dK[e]);
+      if (dV) dV[e] = bf16_round_d(dV[e]);
+    }
   free(P);
   free(orow);
   free(dqrow);
@@ -541,6 +548,8 @@ static void bwdrow_item(void* c, int32_t item) {
     if (x->round_ops) ds = bf16_round_d(ds);
     for (int32_t f = 0; f < d; ++f) dqrow[f] += alpha * ds * (double)orc_f32_from_bf16(K[(size_t)j * d + f]);
   }
+  if (x->round_ops)
+    for (int32_t f = 0; f < d; ++f) dqrow[f] = bf16_round_d(dqrow[f]);
   x->delta[item] = delta;
   free(P);
 }

@@ -113,7 +113,7 @@ int orc_bwd_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
 /* The backward replayed at the method's rounding points: delta computed from
  * o_in (the forward's bf16 output, [B,Hq,N,d]; NULL = exact O) and, with
  * round_ops, P (for dV) and dS (for dK, dQ) rounded to bf16 as the products'
- * operands; all else in double.  Measures the method's own deviation from
+ * operands and dQ, dK, dV rounded to bf16 as outputs; all else in double.  Measures the method's own deviation from
  * orc_bwd_f64 (its floor), not the kernel's.                               */
 int orc_bwd_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
                 const uint16_t* v, const uint16_t* dout, const int32_t* kv_heads,
