@@ -34,8 +34,8 @@ def parse():
     ap.add_argument("--guard", default="beta", choices=["none", "beta", "eps"])
     ap.add_argument("--obar-fp32", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4,
-                    help="KV heads in the CPU oracle's bounded sample")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="KV heads in the CPU oracle's sample (0: every head of the workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
     return ap.parse_args()
@@ -169,13 +169,14 @@ def main():
 
 
 def cpu_baseline(x, wl, args):
-    """The FP64 oracle (forward+backward of softmax attention) on a bounded
-    sample: the first --cpu-heads KV heads of the same workload, all host
-    threads.  Scaled to TFLOP/s with the same counted work per head."""
+    """The FP64 oracle (forward+backward of softmax attention) on the same
+    workload (or its first --cpu-heads KV heads), all host threads.  Scaled
+    to TFLOP/s with the same counted work per head."""
     import oracle as orc
 
     nthreads = os.cpu_count() or 1
-    heads = list(range(min(args.cpu_heads, wl.batch * wl.heads_kv)))
+    nkv = wl.batch * wl.heads_kv
+    heads = list(range(min(args.cpu_heads, nkv) if args.cpu_heads > 0 else nkv))
     p = orc.Problem(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim, wl.causal,
                     {"none": 0, "beta": 1, "eps": 2}[args.guard])
     t0 = time.perf_counter()

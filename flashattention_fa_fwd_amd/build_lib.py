@@ -20,6 +20,9 @@ def hipcc_cmd(out: str) -> list:
         "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-munsafe-fp-atomics",
+        # keep matrix-instruction accumulators in ordinary VGPRs: the softmax
+        # and rescale work on them every step, and AGPRs would need copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,

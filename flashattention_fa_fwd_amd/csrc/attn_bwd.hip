@@ -87,6 +87,83 @@ __global__ __launch_bounds__(kThreads) void bwd_post_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- bwd_main
+// Fetch of one 32-row step (Q, dO rows and their statistics) into registers.
+template <int D, int CPT>
+__device__ __forceinline__ void bwd_fetch(const BwdArgs& a, int sidx, int hk, int b, int qstart,
+                                          int nsteps, int tid, uint4 (&qreg)[CPT],
+                                          uint4 (&greg)[CPT], float& st_m, float& st_l,
+                                          float& st_d) {
+  constexpr int BM = kBwdBlockM;
+  const int N = a.N;
+  const int hq = hk * a.group + sidx / nsteps;
+  const int q0 = qstart + (sidx % nsteps) * BM;
+  const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
+  const size_t roff = (size_t)(b * a.Hq + hq) * N;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = tid + u * kThreads;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    qreg[u] = make_uint4(0, 0, 0, 0);
+    greg[u] = make_uint4(0, 0, 0, 0);
+    if (q0 + row < N) {
+      qreg[u] = *(const uint4*)(a.q + qoff + (size_t)(q0 + row) * D + col);
+      greg[u] = *(const uint4*)(a.dout + qoff + (size_t)(q0 + row) * D + col);
+    }
+  }
+  if (tid < BM) {
+    const int r = q0 + tid;
+    st_m = 0.0f;
+    st_l = 0.0f;
+    st_d = 0.0f;
+    if (r < N) {
+      st_m = a.row_m[roff + r] * kLog2e;
+      st_l = 1.0f / a.row_l[roff + r];
+      st_d = a.delta[roff + r];
+    }
+  }
+}
+
+// Row-major copies, and feature-major copies built from the same registers:
+// rows r and r^1 sit in lanes l and l^(D/8); the even row's lane writes
+// features col..col+3, the odd row's lane col+4..col+7, one dword (row pair)
+// per feature.
+template <int D, int CPT, int QSTR, int TSTR>
+__device__ __forceinline__ void bwd_stage(int tid, const uint4 (&qreg)[CPT],
+                                          const uint4 (&greg)[CPT], float st_m, float st_l,
+                                          float st_d, uint16_t* Qs, uint16_t* dOs, uint16_t* Qt,
+                                          uint16_t* dOt, float* sm2, float* sinvl, float* sdel) {
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = tid + u * kThreads;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    *(uint4*)(&Qs[row * QSTR + col]) = qreg[u];
+    *(uint4*)(&dOs[row * QSTR + col]) = greg[u];
+    const bool even = (row & 1) == 0;
+    const int r0 = row & ~1, e0 = even ? 0 : 4;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const uint4 mine = which ? greg[u] : qreg[u];
+      const uint32_t m0 = even ? mine.x : mine.z, m1 = even ? mine.y : mine.w;
+      const uint32_t o0 = even ? mine.z : mine.x, o1 = even ? mine.w : mine.y;
+      // the partner needs the words this lane does not write
+      const uint32_t p0 = (uint32_t)__shfl_xor((int)o0, D / 8);
+      const uint32_t p1 = (uint32_t)__shfl_xor((int)o1, D / 8);
+      const uint32_t lo0 = even ? m0 : p0, hi0 = even ? p0 : m0;
+      const uint32_t lo1 = even ? m1 : p1, hi1 = even ? p1 : m1;
+      uint16_t* dst = which ? dOt : Qt;
+      *(uint32_t*)(&dst[(col + e0 + 0) * TSTR + r0]) = (lo0 & 0xffffu) | (hi0 << 16);
+      *(uint32_t*)(&dst[(col + e0 + 1) * TSTR + r0]) = (lo0 >> 16) | (hi0 & 0xffff0000u);
+      *(uint32_t*)(&dst[(col + e0 + 2) * TSTR + r0]) = (lo1 & 0xffffu) | (hi1 << 16);
+      *(uint32_t*)(&dst[(col + e0 + 3) * TSTR + r0]) = (lo1 >> 16) | (hi1 & 0xffff0000u);
+    }
+  }
+  if (tid < kBwdBlockM) {
+    sm2[tid] = st_m;
+    sinvl[tid] = st_l;
+    sdel[tid] = st_d;
+  }
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   constexpr int BN = 128;            // keys per workgroup
@@ -113,8 +190,10 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int N = a.N;
-  const int kblk = blockIdx.x;
-  const int hk = blockIdx.y, b = blockIdx.z;
+  const int nkb = (N + BN - 1) / BN;
+  int kvhead, kblk;
+  xcd_map((int)blockIdx.x, nkb, a.B * a.Hkv, kvhead, kblk);
+  const int hk = kvhead % a.Hkv, b = kvhead / a.Hkv;
   const int k0 = kblk * BN;
   const int wk0 = k0 + 32 * wave;     // this wave's first key
   const int key = wk0 + l32;          // the key this lane owns in S/dP
@@ -162,61 +241,30 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
       dv[f][i] = 0.0f;
     }
 
+  // Steps: every 32-row slice of every query head of the group.  The next
+  // step's Q, dO and row statistics are fetched into registers while the
+  // current step computes; its LDS tiles are written right after the dS
+  // barrier of the current step (the staging tiles are free by then).
   const int qstart = CAUSAL ? k0 : 0;  // earlier rows cannot see these keys
-  for (int hh = 0; hh < a.group; ++hh) {
-    const int hq = hk * a.group + hh;
-    const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
-    const size_t roff = (size_t)(b * a.Hq + hq) * N;
-    const uint16_t* __restrict__ Q = a.q + qoff;
-    const uint16_t* __restrict__ dO = a.dout + qoff;
-    float* __restrict__ dQ = a.dq_acc + qoff;
+  const int nsteps = (N - qstart + BM - 1) / BM;
+  const int total = nsteps * a.group;
+  constexpr int CH = BM * D / 8;       // 16-byte chunks per tensor per step
+  constexpr int CPT = CH / kThreads;   // per thread: 1 (d=64) or 2 (d=128)
+  static_assert(CH % kThreads == 0, "step / thread split");
+  uint4 qreg[CPT], greg[CPT];
+  float st_m = 0.0f, st_l = 0.0f, st_d = 0.0f;
 
-    for (int q0 = qstart; q0 < N; q0 += BM) {
-      __syncthreads();  // everyone is done with the previous step's tiles
-      // ---- stage Q and dO rows q0..q0+31: row-major and feature-major
-      {
-        constexpr int CH = BM * D / 8;  // 16-byte chunks per tensor
-        for (int c = tid; c < 2 * CH; c += kThreads) {
-          const int which = c / CH, cc = c % CH;
-          const int row = cc / (D / 8), col = (cc % (D / 8)) * 8;
-          const uint16_t* src = which ? dO : Q;
-          uint4 val = make_uint4(0, 0, 0, 0);
-          if (q0 + row < N) val = *(const uint4*)(src + (size_t)(q0 + row) * D + col);
-          *(uint4*)(&(which ? dOs : Qs)[row * QSTR + col]) = val;
-        }
-        constexpr int TCH = (BM / 2) * (D / 8);
-        for (int c = tid; c < 2 * TCH; c += kThreads) {
-          const int which = c / TCH, cc = c % TCH;
-          const int pr = cc % (BM / 2), col = (cc / (BM / 2)) * 8;
-          const int r = q0 + 2 * pr;
-          const uint16_t* src = which ? dO : Q;
-          uint16_t* dst = which ? dOt : Qt;
-          uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-          if (r < N) v0 = *(const uint4*)(src + (size_t)r * D + col);
-          if (r + 1 < N) v1 = *(const uint4*)(src + (size_t)(r + 1) * D + col);
-          const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-          const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            *(uint32_t*)(&dst[(col + 2 * e) * TSTR + 2 * pr]) = (w0[e] & 0xffffu) | (w1[e] << 16);
-            *(uint32_t*)(&dst[(col + 2 * e + 1) * TSTR + 2 * pr]) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-          }
-        }
-        if (tid < BM) {
-          const int r = q0 + tid;
-          float mm = 0.0f, il = 0.0f, de = 0.0f;
-          if (r < N) {
-            mm = a.row_m[roff + r] * kLog2e;
-            il = 1.0f / a.row_l[roff + r];
-            de = a.delta[roff + r];
-          }
-          sm2[tid] = mm;
-          sinvl[tid] = il;
-          sdel[tid] = de;
-        }
-      }
-      __syncthreads();
+  bwd_fetch<D, CPT>(a, 0, hk, b, qstart, nsteps, tid, qreg, greg, st_m, st_l, st_d);
+  bwd_stage<D, CPT, QSTR, TSTR>(tid, qreg, greg, st_m, st_l, st_d, Qs, dOs, Qt, dOt, sm2, sinvl, sdel);
+  for (int sidx = 0; sidx < total; ++sidx) {
+    const int hq = hk * a.group + sidx / nsteps;
+    const int q0 = qstart + (sidx % nsteps) * BM;
+    float* __restrict__ dQ = a.dq_acc + ((size_t)(b * a.Hq + hq) * N) * D;
+    __syncthreads();  // this step's tiles are visible; the dS tile is free
+    if (sidx + 1 < total)
+      bwd_fetch<D, CPT>(a, sidx + 1, hk, b, qstart, nsteps, tid, qreg, greg, st_m, st_l, st_d);
 
+    {
       const bool active = wk0 < N && (!CAUSAL || q0 + BM - 1 >= wk0);
       if (active) {
         // ---- S = Q K^T and dP = dO V^T: lane = key, register i = row 8(i/4)+4*half+i%4
@@ -278,27 +326,29 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i)
           dSs[(8 * (i >> 2) + 4 * half + (i & 3)) * SSTR + 32 * wave + l32] = 0;
       }
-      __syncthreads();
+    }
+    __syncthreads();  // the dS tile is complete; the staging tiles are free
+    if (sidx + 1 < total)
+      bwd_stage<D, CPT, QSTR, TSTR>(tid, qreg, greg, st_m, st_l, st_d, Qs, dOs, Qt, dOt, sm2, sinvl, sdel);
 
-      // ---- dQ[q0..q0+31][16-feature slice] += dS K over the 128 keys
-      const int lr = lane & 15, lq = lane >> 4;
+    // ---- dQ[q0..q0+31][16-feature slice] += dS K over the 128 keys
+    const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-      for (int sl = 0; sl < DQB; ++sl) {
-        const int d0 = 16 * (wave * DQB + sl);
+    for (int sl = 0; sl < DQB; ++sl) {
+      const int d0 = 16 * (wave * DQB + sl);
 #pragma unroll
-        for (int mq = 0; mq < 2; ++mq) {
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mq = 0; mq < 2; ++mq) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < BN / 32; ++kk) {
-            const bf16x8 da = *(const bf16x8*)(&dSs[(16 * mq + lr) * SSTR + 32 * kk + 8 * lq]);
-            const bf16x8 kb = *(const bf16x8*)(&Kt[(d0 + lr) * KTSTR + 32 * kk + 8 * lq]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, kb, acc, 0, 0, 0);
-          }
+        for (int kk = 0; kk < BN / 32; ++kk) {
+          const bf16x8 da = *(const bf16x8*)(&dSs[(16 * mq + lr) * SSTR + 32 * kk + 8 * lq]);
+          const bf16x8 kb = *(const bf16x8*)(&Kt[(d0 + lr) * KTSTR + 32 * kk + 8 * lq]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, kb, acc, 0, 0, 0);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int qr = q0 + 16 * mq + 4 * lq + i;
-            if (qr < N) unsafeAtomicAdd(&dQ[(size_t)qr * D + d0 + lr], acc[i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int qr = q0 + 16 * mq + 4 * lq + i;
+          if (qr < N) unsafeAtomicAdd(&dQ[(size_t)qr * D + d0 + lr], acc[i]);
         }
       }
     }
@@ -331,7 +381,7 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s) {
 }
 
 hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t s) {
-  const dim3 grid((unsigned)((a.N + 127) / 128), a.Hkv, a.B);
+  const dim3 grid((unsigned)(((a.N + 127) / 128) * a.Hkv * a.B));
   if (d == 64) {
     if (causal)
       hipLaunchKernelGGL((bwd_main_kernel<64, true>), grid, dim3(kThreads), 0, s, a);

@@ -64,9 +64,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int N = a.N;
-  const int nmb = gridDim.x;
-  const int mb = CAUSAL ? (nmb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // heavy blocks first
-  const int hq = blockIdx.y, b = blockIdx.z;
+  const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
+  int head, r;
+  xcd_map((int)blockIdx.x, nmb, a.B * a.Hq, head, r);
+  const int mb = CAUSAL ? (nmb - 1 - r) : r;  // a head's heavy (causal) blocks first
+  const int hq = head % a.Hq, b = head / a.Hq;
   const int hk = hq / a.group;
   const int q0 = mb * kFwdBlockM + wave * 32;
   const int qrow = q0 + l32;
@@ -100,40 +102,62 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int kend = CAUSAL ? min(N, (mb + 1) * kFwdBlockM) : N;
   const bool wave_live = q0 < N;
 
-  for (int j0 = 0; j0 < kend; j0 += BN) {
-    __syncthreads();  // the previous step's readers are done with the tiles
-    // ---- stage K (row-major) and V (transposed) of keys j0 .. j0+63
-    constexpr int KCH = BN * D / 8;  // 16-byte chunks
+  // The next step's K and V rows are fetched into registers while the current
+  // step computes, so global-load latency overlaps the matrix work.
+  constexpr int KCH = BN * D / 8;          // 16-byte chunks of a K tile
+  constexpr int VCH = (BN / 2) * (D / 8);  // key pairs x 8-feature chunks of V
+  constexpr int KPT = KCH / kThreads, VPT = VCH / kThreads;
+  static_assert(KCH % kThreads == 0 && VCH % kThreads == 0, "tile / thread split");
+  uint4 kreg[KPT], vreg0[VPT], vreg1[VPT];
+  auto fetch = [&](int jb) {
 #pragma unroll
-    for (int c = tid; c < KCH; c += kThreads) {
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * kThreads;
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = j0 + row;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (key < N) val = *(const uint4*)(K + (size_t)key * D + col);
-      *(uint4*)(&Ks[row * KSTR + col]) = val;
+      kreg[u] = make_uint4(0, 0, 0, 0);
+      if (jb + row < N) kreg[u] = *(const uint4*)(K + (size_t)(jb + row) * D + col);
     }
-    // V: a thread takes two consecutive keys and 8 features and writes
-    // 8 dwords (key pair) of the feature-major tile
-    constexpr int VCH = (BN / 2) * (D / 8);
 #pragma unroll
-    for (int c = tid; c < VCH; c += kThreads) {
+    for (int u = 0; u < VPT; ++u) {
+      const int c = tid + u * kThreads;
       const int pr = c % (BN / 2), col = (c / (BN / 2)) * 8;
-      const int key = j0 + 2 * pr;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (key < N) v0 = *(const uint4*)(V + (size_t)key * D + col);
-      if (key + 1 < N) v1 = *(const uint4*)(V + (size_t)(key + 1) * D + col);
-      const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-      const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+      const int key = jb + 2 * pr;
+      vreg0[u] = make_uint4(0, 0, 0, 0);
+      vreg1[u] = make_uint4(0, 0, 0, 0);
+      if (key < N) vreg0[u] = *(const uint4*)(V + (size_t)key * D + col);
+      if (key + 1 < N) vreg1[u] = *(const uint4*)(V + (size_t)(key + 1) * D + col);
+    }
+  };
+  // K row-major; V feature-major: a thread holds two consecutive keys x 8
+  // features and writes 8 dwords (one key pair per feature)
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int c = tid + u * kThreads;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *(uint4*)(&Ks[row * KSTR + col]) = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int c = tid + u * kThreads;
+      const int pr = c % (BN / 2), col = (c / (BN / 2)) * 8;
+      const uint32_t w0[4] = {vreg0[u].x, vreg0[u].y, vreg0[u].z, vreg0[u].w};
+      const uint32_t w1[4] = {vreg1[u].x, vreg1[u].y, vreg1[u].z, vreg1[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // features col+2e (low halves) and col+2e+1 (high halves)
-        uint32_t lo = (w0[e] & 0xffffu) | (w1[e] << 16);
-        uint32_t hi = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-        *(uint32_t*)(&Vt[(col + 2 * e) * VSTR + 2 * pr]) = lo;
-        *(uint32_t*)(&Vt[(col + 2 * e + 1) * VSTR + 2 * pr]) = hi;
+        *(uint32_t*)(&Vt[(col + 2 * e) * VSTR + 2 * pr]) = (w0[e] & 0xffffu) | (w1[e] << 16);
+        *(uint32_t*)(&Vt[(col + 2 * e + 1) * VSTR + 2 * pr]) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
       }
     }
+  };
+
+  fetch(0);
+  for (int j0 = 0; j0 < kend; j0 += BN) {
+    __syncthreads();  // the previous step's readers are done with the tiles
+    stage();
     __syncthreads();
+    if (j0 + BN < kend) fetch(j0 + BN);
 
     // a wave whose rows all lie above this block's first key has nothing here
     if (!wave_live || (CAUSAL && j0 > q0 + 31)) continue;
@@ -275,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 template <int D, bool CAUSAL, int GUARD, bool OBAR_F32>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
-  dim3 grid(nmb, a.Hq, a.B);
+  dim3 grid((unsigned)(nmb * a.Hq * a.B));
   hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, GUARD, OBAR_F32>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

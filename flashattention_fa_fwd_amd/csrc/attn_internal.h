@@ -57,6 +57,23 @@ struct BwdArgs {
   float alpha, c1;
 };
 
+// Workgroup order on the 8 XCDs (each with its own L2): the hardware hands
+// consecutive workgroup ids to XCDs round-robin.  When the number of heads is
+// a multiple of 8, head h's blocks get ids that all land on XCD h/(heads/8),
+// so one head's K/V (forward) or Q/dO (backward) is re-read from one L2.
+// Returns (head index, block index) for linear workgroup id L.
+__device__ __forceinline__ void xcd_map(int L, int nblk, int heads, int& head, int& blk) {
+  constexpr int kXcds = 8;
+  if (heads % kXcds == 0) {
+    const int xcd = L % kXcds, local = L / kXcds;
+    head = xcd * (heads / kXcds) + local / nblk;
+    blk = local % nblk;
+  } else {
+    head = L / nblk;
+    blk = L % nblk;
+  }
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
                       hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s);
