@@ -5,7 +5,7 @@ on one MI355X.
 One step = attn_fwd + attn_bwd (every stage of the path) over one batch of
 synthetic inputs that are resident in device memory before timing starts.
 Prints one JSON line (see the keys below).  The CPU oracle's FP64
-forward+backward is timed on a bounded sample of heads as a baseline.
+forward+backward of the same workload is timed on the host as a baseline.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload gpt2s]
 """
@@ -174,7 +174,7 @@ def cpu_baseline(x, wl, args):
     to TFLOP/s with the same counted work per head."""
     import oracle as orc
 
-    nthreads = os.cpu_count() or 1
+    nthreads = min(16, os.cpu_count() or 1)  # the host share of one GPU
     nkv = wl.batch * wl.heads_kv
     heads = list(range(min(args.cpu_heads, nkv) if args.cpu_heads > 0 else nkv))
     p = orc.Problem(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim, wl.causal,
