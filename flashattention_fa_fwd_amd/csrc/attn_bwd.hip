@@ -17,14 +17,18 @@
 //     a wave owns 32 keys, keeps their K and V rows in registers and
 //     accumulates their dK and dV over every query row (and every query
 //     head of the group) in registers -- no atomics for dK/dV;
-//   * per step of 32 query rows: Q and dO staged in LDS row-major and
-//     transposed; S = Q K^T and dP = dO V^T come out with lane = key and
-//     registers = query rows, which is the A-operand layout of dV += P^T dO
-//     and dK += dS^T Q, so P and dS go to those products from registers;
-//   * dQ needs dS with lane = query row: every wave writes its bf16 dS into
-//     one LDS tile, then each wave computes a 16-feature slice of dQ over all
-//     128 keys (v_mfma_f32_16x16x32_bf16) and adds it to the fp32
-//     accumulator with one atomic per element per workgroup;
+//   * per step of 32 query rows, Q and dO are staged row-major in one of two
+//     LDS buffers (one barrier per step: step s computes from one buffer
+//     while step s+1 is written to the other);
+//   * S = Q K^T and dP = dO V^T come out with lane = key and registers =
+//     query rows, the A-operand layout of dV += P^T dO and dK += dS^T Q; the
+//     B operands (dO and Q with the contraction over rows) come from the
+//     row-major tiles through the gfx950 LDS transpose read;
+//   * dS is written key-major (four rows per 8-byte write) into a
+//     double-buffered tile; the next step, each wave reads it back through
+//     the transpose read as the A operand of a 16-feature slice of dQ over
+//     the 128 keys (v_mfma_f32_16x16x32_bf16, K slice held in registers) and
+//     adds it to the fp32 accumulator with one atomic per element;
 //   * bwd_post: dQ = bf16(alpha * accumulator).
 #include "attn_internal.h"
 
@@ -87,108 +91,154 @@ __global__ __launch_bounds__(kThreads) void bwd_post_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- bwd_main
-// Fetch of one 32-row step (Q, dO rows and their statistics) into registers.
-template <int D, int CPT>
-__device__ __forceinline__ void bwd_fetch(const BwdArgs& a, int sidx, int hk, int b, int qstart,
-                                          int nsteps, int tid, uint4 (&qreg)[CPT],
-                                          uint4 (&greg)[CPT], float& st_m, float& st_l,
-                                          float& st_d) {
-  constexpr int BM = kBwdBlockM;
+// LDS transpose read (gfx950): within each group of 16 lanes, lane r points
+// at 4 consecutive bf16 of row r/4, columns 4(r%4)..4(r%4)+3, of a block of
+// 4 rows x 16 columns; lane i receives column i of those 4 rows.  For a
+// matrix stored with the MFMA's m or n index contiguous, that is 4
+// consecutive contraction indices of one m or n: half an operand fragment.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((lds_u16*)p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+__device__ __forceinline__ bf16x8 frag2(uint2 lo, uint2 hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// One step = 32 query rows of one query head of the group.  Its Q and dO
+// rows and the rows' statistics are fetched into registers one step ahead
+// and then written to one of two LDS stages.
+template <int D>
+struct BwdStep {
+  static constexpr int CPT = kBwdBlockM * D / 8 / kThreads;  // 16-byte chunks per thread
+  uint4 q[CPT], g[CPT];
+  float lse2, del;  // threads 0..31: m*log2(e) + log2(l) of the row, and delta
+};
+
+template <int D>
+__device__ __forceinline__ void bwd_fetch(const BwdArgs& a, int hq, int q0, int b, int tid,
+                                          BwdStep<D>& st) {
   const int N = a.N;
-  const int hq = hk * a.group + sidx / nsteps;
-  const int q0 = qstart + (sidx % nsteps) * BM;
   const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
-  const size_t roff = (size_t)(b * a.Hq + hq) * N;
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) {
+  for (int u = 0; u < BwdStep<D>::CPT; ++u) {
     const int c = tid + u * kThreads;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    qreg[u] = make_uint4(0, 0, 0, 0);
-    greg[u] = make_uint4(0, 0, 0, 0);
+    st.q[u] = make_uint4(0, 0, 0, 0);
+    st.g[u] = make_uint4(0, 0, 0, 0);
     if (q0 + row < N) {
-      qreg[u] = *(const uint4*)(a.q + qoff + (size_t)(q0 + row) * D + col);
-      greg[u] = *(const uint4*)(a.dout + qoff + (size_t)(q0 + row) * D + col);
+      st.q[u] = *(const uint4*)(a.q + qoff + (size_t)(q0 + row) * D + col);
+      st.g[u] = *(const uint4*)(a.dout + qoff + (size_t)(q0 + row) * D + col);
     }
   }
-  if (tid < BM) {
-    const int r = q0 + tid;
-    st_m = 0.0f;
-    st_l = 0.0f;
-    st_d = 0.0f;
-    if (r < N) {
-      st_m = a.row_m[roff + r] * kLog2e;
-      st_l = 1.0f / a.row_l[roff + r];
-      st_d = a.delta[roff + r];
+  if (tid < kBwdBlockM) {
+    const size_t r = (size_t)(b * a.Hq + hq) * N + q0 + tid;
+    st.lse2 = 0.0f;
+    st.del = 0.0f;
+    if (q0 + tid < N) {
+      const float l = a.row_l[r];
+      // P = exp(t - m) / l = exp2(t*log2(e) - lse2); a row whose every
+      // weight underflowed (l == 0) keeps P = NaN, as 0 * (1/0) gives
+      st.lse2 = l > 0.0f ? __builtin_fmaf(a.row_m[r], kLog2e, __builtin_log2f(l))
+                         : __builtin_nanf("");
+      st.del = a.delta[r];
     }
   }
 }
 
-// Row-major copies, and feature-major copies built from the same registers:
-// rows r and r^1 sit in lanes l and l^(D/8); the even row's lane writes
-// features col..col+3, the odd row's lane col+4..col+7, one dword (row pair)
-// per feature.
-template <int D, int CPT, int QSTR, int TSTR>
-__device__ __forceinline__ void bwd_stage(int tid, const uint4 (&qreg)[CPT],
-                                          const uint4 (&greg)[CPT], float st_m, float st_l,
-                                          float st_d, uint16_t* Qs, uint16_t* dOs, uint16_t* Qt,
-                                          uint16_t* dOt, float* sm2, float* sinvl, float* sdel) {
+template <int D, int QSTR>
+__device__ __forceinline__ void bwd_stage(int tid, const BwdStep<D>& st, uint16_t* Qs,
+                                          uint16_t* dOs, float* slse, float* sdel) {
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) {
+  for (int u = 0; u < BwdStep<D>::CPT; ++u) {
     const int c = tid + u * kThreads;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    *(uint4*)(&Qs[row * QSTR + col]) = qreg[u];
-    *(uint4*)(&dOs[row * QSTR + col]) = greg[u];
-    const bool even = (row & 1) == 0;
-    const int r0 = row & ~1, e0 = even ? 0 : 4;
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const uint4 mine = which ? greg[u] : qreg[u];
-      const uint32_t m0 = even ? mine.x : mine.z, m1 = even ? mine.y : mine.w;
-      const uint32_t o0 = even ? mine.z : mine.x, o1 = even ? mine.w : mine.y;
-      // the partner needs the words this lane does not write
-      const uint32_t p0 = (uint32_t)__shfl_xor((int)o0, D / 8);
-      const uint32_t p1 = (uint32_t)__shfl_xor((int)o1, D / 8);
-      const uint32_t lo0 = even ? m0 : p0, hi0 = even ? p0 : m0;
-      const uint32_t lo1 = even ? m1 : p1, hi1 = even ? p1 : m1;
-      uint16_t* dst = which ? dOt : Qt;
-      *(uint32_t*)(&dst[(col + e0 + 0) * TSTR + r0]) = (lo0 & 0xffffu) | (hi0 << 16);
-      *(uint32_t*)(&dst[(col + e0 + 1) * TSTR + r0]) = (lo0 >> 16) | (hi0 & 0xffff0000u);
-      *(uint32_t*)(&dst[(col + e0 + 2) * TSTR + r0]) = (lo1 & 0xffffu) | (hi1 << 16);
-      *(uint32_t*)(&dst[(col + e0 + 3) * TSTR + r0]) = (lo1 >> 16) | (hi1 & 0xffff0000u);
-    }
+    *(uint4*)(&Qs[row * QSTR + col]) = st.q[u];
+    *(uint4*)(&dOs[row * QSTR + col]) = st.g[u];
   }
   if (tid < kBwdBlockM) {
-    sm2[tid] = st_m;
-    sinvl[tid] = st_l;
-    sdel[tid] = st_d;
+    slse[tid] = st.lse2;
+    sdel[tid] = st.del;
+  }
+}
+
+constexpr int kBwdKeys = 128;             // keys per workgroup (32 per wave)
+constexpr int kBwdKB = kBwdKeys / 32;     // 32-key blocks per workgroup
+constexpr int kBwdDSTR = kBwdBlockM + 16; // row stride of the key-major dS tile
+
+// Does 32-key block kb of the workgroup hold a key visible to rows q0..q0+31?
+template <bool CAUSAL>
+__device__ __forceinline__ bool bwd_block_live(int k0, int kb, int q0, int N) {
+  return k0 + 32 * kb < N && (!CAUSAL || q0 + kBwdBlockM - 1 >= k0 + 32 * kb);
+}
+
+// dQ[q0..q0+31][this wave's features] += dS K over the workgroup's live key
+// blocks (v_mfma_f32_16x16x32_bf16), one atomic add per element.
+template <int D, bool CAUSAL, int DQB>
+__device__ __forceinline__ void bwd_dq(const BwdArgs& a, const uint16_t* ds,
+                                       const bf16x8 (&kq)[DQB][kBwdKB], float* dQ, int q0,
+                                       int k0, int wave, int g16, int r16) {
+  const int N = a.N;
+#pragma unroll
+  for (int sl = 0; sl < DQB; ++sl) {
+    const int d0 = 16 * (wave * DQB + sl);
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kBwdKB; ++kb) {
+        if (!bwd_block_live<CAUSAL>(k0, kb, q0, N)) continue;
+        // A = dS[rows 16mq + r16][keys 32kb + 8*g16 + 0..7], tile stored key-major
+        const uint16_t* p = ds + (32 * kb + 8 * g16 + (r16 >> 2)) * kBwdDSTR + 16 * mq + 4 * (r16 & 3);
+        const bf16x8 da = frag2(lds_read_tr(p), lds_read_tr(p + 4 * kBwdDSTR));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, kq[sl][kb], acc, 0, 0, 0);
+      }
+      const int r0 = q0 + 16 * mq + 4 * g16;  // C register i holds row r0 + i
+      float* dst = dQ + (size_t)r0 * D + d0 + r16;
+      if (q0 + kBwdBlockM <= N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + (size_t)i * D, acc[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < N) unsafeAtomicAdd(dst + (size_t)i * D, acc[i]);
+      }
+    }
   }
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
-  constexpr int BN = 128;            // keys per workgroup
+  constexpr int BN = kBwdKeys;
   constexpr int BM = kBwdBlockM;     // query rows per step (32)
   constexpr int NT = D / kMfmaK;     // 16-wide steps along d
   constexpr int FB = D / 32;         // 32-feature blocks of dK/dV
-  constexpr int QSTR = D + 8;        // row stride of the row-major tiles
-  constexpr int TSTR = BM + 4;       // row stride of the transposed tiles
-  constexpr int SSTR = BN + 8;       // row stride of the dS tile
-  constexpr int KTSTR = BN + 8;      // row stride of the transposed K tile
+  constexpr int QSTR = D + 8;        // row stride of the Q / dO tiles
+  constexpr int DSTR = kBwdDSTR;
   constexpr int DQB = D / 16 / 4;    // 16-feature dQ slices per wave (1 or 2)
+  constexpr int KB = kBwdKB;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * QSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BM * QSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[BM * SSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * KTSTR];
-  __shared__ __attribute__((aligned(16))) float sm2[BM];
-  __shared__ __attribute__((aligned(16))) float sinvl[BM];
-  __shared__ __attribute__((aligned(16))) float sdel[BM];
+  // two stages: step s computes from stage s&1 while step s+1 is written
+  // to the other; the dS tile is double-buffered the same way
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * QSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BM * QSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t dSt[2][BN * DSTR];
+  __shared__ __attribute__((aligned(16))) float slse[2][BM];
+  __shared__ __attribute__((aligned(16))) float sdel[2][BM];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
+  const int g16 = lane >> 4, r16 = lane & 15;
   const int N = a.N;
   const int nkb = (N + BN - 1) / BN;
   int kvhead, kblk;
@@ -201,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   const uint16_t* __restrict__ K = a.k + kvoff;
   const uint16_t* __restrict__ V = a.v + kvoff;
 
-  // K and V rows of this lane's key as B operands: [16t + 8*half + 0..7]
+  // K and V rows of this lane's key as B operands of S = Q K^T and
+  // dP = dO V^T: [16t + 8*half + 0..7]
   bf16x8 kf[NT], vf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -213,24 +264,24 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
     kf[t] = __builtin_bit_cast(bf16x8, kr);
     vf[t] = __builtin_bit_cast(bf16x8, vr);
   }
-  // the workgroup's 128 K rows, feature-major, for the dQ product
-  {
-    constexpr int CH = (BN / 2) * (D / 8);
-    for (int c = tid; c < CH; c += kThreads) {
-      const int pr = c % (BN / 2), col = (c / (BN / 2)) * 8;
-      const int kk = k0 + 2 * pr;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (kk < N) v0 = *(const uint4*)(K + (size_t)kk * D + col);
-      if (kk + 1 < N) v1 = *(const uint4*)(K + (size_t)(kk + 1) * D + col);
-      const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-      const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+  // K as the B operand of this wave's dQ slices: lane holds
+  // K[k0 + 32kb + 8*g16 + 0..7][d0 + r16] for every 32-key block kb
+  bf16x8 kq[DQB][KB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *(uint32_t*)(&Kt[(col + 2 * e) * KTSTR + 2 * pr]) = (w0[e] & 0xffffu) | (w1[e] << 16);
-        *(uint32_t*)(&Kt[(col + 2 * e + 1) * KTSTR + 2 * pr]) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+  for (int sl = 0; sl < DQB; ++sl)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int d0 = 16 * (wave * DQB + sl);
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = k0 + 32 * kb + 8 * g16 + 2 * j;
+        const uint32_t lo = kk < N ? K[(size_t)kk * D + d0 + r16] : 0u;
+        const uint32_t hi = kk + 1 < N ? K[(size_t)(kk + 1) * D + d0 + r16] : 0u;
+        w[j] = lo | (hi << 16);
       }
+      kq[sl][kb] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
-  }
 
   f32x16 dk[FB], dv[FB];
 #pragma unroll
@@ -241,117 +292,133 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
       dv[f][i] = 0.0f;
     }
 
-  // Steps: every 32-row slice of every query head of the group.  The next
-  // step's Q, dO and row statistics are fetched into registers while the
-  // current step computes; its LDS tiles are written right after the dS
-  // barrier of the current step (the staging tiles are free by then).
-  const int qstart = CAUSAL ? k0 : 0;  // earlier rows cannot see these keys
+  // Steps: every 32-row slice of every query head of the group, from the
+  // first row that can see these keys.
+  const int qstart = CAUSAL ? k0 : 0;
   const int nsteps = (N - qstart + BM - 1) / BM;
   const int total = nsteps * a.group;
-  constexpr int CH = BM * D / 8;       // 16-byte chunks per tensor per step
-  constexpr int CPT = CH / kThreads;   // per thread: 1 (d=64) or 2 (d=128)
-  static_assert(CH % kThreads == 0, "step / thread split");
-  uint4 qreg[CPT], greg[CPT];
-  float st_m = 0.0f, st_l = 0.0f, st_d = 0.0f;
+  const size_t dq_head = (size_t)b * a.Hq * N * D;
 
-  bwd_fetch<D, CPT>(a, 0, hk, b, qstart, nsteps, tid, qreg, greg, st_m, st_l, st_d);
-  bwd_stage<D, CPT, QSTR, TSTR>(tid, qreg, greg, st_m, st_l, st_d, Qs, dOs, Qt, dOt, sm2, sinvl, sdel);
-  for (int sidx = 0; sidx < total; ++sidx) {
-    const int hq = hk * a.group + sidx / nsteps;
-    const int q0 = qstart + (sidx % nsteps) * BM;
-    float* __restrict__ dQ = a.dq_acc + ((size_t)(b * a.Hq + hq) * N) * D;
-    __syncthreads();  // this step's tiles are visible; the dS tile is free
-    if (sidx + 1 < total)
-      bwd_fetch<D, CPT>(a, sidx + 1, hk, b, qstart, nsteps, tid, qreg, greg, st_m, st_l, st_d);
+  BwdStep<D> st;
+  bwd_fetch<D>(a, hk * a.group, qstart, b, tid, st);
+  bwd_stage<D, QSTR>(tid, st, Qs[0], dOs[0], slse[0], sdel[0]);
+  if (total > 1)
+    bwd_fetch<D>(a, hk * a.group + 1 / nsteps, qstart + (1 % nsteps) * BM, b, tid, st);
 
-    {
-      const bool active = wk0 < N && (!CAUSAL || q0 + BM - 1 >= wk0);
-      if (active) {
-        // ---- S = Q K^T and dP = dO V^T: lane = key, register i = row 8(i/4)+4*half+i%4
-        f32x16 s, dp;
+  for (int s = 0; s < total; ++s) {
+    const int cur = s & 1;
+    const int q0 = qstart + (s % nsteps) * BM;
+    // stage s is visible; every wave is done with step s-1's stage (written
+    // next) and with the dS tile that step s-2's dQ read (written below)
+    __syncthreads();
+    if (s + 1 < total) {
+      bwd_stage<D, QSTR>(tid, st, Qs[cur ^ 1], dOs[cur ^ 1], slse[cur ^ 1], sdel[cur ^ 1]);
+      if (s + 2 < total)
+        bwd_fetch<D>(a, hk * a.group + (s + 2) / nsteps, qstart + ((s + 2) % nsteps) * BM, b, tid, st);
+    }
+
+    if (bwd_block_live<CAUSAL>(k0, wave, q0, N)) {
+      const uint16_t* qs = Qs[cur];
+      const uint16_t* gs = dOs[cur];
+      // ---- S = Q K^T and dP = dO V^T: lane = key, register i = row 8(i/4)+4*half+i%4
+      f32x16 sv, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = 0.0f;
+        dp[i] = 0.0f;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 qa = *(const bf16x8*)(&qs[l32 * QSTR + 16 * t + 8 * half]);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], sv, 0, 0, 0);
+        const bf16x8 ga = *(const bf16x8*)(&gs[l32 * QSTR + 16 * t + 8 * half]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[t], dp, 0, 0, 0);
+      }
+      // ---- P = exp2(s * alpha*log2(e) - lse2) and dS = P (dP - delta)
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rl = 8 * g + 4 * half;  // first of the 4 rows of this group
+        const f32x4 lv = *(const f32x4*)(&slse[cur][rl]);
+        const f32x4 dl = *(const f32x4*)(&sdel[cur][rl]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * g + u;
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.c1, -lv[u]));
+          dsv[i] = pv[i] * (dp[i] - dl[u]);
+        }
+      }
+      // only the block on the diagonal and the ragged ends mask: element i
+      // (row q0 + 4*half + r_i, r_i = 8(i/4) + i%4) is visible iff
+      // lo <= r_i < hi
+      const bool edge = (CAUSAL && wk0 + 31 > q0) || q0 + BM > N || wk0 + 32 > N;
+      if (__builtin_expect(edge, 0)) {
+        // an empty volatile asm keeps this block a branch: the compiler
+        // would otherwise turn it into selects executed on every step
+        asm volatile("");
+        const int lo = CAUSAL ? key - q0 - 4 * half : 0;
+        const int hi = key < N ? N - q0 - 4 * half : 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s[i] = 0.0f;
-          dp[i] = 0.0f;
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const bf16x8 qa = *(const bf16x8*)(&Qs[l32 * QSTR + 16 * t + 8 * half]);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], s, 0, 0, 0);
-          const bf16x8 ga = *(const bf16x8*)(&dOs[l32 * QSTR + 16 * t + 8 * half]);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[t], dp, 0, 0, 0);
-        }
-        // ---- P = exp(t - m)/ℓ and dS = P (dP - delta)
-        bf16x8 pa[2], sa[2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rl = 8 * g + 4 * half;  // first of the 4 rows of this group
-          const f32x4 mv = *(const f32x4*)(&sm2[rl]);
-          const f32x4 lv = *(const f32x4*)(&sinvl[rl]);
-          const f32x4 dv4 = *(const f32x4*)(&sdel[rl]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * g + u;
-            const int qr = q0 + rl + u;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.c1, -mv[u])) * lv[u];
-            const bool vis = key < N && qr < N && (!CAUSAL || key <= qr);
-            if (!vis) p = 0.0f;
-            const float ds = vis ? p * (dp[i] - dv4[u]) : 0.0f;
-            pa[i >> 3][i & 7] = (__bf16)p;
-            sa[i >> 3][i & 7] = (__bf16)ds;
-            dSs[(rl + u) * SSTR + 32 * wave + l32] = bf16_bits(ds);
+          const int ri = 8 * (i >> 2) + (i & 3);
+          if (ri < lo || ri >= hi) {
+            pv[i] = 0.0f;
+            dsv[i] = 0.0f;
           }
         }
-        // ---- dV += P^T dO and dK += dS^T Q (contraction over the 32 rows,
-        // register 8t+j holds row 16t + 8(j/4) + 4*half + j%4)
+      }
+      // bf16 operands: register 8t+j of pa/sa is element i = 8t+j
+      bf16x8 pa[2], sa[2];
 #pragma unroll
-        for (int f = 0; f < FB; ++f) {
-          const uint16_t* gr = &dOt[(32 * f + l32) * TSTR];
-          const uint16_t* qr = &Qt[(32 * f + l32) * TSTR];
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t p0 = pack_bf16(pv[8 * t + 0], pv[8 * t + 1]);
+        const uint32_t p1 = pack_bf16(pv[8 * t + 2], pv[8 * t + 3]);
+        const uint32_t p2 = pack_bf16(pv[8 * t + 4], pv[8 * t + 5]);
+        const uint32_t p3 = pack_bf16(pv[8 * t + 6], pv[8 * t + 7]);
+        pa[t] = __builtin_bit_cast(bf16x8, make_uint4(p0, p1, p2, p3));
+        const uint32_t s0 = pack_bf16(dsv[8 * t + 0], dsv[8 * t + 1]);
+        const uint32_t s1 = pack_bf16(dsv[8 * t + 2], dsv[8 * t + 3]);
+        const uint32_t s2 = pack_bf16(dsv[8 * t + 4], dsv[8 * t + 5]);
+        const uint32_t s3 = pack_bf16(dsv[8 * t + 6], dsv[8 * t + 7]);
+        sa[t] = __builtin_bit_cast(bf16x8, make_uint4(s0, s1, s2, s3));
+        // dS key-major: this lane's key, rows 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
+        uint16_t* drow = &dSt[cur][(32 * wave + l32) * DSTR + 16 * t + 4 * half];
+        *(uint2*)(drow) = make_uint2(s0, s1);
+        *(uint2*)(drow + 8) = make_uint2(s2, s3);
+      }
+      // ---- dV += P^T dO and dK += dS^T Q, contraction over the 32 rows:
+      // the k index 8*half + j of product t is row 16t + 8(j/4) + 4*half + j%4,
+      // so the B operand is two transpose reads of 4 rows each
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const uint2 glo = *(const uint2*)(gr + 16 * t + 4 * half);
-            const uint2 ghi = *(const uint2*)(gr + 16 * t + 8 + 4 * half);
-            const bf16x8 gb = __builtin_bit_cast(bf16x8, make_uint4(glo.x, glo.y, ghi.x, ghi.y));
-            dv[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], gb, dv[f], 0, 0, 0);
-            const uint2 qlo = *(const uint2*)(qr + 16 * t + 4 * half);
-            const uint2 qhi = *(const uint2*)(qr + 16 * t + 8 + 4 * half);
-            const bf16x8 qb = __builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
-            dk[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], qb, dk[f], 0, 0, 0);
-          }
+      for (int f = 0; f < FB; ++f) {
+        const int n0 = 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = 16 * t + 4 * (g16 >> 1) + (r16 >> 2);
+          const uint16_t* pg = gs + row * QSTR + n0;
+          const bf16x8 gb = frag2(lds_read_tr(pg), lds_read_tr(pg + 8 * QSTR));
+          dv[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], gb, dv[f], 0, 0, 0);
+          const uint16_t* pq = qs + row * QSTR + n0;
+          const bf16x8 qb = frag2(lds_read_tr(pq), lds_read_tr(pq + 8 * QSTR));
+          dk[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], qb, dk[f], 0, 0, 0);
         }
-      } else {
-        // nothing visible: this wave's dS columns are zero
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          dSs[(8 * (i >> 2) + 4 * half + (i & 3)) * SSTR + 32 * wave + l32] = 0;
       }
     }
-    __syncthreads();  // the dS tile is complete; the staging tiles are free
-    if (sidx + 1 < total)
-      bwd_stage<D, CPT, QSTR, TSTR>(tid, qreg, greg, st_m, st_l, st_d, Qs, dOs, Qt, dOt, sm2, sinvl, sdel);
 
-    // ---- dQ[q0..q0+31][16-feature slice] += dS K over the 128 keys
-    const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-    for (int sl = 0; sl < DQB; ++sl) {
-      const int d0 = 16 * (wave * DQB + sl);
-#pragma unroll
-      for (int mq = 0; mq < 2; ++mq) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk) {
-          const bf16x8 da = *(const bf16x8*)(&dSs[(16 * mq + lr) * SSTR + 32 * kk + 8 * lq]);
-          const bf16x8 kb = *(const bf16x8*)(&Kt[(d0 + lr) * KTSTR + 32 * kk + 8 * lq]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, kb, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qr = q0 + 16 * mq + 4 * lq + i;
-          if (qr < N) unsafeAtomicAdd(&dQ[(size_t)qr * D + d0 + lr], acc[i]);
-        }
-      }
+    // ---- dQ of the previous step (its dS tile is complete since the barrier)
+    if (s > 0) {
+      const int sp = s - 1;
+      const int hq = hk * a.group + sp / nsteps;
+      bwd_dq<D, CAUSAL, DQB>(a, dSt[cur ^ 1], kq, a.dq_acc + dq_head + (size_t)hq * N * D,
+                             qstart + (sp % nsteps) * BM, k0, wave, g16, r16);
     }
+  }
+  __syncthreads();
+  {
+    const int sp = total - 1;
+    const int hq = hk * a.group + sp / nsteps;
+    bwd_dq<D, CAUSAL, DQB>(a, dSt[sp & 1], kq, a.dq_acc + dq_head + (size_t)hq * N * D,
+                           qstart + (sp % nsteps) * BM, k0, wave, g16, r16);
   }
 
   // ---- dK = alpha * sum dS^T Q, dV = sum P^T dO for this wave's 32 keys

@@ -61,7 +61,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform over the wave: keeping it scalar makes every
+  // per-wave condition below a scalar branch instead of an exec mask
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int N = a.N;
   const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
@@ -175,30 +177,39 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
       }
     }
-    // key of s[kb][i] in this lane: j0 + 32kb + 8(i/4) + 4*half + i%4
+    // key of s[kb][i] in this lane: j0 + 32kb + 8(i/4) + 4*half + i%4; only
+    // the block holding the diagonal (causal) or the sequence end masks
     const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > q0);
-    if (edge) {
-      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+    if (__builtin_expect(edge, 0)) {
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - j0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key > lim) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
     }
 
-    // ---- running top two (repeated-maximum detection)
+    // ---- running top two (repeated-maximum detection), two scores at a
+    // time: with tr >= tr2, the second largest of {tr, tr2, x, y} is
+    // max(tr2, med3(tr, x, y)) and the largest is max(tr, x, y)
     float tr = -INFINITY, tr2 = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = s[kb][i];
-        tr2 = __builtin_amdgcn_fmed3f(tr, tr2, x);  // = max(tr2, min(tr, x))
-        tr = fmaxf(tr, x);
+      for (int i = 0; i < 16; i += 2) {
+        const float x = s[kb][i], y = s[kb][i + 1];
+        tr2 = fmaxf(tr2, __builtin_amdgcn_fmed3f(tr, x, y));
+        tr = fmaxf(tr, fmaxf(x, y));
       }
-    top2_merge(tr, tr2, __shfl_xor(tr, 32), __shfl_xor(tr2, 32));
+    // merge with the other lane half (same rows): after the swap each lane
+    // holds both halves' values, paired by source lane
+    {
+      const auto a1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tr), __float_as_uint(tr), false, false);
+      const auto a2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tr2), __float_as_uint(tr2), false, false);
+      tr = __uint_as_float(a1[0]);
+      tr2 = __uint_as_float(a2[0]);
+      top2_merge(tr, tr2, __uint_as_float(a1[1]), __uint_as_float(a2[1]));
+    }
     top2_merge(R, R2, tr, tr2);
 
     // ---- tie decision and shift on the scaled logits t = alpha * s

@@ -80,8 +80,7 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_post(const BwdArgs& a, int d, hipStream_t s);
 
-// Keys per workgroup and query rows per inner step of the backward.
-constexpr int kBwdBlockN = 64;
+// Query rows per inner step of the backward.
 constexpr int kBwdBlockM = 32;
 
 }  // namespace attn
