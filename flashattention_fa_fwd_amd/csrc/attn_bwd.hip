@@ -91,11 +91,11 @@ __global__ __launch_bounds__(kThreads) void bwd_post_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- bwd_main
-// LDS transpose read (gfx950): within each group of 16 lanes, lane r points
-// at 4 consecutive bf16 of row r/4, columns 4(r%4)..4(r%4)+3, of a block of
-// 4 rows x 16 columns; lane i receives column i of those 4 rows.  For a
-// matrix stored with the MFMA's m or n index contiguous, that is 4
-// consecutive contraction indices of one m or n: half an operand fragment.
+// LDS transpose read (gfx950): within each group of 16 lanes, lane r supplies
+// the address of 4 consecutive bf16 E_r; lane i receives E_{4j + i/4}[i%4]
+// for j = 0..3.  If lane r points at row k0 + r/4, columns n0 + 4(r%4)..+3 of
+// a matrix X, lane i receives X[k0 + 0..3][n0 + i]: four consecutive
+// contraction indices of one row or column, half of an MFMA operand.
 __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -113,6 +113,23 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
+
+// Q / dO stage tiles: row r of D bf16, its 16-byte chunk c stored at chunk
+// c ^ qswz(r).  Eight consecutive rows reading one chunk (the A-operand
+// reads) and four consecutive rows reading two adjacent chunks (the
+// transpose reads) then hit 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int qswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int qidx(int r, int col) {  // col % 4 == 0
+  return r * D + ((((col >> 3) ^ qswz(r))) << 3) + (col & 7);
+}
+
+// dS tile, key-major: key k (0..127) holds the 32 rows of the step as eight
+// 8-byte units (rows 4u..4u+3), unit u stored at u ^ dswz(k).  Sixteen
+// consecutive keys writing one unit, and four consecutive keys read at four
+// adjacent units (transpose reads), then use distinct banks.
+__device__ __forceinline__ int dswz(int k) { return (((k >> 1) & 1) << 2) | ((k >> 2) & 3); }
+__device__ __forceinline__ int didx(int k, int u) { return k * kBwdBlockM + 4 * (u ^ dswz(k)); }
 
 // One step = 32 query rows of one query head of the group.  Its Q and dO
 // rows and the rows' statistics are fetched into registers one step ahead
@@ -155,15 +172,15 @@ __device__ __forceinline__ void bwd_fetch(const BwdArgs& a, int hq, int q0, int 
   }
 }
 
-template <int D, int QSTR>
+template <int D>
 __device__ __forceinline__ void bwd_stage(int tid, const BwdStep<D>& st, uint16_t* Qs,
                                           uint16_t* dOs, float* slse, float* sdel) {
 #pragma unroll
   for (int u = 0; u < BwdStep<D>::CPT; ++u) {
     const int c = tid + u * kThreads;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    *(uint4*)(&Qs[row * QSTR + col]) = st.q[u];
-    *(uint4*)(&dOs[row * QSTR + col]) = st.g[u];
+    *(uint4*)(&Qs[qidx<D>(row, col)]) = st.q[u];
+    *(uint4*)(&dOs[qidx<D>(row, col)]) = st.g[u];
   }
   if (tid < kBwdBlockM) {
     slse[tid] = st.lse2;
@@ -171,37 +188,45 @@ __device__ __forceinline__ void bwd_stage(int tid, const BwdStep<D>& st, uint16_
   }
 }
 
-constexpr int kBwdKeys = 128;             // keys per workgroup (32 per wave)
-constexpr int kBwdKB = kBwdKeys / 32;     // 32-key blocks per workgroup
-constexpr int kBwdDSTR = kBwdBlockM + 16; // row stride of the key-major dS tile
+constexpr int kBwdKeys = 128;          // keys per workgroup (32 per wave)
+constexpr int kBwdKB = kBwdKeys / 32;  // 32-key blocks per workgroup
 
-// Does 32-key block kb of the workgroup hold a key visible to rows q0..q0+31?
-template <bool CAUSAL>
-__device__ __forceinline__ bool bwd_block_live(int k0, int kb, int q0, int N) {
-  return k0 + 32 * kb < N && (!CAUSAL || q0 + kBwdBlockM - 1 >= k0 + 32 * kb);
-}
+// Position of a step: query head (within the group) and first row.
+struct StepPos {
+  int h, q0;
+  __device__ __forceinline__ void next(int qstart, int N) {
+    q0 += kBwdBlockM;
+    if (q0 >= N) {
+      q0 = qstart;
+      ++h;
+    }
+  }
+};
 
-// dQ[q0..q0+31][this wave's features] += dS K over the workgroup's live key
-// blocks (v_mfma_f32_16x16x32_bf16), one atomic add per element.
-template <int D, bool CAUSAL, int DQB>
-__device__ __forceinline__ void bwd_dq(const BwdArgs& a, const uint16_t* ds,
+// dQ[q0..q0+31][this wave's features] += dS K over the workgroup's 128 keys
+// (v_mfma_f32_16x16x32_bf16; key blocks with no visible key hold zeros),
+// one atomic add per element.
+template <int D, int DQB>
+__device__ __forceinline__ void bwd_dq(int N, const uint16_t* ds,
                                        const bf16x8 (&kq)[DQB][kBwdKB], float* dQ, int q0,
-                                       int k0, int wave, int g16, int r16) {
-  const int N = a.N;
+                                       int wave, int g16, int r16) {
 #pragma unroll
   for (int sl = 0; sl < DQB; ++sl) {
     const int d0 = 16 * (wave * DQB + sl);
 #pragma unroll
     for (int mq = 0; mq < 2; ++mq) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      // A = dS[rows 16mq + r16][keys 32kb + 8*g16 + 0..7]
+      bf16x8 da[kBwdKB];
 #pragma unroll
       for (int kb = 0; kb < kBwdKB; ++kb) {
-        if (!bwd_block_live<CAUSAL>(k0, kb, q0, N)) continue;
-        // A = dS[rows 16mq + r16][keys 32kb + 8*g16 + 0..7], tile stored key-major
-        const uint16_t* p = ds + (32 * kb + 8 * g16 + (r16 >> 2)) * kBwdDSTR + 16 * mq + 4 * (r16 & 3);
-        const bf16x8 da = frag2(lds_read_tr(p), lds_read_tr(p + 4 * kBwdDSTR));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, kq[sl][kb], acc, 0, 0, 0);
+        const int kk = 32 * kb + 8 * g16 + (r16 >> 2);
+        const int u = 4 * mq + (r16 & 3);
+        da[kb] = frag2(lds_read_tr(ds + didx(kk, u)), lds_read_tr(ds + didx(kk + 4, u)));
       }
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kBwdKB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kb], kq[sl][kb], acc, 0, 0, 0);
       const int r0 = q0 + 16 * mq + 4 * g16;  // C register i holds row r0 + i
       float* dst = dQ + (size_t)r0 * D + d0 + r16;
       if (q0 + kBwdBlockM <= N) {
@@ -222,16 +247,14 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   constexpr int BM = kBwdBlockM;     // query rows per step (32)
   constexpr int NT = D / kMfmaK;     // 16-wide steps along d
   constexpr int FB = D / 32;         // 32-feature blocks of dK/dV
-  constexpr int QSTR = D + 8;        // row stride of the Q / dO tiles
-  constexpr int DSTR = kBwdDSTR;
   constexpr int DQB = D / 16 / 4;    // 16-feature dQ slices per wave (1 or 2)
   constexpr int KB = kBwdKB;
 
   // two stages: step s computes from stage s&1 while step s+1 is written
   // to the other; the dS tile is double-buffered the same way
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * QSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BM * QSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dSt[2][BN * DSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dSt[2][BN * BM];
   __shared__ __attribute__((aligned(16))) float slse[2][BM];
   __shared__ __attribute__((aligned(16))) float sdel[2][BM];
 
@@ -292,32 +315,49 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
       dv[f][i] = 0.0f;
     }
 
+  // per-lane LDS offsets (elements) that do not change from step to step
+  int qa_off[NT];  // A operand: row l32, chunk 2t + half
+#pragma unroll
+  for (int t = 0; t < NT; ++t) qa_off[t] = qidx<D>(l32, 16 * t + 8 * half);
+  const int trow = 4 * (g16 >> 1) + (r16 >> 2);  // transpose reads: row within 16
+  int tb_off[FB];  // B operand of dV/dK, product t = 0; t = 1 is 16 rows on
+#pragma unroll
+  for (int f = 0; f < FB; ++f) tb_off[f] = qidx<D>(trow, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
+  const int kl = 32 * wave + l32;  // this lane's key within the tile
+
   // Steps: every 32-row slice of every query head of the group, from the
   // first row that can see these keys.
   const int qstart = CAUSAL ? k0 : 0;
   const int nsteps = (N - qstart + BM - 1) / BM;
   const int total = nsteps * a.group;
-  const size_t dq_head = (size_t)b * a.Hq * N * D;
+  const int hq0 = hk * a.group;
+  float* const dq_base = a.dq_acc + (size_t)b * a.Hq * N * D;
 
+  StepPos pf{0, qstart};  // the step being fetched
+  StepPos pc{0, qstart};  // the step being computed
+  StepPos pp{0, qstart};  // the step whose dQ is being added
   BwdStep<D> st;
-  bwd_fetch<D>(a, hk * a.group, qstart, b, tid, st);
-  bwd_stage<D, QSTR>(tid, st, Qs[0], dOs[0], slse[0], sdel[0]);
-  if (total > 1)
-    bwd_fetch<D>(a, hk * a.group + 1 / nsteps, qstart + (1 % nsteps) * BM, b, tid, st);
+  bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
+  bwd_stage<D>(tid, st, Qs[0], dOs[0], slse[0], sdel[0]);
+  pf.next(qstart, N);
+  if (total > 1) bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
+  pf.next(qstart, N);
 
   for (int s = 0; s < total; ++s) {
     const int cur = s & 1;
-    const int q0 = qstart + (s % nsteps) * BM;
+    const int q0 = pc.q0;
     // stage s is visible; every wave is done with step s-1's stage (written
     // next) and with the dS tile that step s-2's dQ read (written below)
     __syncthreads();
     if (s + 1 < total) {
-      bwd_stage<D, QSTR>(tid, st, Qs[cur ^ 1], dOs[cur ^ 1], slse[cur ^ 1], sdel[cur ^ 1]);
-      if (s + 2 < total)
-        bwd_fetch<D>(a, hk * a.group + (s + 2) / nsteps, qstart + ((s + 2) % nsteps) * BM, b, tid, st);
+      bwd_stage<D>(tid, st, Qs[cur ^ 1], dOs[cur ^ 1], slse[cur ^ 1], sdel[cur ^ 1]);
+      if (s + 2 < total) bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
+      pf.next(qstart, N);
     }
 
-    if (bwd_block_live<CAUSAL>(k0, wave, q0, N)) {
+    uint16_t* dsw = dSt[cur];
+    const bool live = wk0 < N && (!CAUSAL || q0 + BM - 1 >= wk0);
+    if (live) {
       const uint16_t* qs = Qs[cur];
       const uint16_t* gs = dOs[cur];
       // ---- S = Q K^T and dP = dO V^T: lane = key, register i = row 8(i/4)+4*half+i%4
@@ -329,9 +369,9 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const bf16x8 qa = *(const bf16x8*)(&qs[l32 * QSTR + 16 * t + 8 * half]);
+        const bf16x8 qa = *(const bf16x8*)(&qs[qa_off[t]]);
         sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], sv, 0, 0, 0);
-        const bf16x8 ga = *(const bf16x8*)(&gs[l32 * QSTR + 16 * t + 8 * half]);
+        const bf16x8 ga = *(const bf16x8*)(&gs[qa_off[t]]);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[t], dp, 0, 0, 0);
       }
       // ---- P = exp2(s * alpha*log2(e) - lse2) and dS = P (dP - delta)
@@ -381,45 +421,41 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
         const uint32_t s2 = pack_bf16(dsv[8 * t + 4], dsv[8 * t + 5]);
         const uint32_t s3 = pack_bf16(dsv[8 * t + 6], dsv[8 * t + 7]);
         sa[t] = __builtin_bit_cast(bf16x8, make_uint4(s0, s1, s2, s3));
-        // dS key-major: this lane's key, rows 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
-        uint16_t* drow = &dSt[cur][(32 * wave + l32) * DSTR + 16 * t + 4 * half];
-        *(uint2*)(drow) = make_uint2(s0, s1);
-        *(uint2*)(drow + 8) = make_uint2(s2, s3);
+        // dS key-major: rows 16t + 4*half + 0..3 (unit 4t + half) and 8 on
+        *(uint2*)(&dsw[didx(kl, 4 * t + half)]) = make_uint2(s0, s1);
+        *(uint2*)(&dsw[didx(kl, 4 * t + 2 + half)]) = make_uint2(s2, s3);
       }
       // ---- dV += P^T dO and dK += dS^T Q, contraction over the 32 rows:
       // the k index 8*half + j of product t is row 16t + 8(j/4) + 4*half + j%4,
       // so the B operand is two transpose reads of 4 rows each
 #pragma unroll
       for (int f = 0; f < FB; ++f) {
-        const int n0 = 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int row = 16 * t + 4 * (g16 >> 1) + (r16 >> 2);
-          const uint16_t* pg = gs + row * QSTR + n0;
-          const bf16x8 gb = frag2(lds_read_tr(pg), lds_read_tr(pg + 8 * QSTR));
+          const int o = tb_off[f] + 16 * t * D;  // rows 16t + trow (row & 7 unchanged)
+          const bf16x8 gb = frag2(lds_read_tr(gs + o), lds_read_tr(gs + o + 8 * D));
           dv[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], gb, dv[f], 0, 0, 0);
-          const uint16_t* pq = qs + row * QSTR + n0;
-          const bf16x8 qb = frag2(lds_read_tr(pq), lds_read_tr(pq + 8 * QSTR));
+          const bf16x8 qb = frag2(lds_read_tr(qs + o), lds_read_tr(qs + o + 8 * D));
           dk[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], qb, dk[f], 0, 0, 0);
         }
       }
+    } else {
+      // no key of this wave is visible to these rows: its dS columns are zero
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *(uint2*)(&dsw[didx(kl, 2 * u + half)]) = make_uint2(0, 0);
     }
 
     // ---- dQ of the previous step (its dS tile is complete since the barrier)
     if (s > 0) {
-      const int sp = s - 1;
-      const int hq = hk * a.group + sp / nsteps;
-      bwd_dq<D, CAUSAL, DQB>(a, dSt[cur ^ 1], kq, a.dq_acc + dq_head + (size_t)hq * N * D,
-                             qstart + (sp % nsteps) * BM, k0, wave, g16, r16);
+      bwd_dq<D, DQB>(N, dSt[cur ^ 1], kq, dq_base + (size_t)(hq0 + pp.h) * N * D, pp.q0, wave,
+                     g16, r16);
+      pp.next(qstart, N);
     }
+    pc.next(qstart, N);
   }
   __syncthreads();
-  {
-    const int sp = total - 1;
-    const int hq = hk * a.group + sp / nsteps;
-    bwd_dq<D, CAUSAL, DQB>(a, dSt[sp & 1], kq, a.dq_acc + dq_head + (size_t)hq * N * D,
-                           qstart + (sp % nsteps) * BM, k0, wave, g16, r16);
-  }
+  bwd_dq<D, DQB>(N, dSt[(total - 1) & 1], kq, dq_base + (size_t)(hq0 + pp.h) * N * D, pp.q0,
+                 wave, g16, r16);
 
   // ---- dK = alpha * sum dS^T Q, dV = sum P^T dO for this wave's 32 keys
 #pragma unroll
