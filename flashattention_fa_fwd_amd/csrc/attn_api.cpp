@@ -46,8 +46,12 @@ int guard_of(uint32_t flags) {
   }
 }
 
+// fp32 dQ accumulator [B, Hq, Npad, d]: each head's rows are padded to a
+// multiple of the backward's 32-row step so the last step adds without a
+// bounds test (the padding rows are never read)
 size_t ws_bytes(const attn_params* p) {
-  return (size_t)p->batch * p->heads_q * p->seqlen * p->head_dim * sizeof(float);
+  return (size_t)p->batch * p->heads_q * attn::bwd_padded_rows(p->seqlen) * p->head_dim *
+         sizeof(float);
 }
 
 attn::BwdArgs bwd_args(const attn_params* p, const void* q, const void* k, const void* v,
@@ -70,6 +74,7 @@ attn::BwdArgs bwd_args(const attn_params* p, const void* q, const void* k, const
   a.Hq = p->heads_q;
   a.Hkv = p->heads_kv;
   a.N = p->seqlen;
+  a.Npad = attn::bwd_padded_rows(p->seqlen);
   a.group = p->heads_q / p->heads_kv;
   a.alpha = scale_of(p);
   a.c1 = a.alpha * attn::kLog2e;

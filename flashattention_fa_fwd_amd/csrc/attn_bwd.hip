@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
         acc = __builtin_fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
       }
     }
-    float* dq = a.dq_acc + row * D + part * EPT;
+    float* dq = a.dq_acc + ((row / a.N) * a.Npad + row % a.N) * D + part * EPT;
 #pragma unroll
     for (int c = 0; c < EPT; c += 4) *(f32x4*)(dq + c) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -84,7 +84,8 @@ __global__ __launch_bounds__(kThreads) void bwd_post_kernel(BwdArgs a) {
   const size_t n4 = (size_t)a.B * a.Hq * a.N * D / 4;
   const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n4) return;
-  const f32x4 v = *(const f32x4*)(a.dq_acc + 4 * i);
+  const size_t row = 4 * i / D;
+  const f32x4 v = *(const f32x4*)(a.dq_acc + ((row / a.N) * a.Npad + row % a.N) * D + 4 * i % D);
   const uint32_t lo = bf16_bits(a.alpha * v[0]) | ((uint32_t)bf16_bits(a.alpha * v[1]) << 16);
   const uint32_t hi = bf16_bits(a.alpha * v[2]) | ((uint32_t)bf16_bits(a.alpha * v[3]) << 16);
   *(uint2*)(a.dq + 4 * i) = make_uint2(lo, hi);
@@ -138,7 +139,7 @@ template <int D>
 struct BwdStep {
   static constexpr int CPT = kBwdBlockM * D / 8 / kThreads;  // 16-byte chunks per thread
   uint4 q[CPT], g[CPT];
-  float lse2, del;  // threads 0..31: m*log2(e) + log2(l) of the row, and delta
+  float m, l, del;  // threads 0..31: the row's shift, denominator and delta
 };
 
 template <int D>
@@ -157,16 +158,16 @@ __device__ __forceinline__ void bwd_fetch(const BwdArgs& a, int hq, int q0, int 
       st.g[u] = *(const uint4*)(a.dout + qoff + (size_t)(q0 + row) * D + col);
     }
   }
+  // raw loads only: nothing here waits for them (a wait would also wait for
+  // every atomic issued before)
   if (tid < kBwdBlockM) {
     const size_t r = (size_t)(b * a.Hq + hq) * N + q0 + tid;
-    st.lse2 = 0.0f;
+    st.m = 0.0f;
+    st.l = 1.0f;
     st.del = 0.0f;
     if (q0 + tid < N) {
-      const float l = a.row_l[r];
-      // P = exp(t - m) / l = exp2(t*log2(e) - lse2); a row whose every
-      // weight underflowed (l == 0) keeps P = NaN, as 0 * (1/0) gives
-      st.lse2 = l > 0.0f ? __builtin_fmaf(a.row_m[r], kLog2e, __builtin_log2f(l))
-                         : __builtin_nanf("");
+      st.m = a.row_m[r];
+      st.l = a.row_l[r];
       st.del = a.delta[r];
     }
   }
@@ -183,7 +184,10 @@ __device__ __forceinline__ void bwd_stage(int tid, const BwdStep<D>& st, uint16_
     *(uint4*)(&dOs[qidx<D>(row, col)]) = st.g[u];
   }
   if (tid < kBwdBlockM) {
-    slse[tid] = st.lse2;
+    // P = exp(t - m) / l = exp2(t*log2(e) - lse2); a row whose every weight
+    // underflowed (l == 0) keeps P = NaN, as 0 * (1/0) gives
+    slse[tid] = st.l > 0.0f ? __builtin_fmaf(st.m, kLog2e, __builtin_log2f(st.l))
+                            : __builtin_nanf("");
     sdel[tid] = st.del;
   }
 }
@@ -205,9 +209,10 @@ struct StepPos {
 
 // dQ[q0..q0+31][this wave's features] += dS K over the workgroup's 128 keys
 // (v_mfma_f32_16x16x32_bf16; key blocks with no visible key hold zeros),
-// one atomic add per element.
+// one atomic add per element.  dQ has whole 32-row steps per head (rows past
+// the sequence end receive zeros and are never read).
 template <int D, int DQB>
-__device__ __forceinline__ void bwd_dq(int N, const uint16_t* ds,
+__device__ __forceinline__ void bwd_dq(const uint16_t* ds,
                                        const bf16x8 (&kq)[DQB][kBwdKB], float* dQ, int q0,
                                        int wave, int g16, int r16) {
 #pragma unroll
@@ -227,16 +232,10 @@ __device__ __forceinline__ void bwd_dq(int N, const uint16_t* ds,
 #pragma unroll
       for (int kb = 0; kb < kBwdKB; ++kb)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kb], kq[sl][kb], acc, 0, 0, 0);
-      const int r0 = q0 + 16 * mq + 4 * g16;  // C register i holds row r0 + i
-      float* dst = dQ + (size_t)r0 * D + d0 + r16;
-      if (q0 + kBwdBlockM <= N) {
+      // C register i holds row q0 + 16mq + 4*g16 + i
+      float* dst = dQ + (size_t)(q0 + 16 * mq + 4 * g16) * D + d0 + r16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + (size_t)i * D, acc[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r0 + i < N) unsafeAtomicAdd(dst + (size_t)i * D, acc[i]);
-      }
+      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + (size_t)i * D, acc[i]);
     }
   }
 }
@@ -263,9 +262,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   const int half = lane >> 5, l32 = lane & 31;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int N = a.N;
-  const int nkb = (N + BN - 1) / BN;
   int kvhead, kblk;
-  xcd_map((int)blockIdx.x, nkb, a.B * a.Hkv, kvhead, kblk);
+  xcd_map((int)blockIdx.x, a.B * a.Hkv, kvhead, kblk);  // kblk 0 (most rows) first
   const int hk = kvhead % a.Hkv, b = kvhead / a.Hkv;
   const int k0 = kblk * BN;
   const int wk0 = k0 + 32 * wave;     // this wave's first key
@@ -331,11 +329,15 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   const int nsteps = (N - qstart + BM - 1) / BM;
   const int total = nsteps * a.group;
   const int hq0 = hk * a.group;
-  float* const dq_base = a.dq_acc + (size_t)b * a.Hq * N * D;
+  float* const dq_base = a.dq_acc + (size_t)b * a.Hq * a.Npad * D;
 
   StepPos pf{0, qstart};  // the step being fetched
   StepPos pc{0, qstart};  // the step being computed
   StepPos pp{0, qstart};  // the step whose dQ is being added
+  // the dQ block of step 0 reads "step -1"'s tile: zeros, added to step 0's rows
+#pragma unroll
+  for (int u = 0; u < BN * BM / 8 / kThreads; ++u)
+    *(uint4*)(&dSt[1][8 * (tid + u * kThreads)]) = make_uint4(0, 0, 0, 0);
   BwdStep<D> st;
   bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
   bwd_stage<D>(tid, st, Qs[0], dOs[0], slse[0], sdel[0]);
@@ -346,14 +348,23 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   for (int s = 0; s < total; ++s) {
     const int cur = s & 1;
     const int q0 = pc.q0;
-    // stage s is visible; every wave is done with step s-1's stage (written
-    // next) and with the dS tile that step s-2's dQ read (written below)
+    // stage s and step s-1's dS tile are complete; every wave is done with
+    // step s-1's stage (written next) and with the dS tile that step s-2's
+    // dQ read (written below)
     __syncthreads();
+    // Waiting for a fetch also waits for every global atomic issued before
+    // the wait (the counter covers both), so the order is: stage the step
+    // fetched one iteration ago, issue the next fetch and the previous
+    // step's dQ atomics together, and compute while both are in flight.
     if (s + 1 < total) {
       bwd_stage<D>(tid, st, Qs[cur ^ 1], dOs[cur ^ 1], slse[cur ^ 1], sdel[cur ^ 1]);
       if (s + 2 < total) bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
       pf.next(qstart, N);
     }
+    // dQ of the previous step: issued inside both branches below, so its
+    // matrix and memory work interleaves with this step's
+    const uint16_t* dsp = dSt[cur ^ 1];
+    float* const dqp = dq_base + (size_t)(hq0 + pp.h) * a.Npad * D;
 
     uint16_t* dsw = dSt[cur];
     const bool live = wk0 < N && (!CAUSAL || q0 + BM - 1 >= wk0);
@@ -374,6 +385,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
         const bf16x8 ga = *(const bf16x8*)(&gs[qa_off[t]]);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[t], dp, 0, 0, 0);
       }
+      bwd_dq<D, DQB>(dsp, kq, dqp, pp.q0, wave, g16, r16);
       // ---- P = exp2(s * alpha*log2(e) - lse2) and dS = P (dP - delta)
       float pv[16], dsv[16];
 #pragma unroll
@@ -443,18 +455,13 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
       // no key of this wave is visible to these rows: its dS columns are zero
 #pragma unroll
       for (int u = 0; u < 4; ++u) *(uint2*)(&dsw[didx(kl, 2 * u + half)]) = make_uint2(0, 0);
+      bwd_dq<D, DQB>(dsp, kq, dqp, pp.q0, wave, g16, r16);
     }
-
-    // ---- dQ of the previous step (its dS tile is complete since the barrier)
-    if (s > 0) {
-      bwd_dq<D, DQB>(N, dSt[cur ^ 1], kq, dq_base + (size_t)(hq0 + pp.h) * N * D, pp.q0, wave,
-                     g16, r16);
-      pp.next(qstart, N);
-    }
+    if (s > 0) pp.next(qstart, N);
     pc.next(qstart, N);
   }
   __syncthreads();
-  bwd_dq<D, DQB>(N, dSt[(total - 1) & 1], kq, dq_base + (size_t)(hq0 + pp.h) * N * D, pp.q0,
+  bwd_dq<D, DQB>(dSt[(total - 1) & 1], kq, dq_base + (size_t)(hq0 + pp.h) * a.Npad * D, pp.q0,
                  wave, g16, r16);
 
   // ---- dK = alpha * sum dS^T Q, dV = sum P^T dO for this wave's 32 keys

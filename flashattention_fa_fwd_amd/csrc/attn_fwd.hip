@@ -68,8 +68,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int N = a.N;
   const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
   int head, r;
-  xcd_map((int)blockIdx.x, nmb, a.B * a.Hq, head, r);
-  const int mb = CAUSAL ? (nmb - 1 - r) : r;  // a head's heavy (causal) blocks first
+  xcd_map((int)blockIdx.x, a.B * a.Hq, head, r);
+  const int mb = CAUSAL ? (nmb - 1 - r) : r;  // heavy (causal) blocks first
   const int hq = head % a.Hq, b = head / a.Hq;
   const int hk = hq / a.group;
   const int q0 = mb * kFwdBlockM + wave * 32;

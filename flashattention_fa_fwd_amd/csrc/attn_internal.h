@@ -52,25 +52,29 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;   // workspace: fp32 [B, Hq, N, d]
-  int B, Hq, Hkv, N, group;
+  float* dq_acc;   // workspace: fp32 [B, Hq, Npad, d]
+  int B, Hq, Hkv, N, Npad, group;
   float alpha, c1;
 };
 
 // Workgroup order on the 8 XCDs (each with its own L2): the hardware hands
 // consecutive workgroup ids to XCDs round-robin.  When the number of heads is
-// a multiple of 8, head h's blocks get ids that all land on XCD h/(heads/8),
-// so one head's K/V (forward) or Q/dO (backward) is re-read from one L2.
+// a multiple of 8, head h's blocks all land on XCD h/(heads/8), so one head's
+// K/V (forward) or Q/dO (backward) is re-read from one L2.  Within an XCD the
+// ids go block-major (block 0 of every head, then block 1, ...), and callers
+// number blocks heaviest first, so the longest workgroups of a causal launch
+// start first and the tail is short.
 // Returns (head index, block index) for linear workgroup id L.
-__device__ __forceinline__ void xcd_map(int L, int nblk, int heads, int& head, int& blk) {
+__device__ __forceinline__ void xcd_map(int L, int heads, int& head, int& blk) {
   constexpr int kXcds = 8;
   if (heads % kXcds == 0) {
+    const int hpx = heads / kXcds;
     const int xcd = L % kXcds, local = L / kXcds;
-    head = xcd * (heads / kXcds) + local / nblk;
-    blk = local % nblk;
+    blk = local / hpx;
+    head = xcd * hpx + local % hpx;
   } else {
-    head = L / nblk;
-    blk = L % nblk;
+    blk = L / heads;
+    head = L % heads;
   }
 }
 
@@ -80,7 +84,9 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_post(const BwdArgs& a, int d, hipStream_t s);
 
-// Query rows per inner step of the backward.
+// Query rows per inner step of the backward, and the per-head row count of
+// its fp32 dQ accumulator (rows padded to whole steps).
 constexpr int kBwdBlockM = 32;
+inline int bwd_padded_rows(int n) { return (n + kBwdBlockM - 1) / kBwdBlockM * kBwdBlockM; }
 
 }  // namespace attn
