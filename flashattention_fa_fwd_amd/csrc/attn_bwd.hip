@@ -132,64 +132,75 @@ __device__ __forceinline__ int qidx(int r, int col) {  // col % 4 == 0
 __device__ __forceinline__ int dswz(int k) { return (((k >> 1) & 1) << 2) | ((k >> 2) & 3); }
 __device__ __forceinline__ int didx(int k, int u) { return k * kBwdBlockM + 4 * (u ^ dswz(k)); }
 
-// One step = 32 query rows of one query head of the group.  Its Q and dO
-// rows and the rows' statistics are fetched into registers one step ahead
-// and then written to one of two LDS stages.
-template <int D>
-struct BwdStep {
-  static constexpr int CPT = kBwdBlockM * D / 8 / kThreads;  // 16-byte chunks per thread
-  uint4 q[CPT], g[CPT];
-  float m, l, del;  // threads 0..31: the row's shift, denominator and delta
-};
+// Roles of the four waves of a workgroup.  Every wave computes S, dP, P, dS,
+// dV and dK for its own 32 keys.  Beyond that, waves 0-1 ("loaders") fetch
+// the next steps' Q and dO rows and statistics into the LDS stages, and
+// waves 2-3 ("dQ waves") compute the previous step's dQ rows and add them
+// with global atomics.  A wait for a fetch also waits for every atomic its
+// wave issued before (one counter covers both), and atomics queue at the L2;
+// with the roles split no wave ever waits for an atomic inside the loop.
+constexpr int kBwdLoaders = 2;
+// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family GPUs.
+constexpr int kBufferWord3 = 0x00020000;
+// s_waitcnt vmcnt(0) with the other counters left free.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
+// One step = 32 query rows of one query head of the group.  The loaders copy
+// its Q and dO rows straight into one of the two LDS stages with buffer
+// loads to LDS (16 bytes a lane, a wave's 64 lanes filling 1 KiB of the tile
+// in lane order; each lane picks the global chunk that belongs at its tile
+// position under the swizzle).  Rows past the sequence end lie outside the
+// buffer's range and read as zeros.
 template <int D>
-__device__ __forceinline__ void bwd_fetch(const BwdArgs& a, int hq, int q0, int b, int tid,
-                                          BwdStep<D>& st) {
-  const int N = a.N;
-  const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
+__device__ __forceinline__ void bwd_load(const BwdArgs& a, int hq, int q0, int b, int lw,
+                                         int lane, uint16_t* Qs, uint16_t* dOs) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int CPR = D / 8;                                  // 16-byte chunks per row
+  constexpr int NI = kBwdBlockM * CPR / 64 / kBwdLoaders;     // 1 KiB pieces per loader per tensor
+  const size_t hoff = ((size_t)(b * a.Hq + hq) * a.N) * D;
+  const int nbytes = a.N * D * 2;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + hoff), 0, nbytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rg =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + hoff), 0, nbytes, kBufferWord3);
 #pragma unroll
-  for (int u = 0; u < BwdStep<D>::CPT; ++u) {
-    const int c = tid + u * kThreads;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    st.q[u] = make_uint4(0, 0, 0, 0);
-    st.g[u] = make_uint4(0, 0, 0, 0);
-    if (q0 + row < N) {
-      st.q[u] = *(const uint4*)(a.q + qoff + (size_t)(q0 + row) * D + col);
-      st.g[u] = *(const uint4*)(a.dout + qoff + (size_t)(q0 + row) * D + col);
-    }
-  }
-  // raw loads only: nothing here waits for them (a wait would also wait for
-  // every atomic issued before)
-  if (tid < kBwdBlockM) {
-    const size_t r = (size_t)(b * a.Hq + hq) * N + q0 + tid;
-    st.m = 0.0f;
-    st.l = 1.0f;
-    st.del = 0.0f;
-    if (q0 + tid < N) {
-      st.m = a.row_m[r];
-      st.l = a.row_l[r];
-      st.del = a.delta[r];
-    }
+  for (int u = 0; u < NI; ++u) {
+    const int piece = lw * NI + u;
+    const int p = piece * 64 + lane;                // chunk position in the tile
+    const int row = p / CPR;
+    const int c = (p % CPR) ^ qswz(row);            // logical chunk stored there
+    const int voff = ((q0 + row) * D + 8 * c) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(Qs + piece * 512), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void*)(dOs + piece * 512), 16, voff, 0, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void bwd_stage(int tid, const BwdStep<D>& st, uint16_t* Qs,
-                                          uint16_t* dOs, float* slse, float* sdel) {
-#pragma unroll
-  for (int u = 0; u < BwdStep<D>::CPT; ++u) {
-    const int c = tid + u * kThreads;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    *(uint4*)(&Qs[qidx<D>(row, col)]) = st.q[u];
-    *(uint4*)(&dOs[qidx<D>(row, col)]) = st.g[u];
+// Row statistics of a step (threads 0..31 of wave 0): raw loads, then the
+// log2-domain shift once they have arrived.
+struct BwdStats {
+  float m, l, del;
+};
+
+__device__ __forceinline__ void bwd_stats_load(const BwdArgs& a, int hq, int q0, int b, int tid,
+                                               BwdStats& st) {
+  const size_t r = (size_t)(b * a.Hq + hq) * a.N + q0 + tid;
+  st.m = 0.0f;
+  st.l = 1.0f;
+  st.del = 0.0f;
+  if (q0 + tid < a.N) {
+    st.m = a.row_m[r];
+    st.l = a.row_l[r];
+    st.del = a.delta[r];
   }
-  if (tid < kBwdBlockM) {
-    // P = exp(t - m) / l = exp2(t*log2(e) - lse2); a row whose every weight
-    // underflowed (l == 0) keeps P = NaN, as 0 * (1/0) gives
-    slse[tid] = st.l > 0.0f ? __builtin_fmaf(st.m, kLog2e, __builtin_log2f(st.l))
-                            : __builtin_nanf("");
-    sdel[tid] = st.del;
-  }
+}
+
+__device__ __forceinline__ void bwd_stats_store(int tid, const BwdStats& st, float* slse,
+                                                float* sdel) {
+  // P = exp(t - m) / l = exp2(t*log2(e) - lse2); a row whose every weight
+  // underflowed (l == 0) keeps P = NaN, as 0 * (1/0) gives
+  slse[tid] = st.l > 0.0f ? __builtin_fmaf(st.m, kLog2e, __builtin_log2f(st.l))
+                          : __builtin_nanf("");
+  sdel[tid] = st.del;
 }
 
 constexpr int kBwdKeys = 128;          // keys per workgroup (32 per wave)
@@ -207,53 +218,182 @@ struct StepPos {
   }
 };
 
-// dQ[q0..q0+31][this wave's features] += dS K over the workgroup's 128 keys
-// (v_mfma_f32_16x16x32_bf16; key blocks with no visible key hold zeros),
-// one atomic add per element.  dQ has whole 32-row steps per head (rows past
-// the sequence end receive zeros and are never read).
-template <int D, int DQB>
-__device__ __forceinline__ void bwd_dq(const uint16_t* ds,
-                                       const bf16x8 (&kq)[DQB][kBwdKB], float* dQ, int q0,
-                                       int wave, int g16, int r16) {
+// dQ[q0..q0+31][D/2 features from f0] += dS K over the workgroup's 128 keys
+// (v_mfma_f32_16x16x32_bf16 on 16x16 tiles; key blocks with no visible key
+// hold zeros in the dS tile), one atomic add per element.  K comes from the
+// workgroup's K tile through the transpose read.  dQ has whole 32-row steps
+// per head (rows past the sequence end receive zeros and are never read).
+template <int D>
+__device__ __forceinline__ void bwd_dq(const uint16_t* ds, const uint16_t* ks, float* dQ, int q0,
+                                       int f0, int g16, int r16) {
+  constexpr int NJ = D / 32;  // 16-feature tiles
+  f32x4 acc[2][NJ];
 #pragma unroll
-  for (int sl = 0; sl < DQB; ++sl) {
-    const int d0 = 16 * (wave * DQB + sl);
+  for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[mq][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one 32-key block at a time: its dS rows (A) and K columns (B)
+#pragma unroll
+  for (int kb = 0; kb < kBwdKB; ++kb) {
+    const int kk = 32 * kb + 8 * g16 + (r16 >> 2);
+    bf16x8 da[2], kq[NJ];
 #pragma unroll
     for (int mq = 0; mq < 2; ++mq) {
       // A = dS[rows 16mq + r16][keys 32kb + 8*g16 + 0..7]
-      bf16x8 da[kBwdKB];
-#pragma unroll
-      for (int kb = 0; kb < kBwdKB; ++kb) {
-        const int kk = 32 * kb + 8 * g16 + (r16 >> 2);
-        const int u = 4 * mq + (r16 & 3);
-        da[kb] = frag2(lds_read_tr(ds + didx(kk, u)), lds_read_tr(ds + didx(kk + 4, u)));
-      }
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < kBwdKB; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kb], kq[sl][kb], acc, 0, 0, 0);
-      // C register i holds row q0 + 16mq + 4*g16 + i
-      float* dst = dQ + (size_t)(q0 + 16 * mq + 4 * g16) * D + d0 + r16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + (size_t)i * D, acc[i]);
+      const int u = 4 * mq + (r16 & 3);
+      da[mq] = frag2(lds_read_tr(ds + didx(kk, u)), lds_read_tr(ds + didx(kk + 4, u)));
     }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      // B = K[keys 32kb + 8*g16 + 0..7][f0 + 16j + r16]
+      const int col = f0 + 16 * j + 4 * (r16 & 3);
+      kq[j] = frag2(lds_read_tr(ks + qidx<D>(kk, col)), lds_read_tr(ks + qidx<D>(kk + 4, col)));
+    }
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[mq][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[mq], kq[j], acc[mq][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      // C register i holds row q0 + 16mq + 4*g16 + i
+      float* dst = dQ + (size_t)(q0 + 16 * mq + 4 * g16) * D + f0 + 16 * j + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + (size_t)i * D, acc[mq][j][i]);
+    }
+}
+
+// Everything one wave does for one step after the stage barrier: S, dP, P,
+// dS (written key-major to the step's dS tile), dV and dK for its keys, and
+// for a dQ wave the previous step's dQ, in one block so that the two
+// interleave.
+template <int D, bool CAUSAL, bool DQW>
+__device__ __forceinline__ void bwd_step(
+    const BwdArgs& a, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+    const int (&qa_off)[D / kMfmaK], const int (&ka_off)[D / kMfmaK], const int (&tb_off)[D / 32],
+    const uint16_t* qs, const uint16_t* gs, const float* slse, const float* sdel, uint16_t* dsw,
+    const uint16_t* dsp, const uint16_t* ks, const uint16_t* vs, float* dqp, int qp, int f0, int q0,
+    int wk0, int key, int kl, int half, int l32, int g16, int r16) {
+  constexpr int BM = kBwdBlockM;
+  constexpr int NT = D / kMfmaK;
+  constexpr int FB = D / 32;
+  const int N = a.N;
+  const bool live = wk0 < N && (!CAUSAL || q0 + BM - 1 >= wk0);
+  if (!live) {
+    // no key of this wave is visible to these rows: its dS columns are zero
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(uint2*)(&dsw[didx(kl, 2 * u + half)]) = make_uint2(0, 0);
+    if (DQW) bwd_dq<D>(dsp, ks, dqp, qp, f0, g16, r16);
+    return;
+  }
+  // ---- S = Q K^T and dP = dO V^T: lane = key, register i = row 8(i/4)+4*half+i%4
+  f32x16 sv, dp;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sv[i] = 0.0f;
+    dp[i] = 0.0f;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    // B operands: this lane's key row of K and V, features 16t + 8*half + 0..7
+    const bf16x8 kb = *(const bf16x8*)(&ks[ka_off[t]]);
+    const bf16x8 vb = *(const bf16x8*)(&vs[ka_off[t]]);
+    const bf16x8 qa = *(const bf16x8*)(&qs[qa_off[t]]);
+    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, sv, 0, 0, 0);
+    const bf16x8 ga = *(const bf16x8*)(&gs[qa_off[t]]);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, dp, 0, 0, 0);
+  }
+  // ---- P = exp2(s * alpha*log2(e) - lse2) and dS = P (dP - delta)
+  float pv[16], dsv[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int rl = 8 * g + 4 * half;  // first of the 4 rows of this group
+    const f32x4 lv = *(const f32x4*)(&slse[rl]);
+    const f32x4 dl = *(const f32x4*)(&sdel[rl]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * g + u;
+      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.c1, -lv[u]));
+      dsv[i] = pv[i] * (dp[i] - dl[u]);
+    }
+  }
+  // only the block on the diagonal and the ragged ends mask: element i
+  // (row q0 + 4*half + r_i, r_i = 8(i/4) + i%4) is visible iff lo <= r_i < hi
+  const bool edge = (CAUSAL && wk0 + 31 > q0) || q0 + BM > N || wk0 + 32 > N;
+  if (__builtin_expect(edge, 0)) {
+    // an empty volatile asm keeps this block a branch: the compiler would
+    // otherwise turn it into selects executed on every step
+    asm volatile("");
+    const int lo = CAUSAL ? key - q0 - 4 * half : 0;
+    const int hi = key < N ? N - q0 - 4 * half : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ri = 8 * (i >> 2) + (i & 3);
+      if (ri < lo || ri >= hi) {
+        pv[i] = 0.0f;
+        dsv[i] = 0.0f;
+      }
+    }
+  }
+  // bf16 operands: register 8t+j of pa/sa is element i = 8t+j
+  bf16x8 pa[2], sa[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t p0 = pack_bf16(pv[8 * t + 0], pv[8 * t + 1]);
+    const uint32_t p1 = pack_bf16(pv[8 * t + 2], pv[8 * t + 3]);
+    const uint32_t p2 = pack_bf16(pv[8 * t + 4], pv[8 * t + 5]);
+    const uint32_t p3 = pack_bf16(pv[8 * t + 6], pv[8 * t + 7]);
+    pa[t] = __builtin_bit_cast(bf16x8, make_uint4(p0, p1, p2, p3));
+    const uint32_t s0 = pack_bf16(dsv[8 * t + 0], dsv[8 * t + 1]);
+    const uint32_t s1 = pack_bf16(dsv[8 * t + 2], dsv[8 * t + 3]);
+    const uint32_t s2 = pack_bf16(dsv[8 * t + 4], dsv[8 * t + 5]);
+    const uint32_t s3 = pack_bf16(dsv[8 * t + 6], dsv[8 * t + 7]);
+    sa[t] = __builtin_bit_cast(bf16x8, make_uint4(s0, s1, s2, s3));
+    // dS key-major: rows 16t + 4*half + 0..3 (unit 4t + half) and 8 on
+    *(uint2*)(&dsw[didx(kl, 4 * t + half)]) = make_uint2(s0, s1);
+    *(uint2*)(&dsw[didx(kl, 4 * t + 2 + half)]) = make_uint2(s2, s3);
+  }
+  // ---- dV += P^T dO and dK += dS^T Q, contraction over the 32 rows: the k
+  // index 8*half + j of product t is row 16t + 8(j/4) + 4*half + j%4, so the
+  // B operand is two transpose reads of 4 rows each
+#pragma unroll
+  for (int f = 0; f < FB; ++f) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int o = tb_off[f] + 16 * t * D;  // rows 16t + trow (row & 7 unchanged)
+      const bf16x8 gb = frag2(lds_read_tr(gs + o), lds_read_tr(gs + o + 8 * D));
+      dv[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], gb, dv[f], 0, 0, 0);
+      const bf16x8 qb = frag2(lds_read_tr(qs + o), lds_read_tr(qs + o + 8 * D));
+      dk[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], qb, dk[f], 0, 0, 0);
+    }
+  }
+  if (DQW) {
+    // keep the dQ work after this step's (the scheduler would otherwise
+    // hoist its reads into the softmax and exceed the register budget)
+    __builtin_amdgcn_sched_barrier(0);
+    bwd_dq<D>(dsp, ks, dqp, qp, f0, g16, r16);
   }
 }
 
+// d = 64: two workgroups per CU (two waves per SIMD, at most 256 VGPRs a
+// wave); d = 128 needs more registers and runs one.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs a) {
   constexpr int BN = kBwdKeys;
   constexpr int BM = kBwdBlockM;     // query rows per step (32)
   constexpr int NT = D / kMfmaK;     // 16-wide steps along d
   constexpr int FB = D / 32;         // 32-feature blocks of dK/dV
-  constexpr int DQB = D / 16 / 4;    // 16-feature dQ slices per wave (1 or 2)
-  constexpr int KB = kBwdKB;
 
   // two stages: step s computes from stage s&1 while step s+1 is written
   // to the other; the dS tile is double-buffered the same way
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * D];
   __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BM * D];
   __shared__ __attribute__((aligned(16))) uint16_t dSt[2][BN * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * D];
   __shared__ __attribute__((aligned(16))) float slse[2][BM];
   __shared__ __attribute__((aligned(16))) float sdel[2][BM];
 
@@ -272,37 +412,20 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   const uint16_t* __restrict__ K = a.k + kvoff;
   const uint16_t* __restrict__ V = a.v + kvoff;
 
-  // K and V rows of this lane's key as B operands of S = Q K^T and
-  // dP = dO V^T: [16t + 8*half + 0..7]
-  bf16x8 kf[NT], vf[NT];
+  // the workgroup's K and V rows, row-major (swizzled like the stages): the
+  // B operands of S = Q K^T and dP = dO V^T, and K for the dQ product
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int u = 0; u < BN * D / 8 / kThreads; ++u) {
+    const int c = tid + u * kThreads;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
     uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-    if (key < N) {
-      kr = *(const uint4*)(K + (size_t)key * D + 16 * t + 8 * half);
-      vr = *(const uint4*)(V + (size_t)key * D + 16 * t + 8 * half);
+    if (k0 + row < N) {
+      kr = *(const uint4*)(K + (size_t)(k0 + row) * D + col);
+      vr = *(const uint4*)(V + (size_t)(k0 + row) * D + col);
     }
-    kf[t] = __builtin_bit_cast(bf16x8, kr);
-    vf[t] = __builtin_bit_cast(bf16x8, vr);
+    *(uint4*)(&Ks[qidx<D>(row, col)]) = kr;
+    *(uint4*)(&Vs[qidx<D>(row, col)]) = vr;
   }
-  // K as the B operand of this wave's dQ slices: lane holds
-  // K[k0 + 32kb + 8*g16 + 0..7][d0 + r16] for every 32-key block kb
-  bf16x8 kq[DQB][KB];
-#pragma unroll
-  for (int sl = 0; sl < DQB; ++sl)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int d0 = 16 * (wave * DQB + sl);
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = k0 + 32 * kb + 8 * g16 + 2 * j;
-        const uint32_t lo = kk < N ? K[(size_t)kk * D + d0 + r16] : 0u;
-        const uint32_t hi = kk + 1 < N ? K[(size_t)(kk + 1) * D + d0 + r16] : 0u;
-        w[j] = lo | (hi << 16);
-      }
-      kq[sl][kb] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-    }
 
   f32x16 dk[FB], dv[FB];
 #pragma unroll
@@ -315,13 +438,19 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
 
   // per-lane LDS offsets (elements) that do not change from step to step
   int qa_off[NT];  // A operand: row l32, chunk 2t + half
+  int ka_off[NT];  // K/V B operand: key row 32*wave + l32, chunk 2t + half
 #pragma unroll
-  for (int t = 0; t < NT; ++t) qa_off[t] = qidx<D>(l32, 16 * t + 8 * half);
+  for (int t = 0; t < NT; ++t) {
+    qa_off[t] = qidx<D>(l32, 16 * t + 8 * half);
+    ka_off[t] = qidx<D>(32 * wave + l32, 16 * t + 8 * half);
+  }
   const int trow = 4 * (g16 >> 1) + (r16 >> 2);  // transpose reads: row within 16
   int tb_off[FB];  // B operand of dV/dK, product t = 0; t = 1 is 16 rows on
 #pragma unroll
   for (int f = 0; f < FB; ++f) tb_off[f] = qidx<D>(trow, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
   const int kl = 32 * wave + l32;  // this lane's key within the tile
+  const bool loader = wave < kBwdLoaders;
+  const int f0 = (D / 2) * (wave - kBwdLoaders);  // dQ waves: first of their D/2 features
 
   // Steps: every 32-row slice of every query head of the group, from the
   // first row that can see these keys.
@@ -334,135 +463,56 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
   StepPos pf{0, qstart};  // the step being fetched
   StepPos pc{0, qstart};  // the step being computed
   StepPos pp{0, qstart};  // the step whose dQ is being added
-  // the dQ block of step 0 reads "step -1"'s tile: zeros, added to step 0's rows
+  // the dQ of step 0 reads "step -1"'s tile: zeros, added to step 0's rows
 #pragma unroll
   for (int u = 0; u < BN * BM / 8 / kThreads; ++u)
     *(uint4*)(&dSt[1][8 * (tid + u * kThreads)]) = make_uint4(0, 0, 0, 0);
-  BwdStep<D> st;
-  bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
-  bwd_stage<D>(tid, st, Qs[0], dOs[0], slse[0], sdel[0]);
-  pf.next(qstart, N);
-  if (total > 1) bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
+  BwdStats st;
+  if (loader) {
+    bwd_load<D>(a, hq0 + pf.h, pf.q0, b, wave, lane, Qs[0], dOs[0]);
+    if (tid < BM) {
+      bwd_stats_load(a, hq0 + pf.h, pf.q0, b, tid, st);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      bwd_stats_store(tid, st, slse[0], sdel[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
   pf.next(qstart, N);
 
   for (int s = 0; s < total; ++s) {
     const int cur = s & 1;
-    const int q0 = pc.q0;
     // stage s and step s-1's dS tile are complete; every wave is done with
     // step s-1's stage (written next) and with the dS tile that step s-2's
     // dQ read (written below)
     __syncthreads();
-    // Waiting for a fetch also waits for every global atomic issued before
-    // the wait (the counter covers both), so the order is: stage the step
-    // fetched one iteration ago, issue the next fetch and the previous
-    // step's dQ atomics together, and compute while both are in flight.
-    if (s + 1 < total) {
-      bwd_stage<D>(tid, st, Qs[cur ^ 1], dOs[cur ^ 1], slse[cur ^ 1], sdel[cur ^ 1]);
-      if (s + 2 < total) bwd_fetch<D>(a, hq0 + pf.h, pf.q0, b, tid, st);
-      pf.next(qstart, N);
+    // loaders: step s+1 goes to the other stage while step s computes
+    const bool more = s + 1 < total;
+    if (loader && more) {
+      bwd_load<D>(a, hq0 + pf.h, pf.q0, b, wave, lane, Qs[cur ^ 1], dOs[cur ^ 1]);
+      if (tid < BM) bwd_stats_load(a, hq0 + pf.h, pf.q0, b, tid, st);
     }
-    // dQ of the previous step: issued inside both branches below, so its
-    // matrix and memory work interleaves with this step's
-    const uint16_t* dsp = dSt[cur ^ 1];
+    pf.next(qstart, N);
     float* const dqp = dq_base + (size_t)(hq0 + pp.h) * a.Npad * D;
-
-    uint16_t* dsw = dSt[cur];
-    const bool live = wk0 < N && (!CAUSAL || q0 + BM - 1 >= wk0);
-    if (live) {
-      const uint16_t* qs = Qs[cur];
-      const uint16_t* gs = dOs[cur];
-      // ---- S = Q K^T and dP = dO V^T: lane = key, register i = row 8(i/4)+4*half+i%4
-      f32x16 sv, dp;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = 0.0f;
-        dp[i] = 0.0f;
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 qa = *(const bf16x8*)(&qs[qa_off[t]]);
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], sv, 0, 0, 0);
-        const bf16x8 ga = *(const bf16x8*)(&gs[qa_off[t]]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[t], dp, 0, 0, 0);
-      }
-      bwd_dq<D, DQB>(dsp, kq, dqp, pp.q0, wave, g16, r16);
-      // ---- P = exp2(s * alpha*log2(e) - lse2) and dS = P (dP - delta)
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = 8 * g + 4 * half;  // first of the 4 rows of this group
-        const f32x4 lv = *(const f32x4*)(&slse[cur][rl]);
-        const f32x4 dl = *(const f32x4*)(&sdel[cur][rl]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * g + u;
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.c1, -lv[u]));
-          dsv[i] = pv[i] * (dp[i] - dl[u]);
-        }
-      }
-      // only the block on the diagonal and the ragged ends mask: element i
-      // (row q0 + 4*half + r_i, r_i = 8(i/4) + i%4) is visible iff
-      // lo <= r_i < hi
-      const bool edge = (CAUSAL && wk0 + 31 > q0) || q0 + BM > N || wk0 + 32 > N;
-      if (__builtin_expect(edge, 0)) {
-        // an empty volatile asm keeps this block a branch: the compiler
-        // would otherwise turn it into selects executed on every step
-        asm volatile("");
-        const int lo = CAUSAL ? key - q0 - 4 * half : 0;
-        const int hi = key < N ? N - q0 - 4 * half : 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ri = 8 * (i >> 2) + (i & 3);
-          if (ri < lo || ri >= hi) {
-            pv[i] = 0.0f;
-            dsv[i] = 0.0f;
-          }
-        }
-      }
-      // bf16 operands: register 8t+j of pa/sa is element i = 8t+j
-      bf16x8 pa[2], sa[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t p0 = pack_bf16(pv[8 * t + 0], pv[8 * t + 1]);
-        const uint32_t p1 = pack_bf16(pv[8 * t + 2], pv[8 * t + 3]);
-        const uint32_t p2 = pack_bf16(pv[8 * t + 4], pv[8 * t + 5]);
-        const uint32_t p3 = pack_bf16(pv[8 * t + 6], pv[8 * t + 7]);
-        pa[t] = __builtin_bit_cast(bf16x8, make_uint4(p0, p1, p2, p3));
-        const uint32_t s0 = pack_bf16(dsv[8 * t + 0], dsv[8 * t + 1]);
-        const uint32_t s1 = pack_bf16(dsv[8 * t + 2], dsv[8 * t + 3]);
-        const uint32_t s2 = pack_bf16(dsv[8 * t + 4], dsv[8 * t + 5]);
-        const uint32_t s3 = pack_bf16(dsv[8 * t + 6], dsv[8 * t + 7]);
-        sa[t] = __builtin_bit_cast(bf16x8, make_uint4(s0, s1, s2, s3));
-        // dS key-major: rows 16t + 4*half + 0..3 (unit 4t + half) and 8 on
-        *(uint2*)(&dsw[didx(kl, 4 * t + half)]) = make_uint2(s0, s1);
-        *(uint2*)(&dsw[didx(kl, 4 * t + 2 + half)]) = make_uint2(s2, s3);
-      }
-      // ---- dV += P^T dO and dK += dS^T Q, contraction over the 32 rows:
-      // the k index 8*half + j of product t is row 16t + 8(j/4) + 4*half + j%4,
-      // so the B operand is two transpose reads of 4 rows each
-#pragma unroll
-      for (int f = 0; f < FB; ++f) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int o = tb_off[f] + 16 * t * D;  // rows 16t + trow (row & 7 unchanged)
-          const bf16x8 gb = frag2(lds_read_tr(gs + o), lds_read_tr(gs + o + 8 * D));
-          dv[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], gb, dv[f], 0, 0, 0);
-          const bf16x8 qb = frag2(lds_read_tr(qs + o), lds_read_tr(qs + o + 8 * D));
-          dk[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], qb, dk[f], 0, 0, 0);
-        }
-      }
-    } else {
-      // no key of this wave is visible to these rows: its dS columns are zero
-#pragma unroll
-      for (int u = 0; u < 4; ++u) *(uint2*)(&dsw[didx(kl, 2 * u + half)]) = make_uint2(0, 0);
-      bwd_dq<D, DQB>(dsp, kq, dqp, pp.q0, wave, g16, r16);
+    if (loader)
+      bwd_step<D, CAUSAL, false>(a, dk, dv, qa_off, ka_off, tb_off, Qs[cur], dOs[cur], slse[cur],
+                                 sdel[cur], dSt[cur], dSt[cur ^ 1], Ks, Vs, dqp, pp.q0, f0,
+                                 pc.q0, wk0, key, kl, half, l32, g16, r16);
+    else
+      bwd_step<D, CAUSAL, true>(a, dk, dv, qa_off, ka_off, tb_off, Qs[cur], dOs[cur], slse[cur],
+                                sdel[cur], dSt[cur], dSt[cur ^ 1], Ks, Vs, dqp, pp.q0, f0, pc.q0,
+                                wk0, key, kl, half, l32, g16, r16);
+    if (loader && more) {
+      // the copies must land before the next barrier publishes the stage
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      if (tid < BM) bwd_stats_store(tid, st, slse[cur ^ 1], sdel[cur ^ 1]);
     }
     if (s > 0) pp.next(qstart, N);
     pc.next(qstart, N);
   }
   __syncthreads();
-  bwd_dq<D, DQB>(dSt[(total - 1) & 1], kq, dq_base + (size_t)(hq0 + pp.h) * a.Npad * D, pp.q0,
-                 wave, g16, r16);
+  if (!loader)
+    bwd_dq<D>(dSt[(total - 1) & 1], Ks, dq_base + (size_t)(hq0 + pp.h) * a.Npad * D, pp.q0, f0,
+              g16, r16);
 
   // ---- dK = alpha * sum dS^T Q, dV = sum P^T dO for this wave's 32 keys
 #pragma unroll
