@@ -66,15 +66,14 @@ def main():
     kw = dict(causal=wl.causal, guard=args.guard)
     p = fa.make_params(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim,
                        obar_fp32=args.obar_fp32, **kw)
-    ws = fa.alloc_workspace(p, q.device)
     fout, bout = {}, {}
     fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
-    fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], workspace=ws, out=bout, **kw)
+    fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], out=bout, **kw)
     torch.cuda.synchronize()
 
     def step():
         fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
-        fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], workspace=ws, out=bout, **kw)
+        fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], out=bout, **kw)
 
     stream = torch.cuda.current_stream()
 
@@ -98,15 +97,16 @@ def main():
     n_rep = max(20, args.steps)
     ms_fwd = timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw), n_rep, 3)
     delta = bout["delta"]
-    ms_pre = timed(lambda: fa.attn_bwd_preprocess(p, fout["o"], do, delta, ws), n_rep, 3)
-    ms_main = timed(lambda: fa.attn_bwd_main(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
-                                             bout["dk"], bout["dv"], ws), n_rep, 3)
-    ms_fin = timed(lambda: fa.attn_bwd_finalize(p, bout["dq"], ws), n_rep, 3)
+    ms_pre = timed(lambda: fa.attn_bwd_preprocess(p, fout["o"], do, delta), n_rep, 3)
+    ms_dkdv = timed(lambda: fa.attn_bwd_dkdv(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
+                                             bout["dk"], bout["dv"]), n_rep, 3)
+    ms_dq = timed(lambda: fa.attn_bwd_dq(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
+                                         bout["dq"]), n_rep, 3)
     other = "none" if args.guard != "none" else "beta"
     fo2 = {}
     ms_fwd_other = timed(lambda: fa.attn_fwd(q, k, v, causal=wl.causal, guard=other, out=fo2), n_rep, 3)
-    print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_pre {ms_pre:.4f}, bwd_main {ms_main:.4f}, "
-          f"bwd_post {ms_fin:.4f}; fwd with guard={other}: {ms_fwd_other:.4f}", file=sys.stderr, flush=True)
+    print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_pre {ms_pre:.4f}, bwd_dkdv {ms_dkdv:.4f}, "
+          f"bwd_dq {ms_dq:.4f}; fwd with guard={other}: {ms_fwd_other:.4f}", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
@@ -115,13 +115,19 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # Algorithmic matrix flops (causal: the visible half): the forward's two
+    # products (S = Q K^T, O = P V); the backward's five (S recomputed once,
+    # dP, dV, dK, dQ).  Per kernel, the products it performs: bwd_dkdv S, dP,
+    # dV, dK; bwd_dq S, dP, dQ (S and dP are recomputed by both kernels).
     fl_fwd = wl.flops_fwd()
-    fl_bwd = 2.5 * fl_fwd
+    fl_gemm = fl_fwd / 2          # one [N x N x d] product
+    fl_bwd = 5 * fl_gemm
     fl_step = fl_fwd + fl_bwd
     value = fl_step / (ms_step * 1e-3) / 1e12
     kernels = {
         "attn_fwd": (ms_fwd, fl_fwd),
-        "bwd_main": (ms_main, fl_bwd),
+        "bwd_dkdv": (ms_dkdv, 4 * fl_gemm),
+        "bwd_dq": (ms_dq, 3 * fl_gemm),
     }
     dom = max(kernels, key=lambda n: kernels[n][0])
     dms, dfl = kernels[dom]
@@ -148,9 +154,9 @@ def main():
         },
         "pct_of_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "fwd_tflops": round(fl_fwd / (ms_fwd * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(fl_bwd / ((ms_pre + ms_main + ms_fin) * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(fl_bwd / ((ms_pre + ms_dkdv + ms_dq) * 1e-3) / 1e12, 2),
         "kernel_ms": {"attn_fwd": round(ms_fwd, 5), "bwd_pre": round(ms_pre, 5),
-                      "bwd_main": round(ms_main, 5), "bwd_post": round(ms_fin, 5)},
+                      "bwd_dkdv": round(ms_dkdv, 5), "bwd_dq": round(ms_dq, 5)},
         "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
         "roofline": {
             "kernel": dom,

@@ -6,8 +6,8 @@ used only to own device memory and to name the current HIP stream.  There is
 no fallback: if the library is missing or fails to load, every call raises.
 
 The functions carry the C ABI's names: attn_fwd, attn_bwd (and its stages
-attn_bwd_preprocess / attn_bwd_main / attn_bwd_finalize), attn_schedule,
-attn_bwd_workspace_bytes, attn_strerror, attn_abi_version.
+attn_bwd_preprocess / attn_bwd_dkdv / attn_bwd_dq), attn_schedule,
+attn_strerror, attn_abi_version.
 """
 from __future__ import annotations
 
@@ -60,14 +60,12 @@ def lib():
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p]
         L.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.attn_bwd_workspace_bytes.argtypes = [pp]
-        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        L.attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        L.attn_bwd_main.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        L.attn_bwd_finalize.argtypes = [pp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, vp]
+        L.attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for n in ("attn_schedule", "attn_fwd", "attn_bwd", "attn_bwd_preprocess",
-                  "attn_bwd_main", "attn_bwd_finalize"):
+                  "attn_bwd_dkdv", "attn_bwd_dq"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -154,26 +152,14 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
     return res
 
 
-def attn_bwd_workspace_bytes(p: Params) -> int:
-    return int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
-
-
-def alloc_workspace(p: Params, device) -> torch.Tensor:
-    n = attn_bwd_workspace_bytes(p)
-    # torch's caching allocator hands out 512-byte aligned blocks
-    return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=device)
-
-
 def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=2.0,
-             tie_eps=1e-3, shift_eps=2.0 ** -5, softmax_scale=None, workspace=None,
-             out=None, stream=None):
+             tie_eps=1e-3, shift_eps=2.0 ** -5, softmax_scale=None, out=None, stream=None):
     """Backward.  Returns a dict: dq, dk, dv (bf16) and delta (fp32)."""
     for n_, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_bf16(n_, t)
     B, Hq, N, d = q.shape
     p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
                      shift_eps=shift_eps, softmax_scale=softmax_scale)
-    ws = workspace if workspace is not None else alloc_workspace(p, q.device)
     res = out if out is not None else {}
     if "dq" not in res:
         res["dq"] = torch.empty_like(q)
@@ -182,28 +168,25 @@ def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=
         res["delta"] = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _call("attn_bwd", lib().attn_bwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
-        _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["delta"]), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["delta"]), _stream(stream)))
     return res
 
 
-def attn_bwd_preprocess(p: Params, o, dout, delta, workspace, stream=None):
+def attn_bwd_preprocess(p: Params, o, dout, delta, stream=None):
     _call("attn_bwd_preprocess", lib().attn_bwd_preprocess(
-        ctypes.byref(p), _ptr(o), _ptr(dout), _ptr(delta), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        ctypes.byref(p), _ptr(o), _ptr(dout), _ptr(delta), _stream(stream)))
 
 
-def attn_bwd_main(p: Params, q, k, v, dout, row_m, row_l, delta, dk, dv, workspace, stream=None):
-    _call("attn_bwd_main", lib().attn_bwd_main(
+def attn_bwd_dkdv(p: Params, q, k, v, dout, row_m, row_l, delta, dk, dv, stream=None):
+    _call("attn_bwd_dkdv", lib().attn_bwd_dkdv(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(row_m), _ptr(row_l),
-        _ptr(delta), _ptr(dk), _ptr(dv), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
-def attn_bwd_finalize(p: Params, dq, workspace, stream=None):
-    _call("attn_bwd_finalize", lib().attn_bwd_finalize(
-        ctypes.byref(p), _ptr(dq), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+def attn_bwd_dq(p: Params, q, k, v, dout, row_m, row_l, delta, dq, stream=None):
+    _call("attn_bwd_dq", lib().attn_bwd_dq(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(row_m), _ptr(row_l),
+        _ptr(delta), _ptr(dq), _stream(stream)))
 
 
 def default_scale(head_dim: int) -> float:

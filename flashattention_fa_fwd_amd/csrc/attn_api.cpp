@@ -32,9 +32,11 @@ int check_params(const attn_params* p) {
   if (g == ATTN_GUARD_BETA && !(p->beta > 1.0f && std::isfinite(p->beta))) return ATTN_E_PARAM;
   if (!(p->tie_eps >= 0.0f && std::isfinite(p->tie_eps))) return ATTN_E_PARAM;
   if (g == ATTN_GUARD_EPS && !(p->shift_eps > 0.0f && std::isfinite(p->shift_eps))) return ATTN_E_PARAM;
-  // rows * head_dim must fit the kernels' index arithmetic
+  // rows * head_dim must fit the kernels' index arithmetic, and one head's
+  // rows (in bytes) a 32-bit buffer range
   const double elems = (double)p->batch * p->heads_q * p->seqlen * p->head_dim;
   if (elems > 9.0e15) return ATTN_E_SHAPE;
+  if ((double)p->seqlen * p->head_dim * 2.0 >= 2147483648.0) return ATTN_E_SHAPE;
   return ATTN_OK;
 }
 
@@ -46,17 +48,9 @@ int guard_of(uint32_t flags) {
   }
 }
 
-// fp32 dQ accumulator [B, Hq, Npad, d]: each head's rows are padded to a
-// multiple of the backward's 32-row step so the last step adds without a
-// bounds test (the padding rows are never read)
-size_t ws_bytes(const attn_params* p) {
-  return (size_t)p->batch * p->heads_q * attn::bwd_padded_rows(p->seqlen) * p->head_dim *
-         sizeof(float);
-}
-
 attn::BwdArgs bwd_args(const attn_params* p, const void* q, const void* k, const void* v,
                        const void* o, const void* dout, const float* row_m, const float* row_l,
-                       void* dq, void* dk, void* dv, float* delta, void* ws) {
+                       void* dq, void* dk, void* dv, float* delta) {
   attn::BwdArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -69,23 +63,14 @@ attn::BwdArgs bwd_args(const attn_params* p, const void* q, const void* k, const
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
-  a.dq_acc = (float*)ws;
   a.B = p->batch;
   a.Hq = p->heads_q;
   a.Hkv = p->heads_kv;
   a.N = p->seqlen;
-  a.Npad = attn::bwd_padded_rows(p->seqlen);
   a.group = p->heads_q / p->heads_kv;
   a.alpha = scale_of(p);
   a.c1 = a.alpha * attn::kLog2e;
   return a;
-}
-
-int check_ws(const attn_params* p, const void* ws, size_t bytes) {
-  if (!ws) return ATTN_E_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ATTN_E_WORKSPACE;
-  if (bytes < ws_bytes(p)) return ATTN_E_WORKSPACE;
-  return ATTN_OK;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
@@ -100,10 +85,9 @@ const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULL: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "invalid shape (non-positive size or heads_q not a multiple of heads_kv)";
+    case ATTN_E_SHAPE: return "invalid shape (non-positive size, heads_q not a multiple of heads_kv, or a head too large)";
     case ATTN_E_UNSUPPORTED: return "unsupported head_dim (64 or 128) or misaligned tensor pointer";
     case ATTN_E_PARAM: return "invalid parameter (beta, tie_eps, shift_eps, scale or flags)";
-    case ATTN_E_WORKSPACE: return "workspace missing, misaligned or too small";
     case ATTN_E_HIP: return "the HIP runtime rejected a kernel launch";
     default: return "unknown error code";
   }
@@ -154,58 +138,49 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
                                      (hipStream_t)stream));
 }
 
-size_t attn_bwd_workspace_bytes(const attn_params* p) {
-  if (check_params(p) != ATTN_OK) return 0;
-  return ws_bytes(p);
-}
-
 int attn_bwd_preprocess(const attn_params* p, const void* o, const void* dout, float* delta,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_params(p);
+                        void* stream) {
+  const int rc = check_params(p);
   if (rc) return rc;
   if (!o || !dout || !delta) return ATTN_E_NULL;
   if (!aligned16(o) || !aligned16(dout)) return ATTN_E_UNSUPPORTED;
-  rc = check_ws(p, workspace, workspace_bytes);
-  if (rc) return rc;
-  const attn::BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr,
-                                   nullptr, nullptr, nullptr, delta, workspace);
+  const attn::BwdArgs a =
+      bwd_args(p, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, nullptr, delta);
   return hip_status(attn::launch_bwd_pre(a, p->head_dim, (hipStream_t)stream));
 }
 
-int attn_bwd_main(const attn_params* p, const void* q, const void* k, const void* v,
+int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void* v,
                   const void* dout, const float* row_m, const float* row_l, const float* delta,
-                  void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_params(p);
+                  void* dk, void* dv, void* stream) {
+  const int rc = check_params(p);
   if (rc) return rc;
   if (!q || !k || !v || !dout || !row_m || !row_l || !delta || !dk || !dv) return ATTN_E_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dk) ||
       !aligned16(dv))
     return ATTN_E_UNSUPPORTED;
-  rc = check_ws(p, workspace, workspace_bytes);
-  if (rc) return rc;
   const attn::BwdArgs a = bwd_args(p, q, k, v, nullptr, dout, row_m, row_l, nullptr, dk, dv,
-                                   const_cast<float*>(delta), workspace);
-  return hip_status(attn::launch_bwd_main(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
+                                   const_cast<float*>(delta));
+  return hip_status(attn::launch_bwd_dkdv(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
                                           (hipStream_t)stream));
 }
 
-int attn_bwd_finalize(const attn_params* p, void* dq, const void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  int rc = check_params(p);
+int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v,
+                const void* dout, const float* row_m, const float* row_l, const float* delta,
+                void* dq, void* stream) {
+  const int rc = check_params(p);
   if (rc) return rc;
-  if (!dq) return ATTN_E_NULL;
-  if (!aligned16(dq)) return ATTN_E_UNSUPPORTED;
-  rc = check_ws(p, workspace, workspace_bytes);
-  if (rc) return rc;
-  const attn::BwdArgs a = bwd_args(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                   nullptr, dq, nullptr, nullptr, nullptr,
-                                   const_cast<void*>(workspace));
-  return hip_status(attn::launch_bwd_post(a, p->head_dim, (hipStream_t)stream));
+  if (!q || !k || !v || !dout || !row_m || !row_l || !delta || !dq) return ATTN_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq))
+    return ATTN_E_UNSUPPORTED;
+  const attn::BwdArgs a = bwd_args(p, q, k, v, nullptr, dout, row_m, row_l, dq, nullptr, nullptr,
+                                   const_cast<float*>(delta));
+  return hip_status(attn::launch_bwd_dq(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
+                                        (hipStream_t)stream));
 }
 
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
              const void* dout, const float* row_m, const float* row_l, void* dq, void* dk,
-             void* dv, float* delta, void* workspace, size_t workspace_bytes, void* stream) {
+             void* dv, float* delta, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if (!q || !k || !v || !o || !dout || !row_m || !row_l || !dq || !dk || !dv || !delta)
@@ -213,14 +188,11 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_E_UNSUPPORTED;
-  rc = check_ws(p, workspace, workspace_bytes);
+  rc = attn_bwd_preprocess(p, o, dout, delta, stream);
   if (rc) return rc;
-  rc = attn_bwd_preprocess(p, o, dout, delta, workspace, workspace_bytes, stream);
+  rc = attn_bwd_dkdv(p, q, k, v, dout, row_m, row_l, delta, dk, dv, stream);
   if (rc) return rc;
-  rc = attn_bwd_main(p, q, k, v, dout, row_m, row_l, delta, dk, dv, workspace, workspace_bytes,
-                     stream);
-  if (rc) return rc;
-  return attn_bwd_finalize(p, dq, workspace, workspace_bytes, stream);
+  return attn_bwd_dq(p, q, k, v, dout, row_m, row_l, delta, dq, stream);
 }
 
 }  // extern "C"

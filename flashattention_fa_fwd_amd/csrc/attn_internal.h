@@ -52,8 +52,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;   // workspace: fp32 [B, Hq, Npad, d]
-  int B, Hq, Hkv, N, Npad, group;
+  int B, Hq, Hkv, N, group;
   float alpha, c1;
 };
 
@@ -81,12 +80,10 @@ __device__ __forceinline__ void xcd_map(int L, int heads, int& head, int& blk) {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
                       hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s);
-hipError_t launch_bwd_main(const BwdArgs& a, int d, bool causal, hipStream_t s);
-hipError_t launch_bwd_post(const BwdArgs& a, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, hipStream_t s);
 
-// Query rows per inner step of the backward, and the per-head row count of
-// its fp32 dQ accumulator (rows padded to whole steps).
+// Query rows per inner step of the dK/dV kernel.
 constexpr int kBwdBlockM = 32;
-inline int bwd_padded_rows(int n) { return (n + kBwdBlockM - 1) / kBwdBlockM * kBwdBlockM; }
 
 }  // namespace attn

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -54,10 +54,10 @@ extern "C" {
 /* return codes */
 #define ATTN_OK 0
 #define ATTN_E_NULL (-1)        /* a required pointer is NULL                   */
-#define ATTN_E_SHAPE (-2)       /* non-positive size, heads_q % heads_kv != 0   */
+#define ATTN_E_SHAPE (-2)       /* non-positive size, heads_q % heads_kv != 0,
+                                   or seqlen*head_dim*2 >= 2^31                 */
 #define ATTN_E_UNSUPPORTED (-3) /* head_dim not 64/128, misaligned pointer      */
 #define ATTN_E_PARAM (-4)       /* bad beta/tie_eps/shift_eps/flags/scale       */
-#define ATTN_E_WORKSPACE (-5)   /* workspace missing or too small               */
 #define ATTN_E_HIP (-6)         /* the HIP runtime refused a launch             */
 
 typedef struct {
@@ -109,32 +109,31 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
  *   q, k, v, o (bf16), dout [B,Hq,N,d] bf16, row_m, row_l from attn_fwd (in)
  *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d] bf16                  (out)
  *   delta [B,Hq,N] fp32 = rowsum(dO∘O)                      (out, required)
- *   workspace of attn_bwd_workspace_bytes(p) bytes, 256-byte aligned (scratch)
  * dK and dV sum over the heads_q/heads_kv query heads sharing a KV head.
+ * No scratch memory: every output element is written once, by one
+ * workgroup, so results are bitwise reproducible.
  */
-size_t attn_bwd_workspace_bytes(const attn_params* p);
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
              const void* o, const void* dout, const float* row_m, const float* row_l,
-             void* dq, void* dk, void* dv, float* delta, void* workspace,
-             size_t workspace_bytes, void* stream);
+             void* dq, void* dk, void* dv, float* delta, void* stream);
 
-/* attn_bwd's stages, callable one by one (same arguments and rules):
- *   attn_bwd_preprocess: delta = rowsum(dO∘O) in fp32 from the bf16 O, and
- *     clears the fp32 dQ accumulator in the workspace
+/* attn_bwd's stages, callable one by one (same arguments and rules); the
+ * last two only read delta and are independent of each other:
+ *   attn_bwd_preprocess: delta = rowsum(dO∘O) in fp32 from the bf16 O
  *     ([R] "Core idea"/method: the delta term, paper §3.2).
- *   attn_bwd_main: per key block, recompute S and P, then dV += P^T dO,
- *     dP = dO V^T, dS = P∘(dP - delta), dK += dS^T Q, dQ += dS K (fp32
- *     accumulation in the workspace) ([R] "Core idea", Eq. 1-2).
- *   attn_bwd_finalize: dQ = bf16(alpha * accumulated dQ).                 */
+ *   attn_bwd_dkdv: per key, over every query row that sees it, recompute S
+ *     and P, dP = dO V^T, dS = P∘(dP - delta); dV = P^T dO and dK =
+ *     alpha dS^T Q ([R] "Core idea", Eq. 1-2).
+ *   attn_bwd_dq: per query row, over every key it sees, the same S, P, dP
+ *     and dS; dQ = alpha dS K ([R] "Core idea", Eq. 1-2).                  */
 int attn_bwd_preprocess(const attn_params* p, const void* o, const void* dout,
-                        float* delta, void* workspace, size_t workspace_bytes,
-                        void* stream);
-int attn_bwd_main(const attn_params* p, const void* q, const void* k, const void* v,
+                        float* delta, void* stream);
+int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void* v,
                   const void* dout, const float* row_m, const float* row_l,
-                  const float* delta, void* dk, void* dv, void* workspace,
-                  size_t workspace_bytes, void* stream);
-int attn_bwd_finalize(const attn_params* p, void* dq, const void* workspace,
-                      size_t workspace_bytes, void* stream);
+                  const float* delta, void* dk, void* dv, void* stream);
+int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v,
+                const void* dout, const float* row_m, const float* row_l,
+                const float* delta, void* dq, void* stream);
 
 /*
  * attn_schedule -- the rounding schedule attn_fwd uses for these params, so

@@ -29,14 +29,15 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_functions()
-    assert {"attn_fwd", "attn_bwd", "attn_schedule", "attn_bwd_workspace_bytes"} <= set(names)
+    assert {"attn_fwd", "attn_bwd", "attn_schedule", "attn_bwd_preprocess", "attn_bwd_dkdv",
+            "attn_bwd_dq"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    assert fa.attn_abi_version() == 2
+    for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
 
@@ -97,18 +98,20 @@ def test_null_and_alignment_errors(L):
     assert _fwd(L, p, obar=FAKE + 8) == -3
 
 
-def test_workspace_errors(L):
-    p = fa.make_params(2, 4, 2, 100, 64)
-    need = fa.attn_bwd_workspace_bytes(p)
-    assert need == 2 * 4 * 128 * 64 * 4  # fp32 dQ rows padded per head to whole 32-row steps
+def test_backward_argument_errors(L):
+    """The backward stages validate before enqueueing anything (no GPU needed)."""
     vp = ctypes.c_void_p
+    p = fa.make_params(2, 4, 2, 100, 64)
     args = [vp(FAKE)] * 11
-    assert L.attn_bwd(ctypes.byref(p), *args, None, need, None) == -5          # no workspace
-    assert L.attn_bwd(ctypes.byref(p), *args, vp(FAKE), need - 4, None) == -5  # too small
-    assert L.attn_bwd(ctypes.byref(p), *args, vp(FAKE + 16), need, None) == -5  # misaligned
-    assert L.attn_bwd_finalize(ctypes.byref(p), vp(FAKE), None, need, None) == -5
+    assert L.attn_bwd(ctypes.byref(p), *[None] + args[1:], None) == -1          # q missing
+    assert L.attn_bwd(ctypes.byref(p), *[vp(FAKE + 2)] + args[1:], None) == -3  # misaligned
+    assert L.attn_bwd_preprocess(ctypes.byref(p), vp(FAKE), vp(FAKE), None, None) == -1
+    assert L.attn_bwd_dkdv(ctypes.byref(p), *[vp(FAKE)] * 8, None, None) == -1  # dv missing
+    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 7, vp(FAKE + 8), None) == -3
     bad = fa.make_params(1, 3, 2, 10, 64)
-    assert fa.attn_bwd_workspace_bytes(bad) == 0
+    assert L.attn_bwd_dq(ctypes.byref(bad), *[vp(FAKE)] * 8, None) == -2
+    huge = fa.make_params(1, 1, 1, 1 << 24, 64)  # one head past a 32-bit byte range
+    assert L.attn_bwd_dkdv(ctypes.byref(huge), *[vp(FAKE)] * 9, None) == -2
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
