@@ -19,16 +19,18 @@
 // Mapping to CDNA4 (not from the pages):
 //   * one workgroup = 4 wave64s = 128 query rows of one (batch, head); a
 //     wave owns 32 rows;
-//   * per step of 64 keys the block's K rows are staged in LDS row-major
-//     and its V rows transposed (feature-major), shared by the 4 waves;
+//   * per step of 64 keys the block's K and V rows are copied row-major into
+//     one of two LDS stages by buffer-to-LDS loads (the next block is copied
+//     while this one computes; one barrier per step), shared by the 4 waves;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: lane l of a wave owns query
 //     row l%32 and holds 32 of that row's 64 scores (the other 32 sit in lane
 //     l^32), so the row max, the top-two merge and the row sum are in-lane
 //     plus one exchange between the two lane halves;
 //   * P̄ goes to bf16 in registers and is used directly as the B operand of
 //     O^T = V^T P̄^T, whose accumulator has the same lane-to-row ownership,
-//     so the rescale by exp(m_old - m) is a per-lane scalar.
-#include "attn_internal.h"
+//     so the rescale by exp(m_old - m) is a per-lane scalar; the A operand
+//     V^T comes from the row-major V tile through the LDS transpose read.
+#include "attn_device.h"
 
 namespace attn {
 namespace {
@@ -53,18 +55,17 @@ __device__ __forceinline__ void top2_merge(float& a, float& a2, float b, float b
 template <int D, bool CAUSAL, int GUARD, bool OBAR_F32>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   constexpr int BN = kFwdBlockN;
-  constexpr int KSTR = D + 8;    // LDS row stride (elements) of the K tile
-  constexpr int VSTR = BN + 4;   // LDS row stride of the transposed V tile
   constexpr int NT = D / kMfmaK; // matrix steps along d for S
   constexpr int FB = D / 32;     // 32-feature blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
 
   const int tid = threadIdx.x;
   // the wave index is uniform over the wave: keeping it scalar makes every
   // per-wave condition below a scalar branch instead of an exec mask
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
+  const int g16 = lane >> 4, r16 = lane & 15;
   const int N = a.N;
   const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
   int head, r;
@@ -104,65 +105,40 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int kend = CAUSAL ? min(N, (mb + 1) * kFwdBlockM) : N;
   const bool wave_live = q0 < N;
 
-  // The next step's K and V rows are fetched into registers while the current
-  // step computes, so global-load latency overlaps the matrix work.
-  constexpr int KCH = BN * D / 8;          // 16-byte chunks of a K tile
-  constexpr int VCH = (BN / 2) * (D / 8);  // key pairs x 8-feature chunks of V
-  constexpr int KPT = KCH / kThreads, VPT = VCH / kThreads;
-  static_assert(KCH % kThreads == 0 && VCH % kThreads == 0, "tile / thread split");
-  uint4 kreg[KPT], vreg0[VPT], vreg1[VPT];
-  auto fetch = [&](int jb) {
+  const i32x4 rk = head_desc(a.k + kvoff, N, D), rv = head_desc(a.v + kvoff, N, D);
+  // per-lane LDS offsets: K rows as the A operand of S^T (key row 32kb + l32,
+  // chunk 2t + half); V^T as the A operand of O^T through the transpose read
+  // (keys 16t + trow and 16t + 8 + trow, features 32f + 16(g16&1) + ...)
+  int ka_off[2][NT];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * kThreads;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      kreg[u] = make_uint4(0, 0, 0, 0);
-      if (jb + row < N) kreg[u] = *(const uint4*)(K + (size_t)(jb + row) * D + col);
-    }
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int c = tid + u * kThreads;
-      const int pr = c % (BN / 2), col = (c / (BN / 2)) * 8;
-      const int key = jb + 2 * pr;
-      vreg0[u] = make_uint4(0, 0, 0, 0);
-      vreg1[u] = make_uint4(0, 0, 0, 0);
-      if (key < N) vreg0[u] = *(const uint4*)(V + (size_t)key * D + col);
-      if (key + 1 < N) vreg1[u] = *(const uint4*)(V + (size_t)(key + 1) * D + col);
-    }
-  };
-  // K row-major; V feature-major: a thread holds two consecutive keys x 8
-  // features and writes 8 dwords (one key pair per feature)
-  auto stage = [&]() {
+    for (int t = 0; t < NT; ++t) ka_off[kb][t] = qidx<D>(32 * kb + l32, 16 * t + 8 * half);
+  const int trow = 4 * (g16 >> 1) + (r16 >> 2);
+  int ta_off[FB];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int c = tid + u * kThreads;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(uint4*)(&Ks[row * KSTR + col]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int c = tid + u * kThreads;
-      const int pr = c % (BN / 2), col = (c / (BN / 2)) * 8;
-      const uint32_t w0[4] = {vreg0[u].x, vreg0[u].y, vreg0[u].z, vreg0[u].w};
-      const uint32_t w1[4] = {vreg1[u].x, vreg1[u].y, vreg1[u].z, vreg1[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // features col+2e (low halves) and col+2e+1 (high halves)
-        *(uint32_t*)(&Vt[(col + 2 * e) * VSTR + 2 * pr]) = (w0[e] & 0xffffu) | (w1[e] << 16);
-        *(uint32_t*)(&Vt[(col + 2 * e + 1) * VSTR + 2 * pr]) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-      }
-    }
-  };
+  for (int f = 0; f < FB; ++f) ta_off[f] = qidx<D>(trow, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
 
-  fetch(0);
+  dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
+  dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   for (int j0 = 0; j0 < kend; j0 += BN) {
-    __syncthreads();  // the previous step's readers are done with the tiles
-    stage();
+    const int cur = (j0 / BN) & 1;
+    // tile j0 is complete; every wave is done with the previous tile
     __syncthreads();
-    if (j0 + BN < kend) fetch(j0 + BN);
+    const bool more = j0 + BN < kend;
+    if (more) {
+      dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, Ks[cur ^ 1]);
+      dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, Vs[cur ^ 1]);
+    }
+    const uint16_t* ks = Ks[cur];
+    const uint16_t* vs = Vs[cur];
 
     // a wave whose rows all lie above this block's first key has nothing here
-    if (!wave_live || (CAUSAL && j0 > q0 + 31)) continue;
+    if (!wave_live || (CAUSAL && j0 > q0 + 31)) {
+      if (more) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      continue;
+    }
 
     // ---- S^T = K Q^T for the 64 keys: two 32-key blocks
     f32x16 s[2];
@@ -172,8 +148,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const bf16x8 kf =
-            *(const bf16x8*)(&Ks[(32 * kb + l32) * KSTR + 16 * t + 8 * half]);
+        const bf16x8 kf = *(const bf16x8*)(&ks[ka_off[kb][t]]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
       }
     }
@@ -248,12 +223,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
-      const uint16_t* vrow = &Vt[(32 * f + l32) * VSTR];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint2 lo = *(const uint2*)(vrow + 16 * t + 4 * half);
-        const uint2 hi = *(const uint2*)(vrow + 16 * t + 8 + 4 * half);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        // A = V^T: feature 32f + l32, keys 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
+        const int o = ta_off[f] + 16 * t * D;
+        const bf16x8 vf = frag2(lds_read_tr(vs + o), lds_read_tr(vs + o + 8 * D));
         oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[f], 0, 0, 0);
       }
     }
@@ -266,6 +240,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[f][i] = bf16_round(oacc[f][i]);
     }
+    // the copies must land before the next barrier publishes the tile
+    if (more) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
   if (!wave_live) return;
