@@ -97,16 +97,15 @@ def main():
     n_rep = max(20, args.steps)
     ms_fwd = timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw), n_rep, 3)
     delta = bout["delta"]
-    ms_pre = timed(lambda: fa.attn_bwd_preprocess(p, fout["o"], do, delta), n_rep, 3)
     ms_dkdv = timed(lambda: fa.attn_bwd_dkdv(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
                                              bout["dk"], bout["dv"]), n_rep, 3)
-    ms_dq = timed(lambda: fa.attn_bwd_dq(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
-                                         bout["dq"]), n_rep, 3)
+    ms_dq = timed(lambda: fa.attn_bwd_dq(p, q, k, v, fout["o"], do, fout["row_m"], fout["row_l"],
+                                         bout["dq"], delta), n_rep, 3)
     other = "none" if args.guard != "none" else "beta"
     fo2 = {}
     ms_fwd_other = timed(lambda: fa.attn_fwd(q, k, v, causal=wl.causal, guard=other, out=fo2), n_rep, 3)
-    print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_pre {ms_pre:.4f}, bwd_dkdv {ms_dkdv:.4f}, "
-          f"bwd_dq {ms_dq:.4f}; fwd with guard={other}: {ms_fwd_other:.4f}", file=sys.stderr, flush=True)
+    print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_dq {ms_dq:.4f}, bwd_dkdv {ms_dkdv:.4f}; "
+          f"fwd with guard={other}: {ms_fwd_other:.4f}", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
@@ -154,9 +153,9 @@ def main():
         },
         "pct_of_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "fwd_tflops": round(fl_fwd / (ms_fwd * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(fl_bwd / ((ms_pre + ms_dkdv + ms_dq) * 1e-3) / 1e12, 2),
-        "kernel_ms": {"attn_fwd": round(ms_fwd, 5), "bwd_pre": round(ms_pre, 5),
-                      "bwd_dkdv": round(ms_dkdv, 5), "bwd_dq": round(ms_dq, 5)},
+        "bwd_tflops": round(fl_bwd / ((ms_dkdv + ms_dq) * 1e-3) / 1e12, 2),
+        "kernel_ms": {"attn_fwd": round(ms_fwd, 5), "bwd_dq": round(ms_dq, 5),
+                      "bwd_dkdv": round(ms_dkdv, 5)},
         "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
         "roofline": {
             "kernel": dom,

@@ -6,7 +6,7 @@ used only to own device memory and to name the current HIP stream.  There is
 no fallback: if the library is missing or fails to load, every call raises.
 
 The functions carry the C ABI's names: attn_fwd, attn_bwd (and its stages
-attn_bwd_preprocess / attn_bwd_dkdv / attn_bwd_dq), attn_schedule,
+attn_bwd_dq / attn_bwd_dkdv), attn_schedule,
 attn_strerror, attn_abi_version.
 """
 from __future__ import annotations
@@ -61,11 +61,9 @@ def lib():
         L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p]
         L.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, vp]
         L.attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        for n in ("attn_schedule", "attn_fwd", "attn_bwd", "attn_bwd_preprocess",
-                  "attn_bwd_dkdv", "attn_bwd_dq"):
+        L.attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        for n in ("attn_schedule", "attn_fwd", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,21 +170,16 @@ def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=
     return res
 
 
-def attn_bwd_preprocess(p: Params, o, dout, delta, stream=None):
-    _call("attn_bwd_preprocess", lib().attn_bwd_preprocess(
-        ctypes.byref(p), _ptr(o), _ptr(dout), _ptr(delta), _stream(stream)))
-
-
 def attn_bwd_dkdv(p: Params, q, k, v, dout, row_m, row_l, delta, dk, dv, stream=None):
     _call("attn_bwd_dkdv", lib().attn_bwd_dkdv(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(row_m), _ptr(row_l),
         _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
-def attn_bwd_dq(p: Params, q, k, v, dout, row_m, row_l, delta, dq, stream=None):
+def attn_bwd_dq(p: Params, q, k, v, o, dout, row_m, row_l, dq, delta, stream=None):
     _call("attn_bwd_dq", lib().attn_bwd_dq(
-        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(row_m), _ptr(row_l),
-        _ptr(delta), _ptr(dq), _stream(stream)))
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
+        _ptr(dq), _ptr(delta), _stream(stream)))
 
 
 def default_scale(head_dim: int) -> float:

@@ -138,17 +138,6 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
                                      (hipStream_t)stream));
 }
 
-int attn_bwd_preprocess(const attn_params* p, const void* o, const void* dout, float* delta,
-                        void* stream) {
-  const int rc = check_params(p);
-  if (rc) return rc;
-  if (!o || !dout || !delta) return ATTN_E_NULL;
-  if (!aligned16(o) || !aligned16(dout)) return ATTN_E_UNSUPPORTED;
-  const attn::BwdArgs a =
-      bwd_args(p, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, nullptr, delta);
-  return hip_status(attn::launch_bwd_pre(a, p->head_dim, (hipStream_t)stream));
-}
-
 int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void* v,
                   const void* dout, const float* row_m, const float* row_l, const float* delta,
                   void* dk, void* dv, void* stream) {
@@ -164,16 +153,16 @@ int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void
                                           (hipStream_t)stream));
 }
 
-int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v,
-                const void* dout, const float* row_m, const float* row_l, const float* delta,
-                void* dq, void* stream) {
+int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                const void* dout, const float* row_m, const float* row_l, void* dq, float* delta,
+                void* stream) {
   const int rc = check_params(p);
   if (rc) return rc;
-  if (!q || !k || !v || !dout || !row_m || !row_l || !delta || !dq) return ATTN_E_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq))
+  if (!q || !k || !v || !o || !dout || !row_m || !row_l || !dq || !delta) return ATTN_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq))
     return ATTN_E_UNSUPPORTED;
-  const attn::BwdArgs a = bwd_args(p, q, k, v, nullptr, dout, row_m, row_l, dq, nullptr, nullptr,
-                                   const_cast<float*>(delta));
+  const attn::BwdArgs a = bwd_args(p, q, k, v, o, dout, row_m, row_l, dq, nullptr, nullptr, delta);
   return hip_status(attn::launch_bwd_dq(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
                                         (hipStream_t)stream));
 }
@@ -188,11 +177,9 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_E_UNSUPPORTED;
-  rc = attn_bwd_preprocess(p, o, dout, delta, stream);
+  rc = attn_bwd_dq(p, q, k, v, o, dout, row_m, row_l, dq, delta, stream);
   if (rc) return rc;
-  rc = attn_bwd_dkdv(p, q, k, v, dout, row_m, row_l, delta, dk, dv, stream);
-  if (rc) return rc;
-  return attn_bwd_dq(p, q, k, v, dout, row_m, row_l, delta, dq, stream);
+  return attn_bwd_dkdv(p, q, k, v, dout, row_m, row_l, delta, dk, dv, stream);
 }
 
 }  // extern "C"

@@ -11,7 +11,6 @@
 // softmax is unchanged by the shift ([R] the fix, paper §4).
 //
 // Mapping to CDNA4 (not from the pages):
-//   * bwd_pre: one pass over O and dO for delta;
 //   * bwd_dkdv: one workgroup = 4 wave64s = 128 keys of one (batch, KV
 //     head); a wave owns 32 keys and accumulates their dK and dV over every
 //     query row (and every query head of the group) in registers.  Per step
@@ -21,8 +20,10 @@
 //     A-operand layout of dV += P^T dO and dK += dS^T Q, whose B operands
 //     (dO and Q, contraction over rows) come from the row-major stages
 //     through the gfx950 LDS transpose read;
-//   * bwd_dq: one workgroup = 128 query rows, a wave owns 32 of them
-//     (lane = row) and streams the keys in blocks of 64 like the forward:
+//   * bwd_dq (runs first): one workgroup = 128 query rows, a wave owns 32 of
+//     them (lane = row); it forms delta for its rows from their O and dO
+//     (and writes it for bwd_dkdv), then streams the keys in blocks of 64
+//     like the forward:
 //     S^T = K Q^T and dP^T = V dO^T, then dS^T in registers is the B
 //     operand of dQ^T += K^T dS^T, K^T read from the row-major K tile
 //     through the transpose read.  dQ is finished in registers: no atomics
@@ -45,40 +46,6 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // gives.
 __device__ __forceinline__ float row_lse2(float m, float l) {
   return l > 0.0f ? __builtin_fmaf(m, kLog2e, __builtin_log2f(l)) : __builtin_nanf("");
-}
-
-// ---------------------------------------------------------------- bwd_pre
-// delta = rowsum(dO∘O): 8 threads per row (16 bytes each), 32 rows per workgroup.
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int TPR = 8;            // threads per row
-  constexpr int EPT = D / TPR;      // elements per thread (8 or 16)
-  const int tid = threadIdx.x;
-  const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const size_t row = (size_t)blockIdx.x * (kThreads / TPR) + tid / TPR;
-  const int part = tid % TPR;
-  float acc = 0.0f;
-  if (row < rows) {
-    const uint16_t* o = a.o + row * D + part * EPT;
-    const uint16_t* g = a.dout + row * D + part * EPT;
-#pragma unroll
-    for (int c = 0; c < EPT; c += 8) {
-      const uint4 ov = *(const uint4*)(o + c);
-      const uint4 gv = *(const uint4*)(g + c);
-      const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = __builtin_fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), acc);
-        acc = __builtin_fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
-      }
-    }
-  }
-  // reduce over the 8 threads of the row (consecutive lanes)
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  if (row < rows && part == 0) a.delta[row] = acc;
 }
 
 // ---------------------------------------------------------------- bwd_dkdv
@@ -447,11 +414,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     qf[t] = __builtin_bit_cast(bf16x8, qr);
     gf[t] = __builtin_bit_cast(bf16x8, gr);
   }
+  // delta = rowsum(dO∘O) of this lane's row: its 32 features here, the
+  // other 32 (d = 64) in lane ^ 32 (every lane returns the full sum)
   float lse2 = 0.0f, del = 0.0f;
-  if (qrow < N) {
-    const size_t ridx = (size_t)(b * a.Hq + hq) * N + qrow;
-    lse2 = row_lse2(a.row_m[ridx], a.row_l[ridx]);
-    del = a.delta[ridx];
+  {
+    float part = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint4 orow = make_uint4(0, 0, 0, 0);
+      if (qrow < N) orow = *(const uint4*)(a.o + qoff + (size_t)qrow * D + 16 * t + 8 * half);
+      const uint4 grow = __builtin_bit_cast(uint4, gf[t]);
+      const uint32_t ow[4] = {orow.x, orow.y, orow.z, orow.w};
+      const uint32_t gw[4] = {grow.x, grow.y, grow.z, grow.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = __builtin_fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), part);
+        part = __builtin_fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), part);
+      }
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    del = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (qrow < N) {
+      const size_t ridx = (size_t)(b * a.Hq + hq) * N + qrow;
+      lse2 = row_lse2(a.row_m[ridx], a.row_l[ridx]);
+      if (half == 0) a.delta[ridx] = del;
+    }
   }
 
   f32x16 dq[FB];
@@ -504,16 +491,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s) {
-  const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const dim3 grid((unsigned)((rows + 31) / 32));
-  if (d == 64)
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s) {
   const dim3 grid((unsigned)(((a.N + kDkdvKeys - 1) / kDkdvKeys) * a.Hkv * a.B));

@@ -79,7 +79,6 @@ __device__ __forceinline__ void xcd_map(int L, int heads, int& head, int& blk) {
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
                       hipStream_t s);
-hipError_t launch_bwd_pre(const BwdArgs& a, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, hipStream_t s);
 

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -100,7 +100,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
              void* obar_out, float* row_max, void* stream);
 
 /*
- * attn_bwd -- backward of attn_fwd, the three stages below in order.
+ * attn_bwd -- backward of attn_fwd: attn_bwd_dq then attn_bwd_dkdv.
  * Defines: [R] "Core idea", equations (paper Eq. 1-2: dS = alpha P∘(dP -
  * delta), dQ = dS K, delta = rowsum(dO∘O)) and the summary/method sections
  * (delta computed from the bf16 O, paper §3.2).  The guard is carried by
@@ -117,23 +117,22 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
              const void* o, const void* dout, const float* row_m, const float* row_l,
              void* dq, void* dk, void* dv, float* delta, void* stream);
 
-/* attn_bwd's stages, callable one by one (same arguments and rules); the
- * last two only read delta and are independent of each other:
- *   attn_bwd_preprocess: delta = rowsum(dO∘O) in fp32 from the bf16 O
- *     ([R] "Core idea"/method: the delta term, paper §3.2).
- *   attn_bwd_dkdv: per key, over every query row that sees it, recompute S
- *     and P, dP = dO V^T, dS = P∘(dP - delta); dV = P^T dO and dK =
- *     alpha dS^T Q ([R] "Core idea", Eq. 1-2).
- *   attn_bwd_dq: per query row, over every key it sees, the same S, P, dP
- *     and dS; dQ = alpha dS K ([R] "Core idea", Eq. 1-2).                  */
-int attn_bwd_preprocess(const attn_params* p, const void* o, const void* dout,
-                        float* delta, void* stream);
+/* attn_bwd's stages, callable one by one (same arguments and rules), in
+ * this order:
+ *   attn_bwd_dq: per query row, delta = rowsum(dO∘O) in fp32 from the bf16
+ *     O ([R] "Core idea"/method: the delta term, paper §3.2), written to
+ *     delta; then over every key the row sees, S, P = exp(t - row_m)/row_l,
+ *     dP = dO V^T, dS = P∘(dP - delta) and dQ = alpha dS K ([R] "Core
+ *     idea", Eq. 1-2).
+ *   attn_bwd_dkdv: per key, over every query row that sees it, the same S,
+ *     P, dP and dS from delta (as written by attn_bwd_dq); dV = P^T dO and
+ *     dK = alpha dS^T Q ([R] "Core idea", Eq. 1-2).                        */
+int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v,
+                const void* o, const void* dout, const float* row_m, const float* row_l,
+                void* dq, float* delta, void* stream);
 int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void* v,
                   const void* dout, const float* row_m, const float* row_l,
                   const float* delta, void* dk, void* dv, void* stream);
-int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v,
-                const void* dout, const float* row_m, const float* row_l,
-                const float* delta, void* dq, void* stream);
 
 /*
  * attn_schedule -- the rounding schedule attn_fwd uses for these params, so

@@ -29,14 +29,13 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_functions()
-    assert {"attn_fwd", "attn_bwd", "attn_schedule", "attn_bwd_preprocess", "attn_bwd_dkdv",
-            "attn_bwd_dq"} <= set(names)
+    assert {"attn_fwd", "attn_bwd", "attn_schedule", "attn_bwd_dkdv", "attn_bwd_dq"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 2
+    assert fa.attn_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -105,11 +104,11 @@ def test_backward_argument_errors(L):
     args = [vp(FAKE)] * 11
     assert L.attn_bwd(ctypes.byref(p), *[None] + args[1:], None) == -1          # q missing
     assert L.attn_bwd(ctypes.byref(p), *[vp(FAKE + 2)] + args[1:], None) == -3  # misaligned
-    assert L.attn_bwd_preprocess(ctypes.byref(p), vp(FAKE), vp(FAKE), None, None) == -1
     assert L.attn_bwd_dkdv(ctypes.byref(p), *[vp(FAKE)] * 8, None, None) == -1  # dv missing
-    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 7, vp(FAKE + 8), None) == -3
+    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 8, None, None) == -1  # delta missing
+    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 7, vp(FAKE + 8), vp(FAKE), None) == -3
     bad = fa.make_params(1, 3, 2, 10, 64)
-    assert L.attn_bwd_dq(ctypes.byref(bad), *[vp(FAKE)] * 8, None) == -2
+    assert L.attn_bwd_dq(ctypes.byref(bad), *[vp(FAKE)] * 9, None) == -2
     huge = fa.make_params(1, 1, 1, 1 << 24, 64)  # one head past a 32-bit byte range
     assert L.attn_bwd_dkdv(ctypes.byref(huge), *[vp(FAKE)] * 9, None) == -2
 

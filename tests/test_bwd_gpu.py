@@ -185,8 +185,7 @@ def test_stages_equal_fused_and_deterministic():
     p = fa.make_params(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim, causal=True)
     delta = torch.empty_like(b1["delta"])
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa.attn_bwd_preprocess(p, f["o"], do, delta)
-    fa.attn_bwd_dq(p, q, k, v, do, f["row_m"], f["row_l"], delta, dq)  # independent of dkdv
+    fa.attn_bwd_dq(p, q, k, v, f["o"], do, f["row_m"], f["row_l"], dq, delta)
     fa.attn_bwd_dkdv(p, q, k, v, do, f["row_m"], f["row_l"], delta, dk, dv)
     torch.cuda.synchronize()
     # every output element is written once by one workgroup: bitwise equal
