@@ -98,7 +98,7 @@ __device__ __forceinline__ void bwd_stats_store(const float (&stat)[3], int q0, 
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_step(
     const BwdArgs& a, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const int (&qa_off)[D / kMfmaK],
-    const int (&ka_off)[D / kMfmaK], const int (&tb_off)[D / 32], const uint16_t* __restrict__ qs,
+    const int (&ka_off)[D / kMfmaK], const int (&tb_off)[D / 32][2], const uint16_t* __restrict__ qs,
     const uint16_t* __restrict__ gs, const uint16_t* __restrict__ ks,
     const uint16_t* __restrict__ vs, const float* __restrict__ slse,
     const float* __restrict__ sdel, uint16_t* __restrict__ qs_next,
@@ -178,10 +178,11 @@ __device__ __forceinline__ void dkdv_step(
     for (int f = 0; f < FB; ++f) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int o = tb_off[f] + 16 * t * D;  // rows 16t + trow (row & 7 unchanged)
-        const bf16x8 gb = frag2(lds_read_tr(gs + o), lds_read_tr(gs + o + 8 * D));
+        // rows 16t + trow and 16t + 8 + trow (the swizzle ignores bit 4 and up)
+        const int o0 = tb_off[f][0] + 16 * t * D, o1 = tb_off[f][1] + 16 * t * D;
+        const bf16x8 gb = frag2(lds_read_tr(gs + o0), lds_read_tr(gs + o1));
         dv[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], gb, dv[f], 0, 0, 0);
-        const bf16x8 qb = frag2(lds_read_tr(qs + o), lds_read_tr(qs + o + 8 * D));
+        const bf16x8 qb = frag2(lds_read_tr(qs + o0), lds_read_tr(qs + o1));
         dk[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], qb, dk[f], 0, 0, 0);
       }
     }
@@ -241,9 +242,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void bwd_dkdv_kernel(Bwd
     ka_off[t] = qidx<D>(32 * wave + l32, 16 * t + 8 * half);
   }
   const int trow = 4 * (g16 >> 1) + (r16 >> 2);  // transpose reads: row within 16
-  int tb_off[FB];  // B operand of dV/dK, product t = 0; t = 1 is 16 rows on
+  int tb_off[FB][2];  // B operand of dV/dK, product t = 0 (rows trow, trow + 8)
 #pragma unroll
-  for (int f = 0; f < FB; ++f) tb_off[f] = qidx<D>(trow, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      tb_off[f][e] = qidx<D>(trow + 8 * e, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
 
   // Steps: every 32-row slice of every query head of the group, from the
   // first row that can see these keys.
@@ -303,7 +307,7 @@ constexpr int kDqKeys = 64;   // keys per streaming step
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_step(
     const BwdArgs& a, f32x16 (&dq)[D / 32], const bf16x8 (&qf)[D / kMfmaK],
-    const bf16x8 (&gf)[D / kMfmaK], const int (&ka_off)[2][D / kMfmaK], const int (&ta_off)[D / 32],
+    const bf16x8 (&gf)[D / kMfmaK], const int (&ka_off)[2][D / kMfmaK], const int (&ta_off)[D / 32][2],
     const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs,
     uint16_t* __restrict__ ks_next, uint16_t* __restrict__ vs_next, i32x4 rk,
     i32x4 rv, bool more, int j0, int wave, int lane, bool wave_live, int q0,
@@ -368,8 +372,9 @@ __device__ __forceinline__ void dq_step(
     for (int f = 0; f < FB; ++f) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int o = ta_off[f] + 16 * t * D;  // keys 16t + trow (key & 7 unchanged)
-        const bf16x8 kt = frag2(lds_read_tr(ks + o), lds_read_tr(ks + o + 8 * D));
+        // keys 16t + trow and 16t + 8 + trow (the swizzle ignores bit 4 and up)
+        const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
+        const bf16x8 kt = frag2(lds_read_tr(ks + o0), lds_read_tr(ks + o1));
         dq[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, sb[t], dq[f], 0, 0, 0);
       }
     }
@@ -453,9 +458,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) ka_off[kb][t] = qidx<D>(32 * kb + l32, 16 * t + 8 * half);
   const int trow = 4 * (g16 >> 1) + (r16 >> 2);  // transpose reads: key within 16
-  int ta_off[FB];  // A operand of dQ^T (K^T), product t = 0; t is 16 keys on
+  int ta_off[FB][2];  // A operand of dQ^T (K^T), product t = 0 (keys trow, trow + 8)
 #pragma unroll
-  for (int f = 0; f < FB; ++f) ta_off[f] = qidx<D>(trow, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      ta_off[f][e] = qidx<D>(trow + 8 * e, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
 
   const int kend = CAUSAL ? min(N, (mb + 1) * kDqRows) : N;
   const bool wave_live = q0 < N;

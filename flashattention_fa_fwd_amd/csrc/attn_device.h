@@ -36,13 +36,20 @@ __device__ __forceinline__ bf16x8 frag2(uint2 lo, uint2 hi) {
 }
 
 // LDS tiles of D-wide bf16 rows: the 16-byte chunk c of row r is stored at
-// chunk c ^ qswz(r).  Eight consecutive rows reading one chunk (row-operand
-// reads) and four consecutive rows reading two adjacent chunks (transpose
-// reads) then hit 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int qswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// chunk c ^ qswz(r).  The gfx950 LDS has 64 four-byte banks; a 16-byte-per-
+// lane read is served 16 lanes at a time and a transpose read 32 at a time.
+// The permutation (row bits 1..3, and bit 0 for 256-byte rows) makes both
+// patterns the kernels use hit 16 distinct 16-byte bank groups: 16
+// consecutive rows reading one chunk (row operands) and 4 consecutive rows
+// reading 4 adjacent chunks (transpose reads).
+template <int D>
+__device__ __forceinline__ int qswz(int r) {
+  const int s = (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return D == 64 ? s : (s | ((r & 1) << 3));
+}
 template <int D>
 __device__ __forceinline__ int qidx(int r, int col) {  // col % 4 == 0
-  return r * D + ((((col >> 3) ^ qswz(r))) << 3) + (col & 7);
+  return r * D + ((((col >> 3) ^ qswz<D>(r))) << 3) + (col & 7);
 }
 
 // Buffer resource (gfx9 layout) of one head's rows: n*d bf16 from base;
@@ -89,7 +96,7 @@ __device__ __forceinline__ void dma_tile(i32x4 desc, int r0, int w, int lane, ui
     const int piece = w * (PIECES / NW) + u;
     const int p = piece * 64 + lane;          // chunk position in the tile
     const int row = p / CPR;
-    const int c = (p % CPR) ^ qswz(row);      // logical chunk stored there
+    const int c = (p % CPR) ^ qswz<D>(row);   // logical chunk stored there
     const int voff = ((r0 + row) * D + 8 * c) * 2;
     lds_dma16(desc, __builtin_amdgcn_readfirstlane(lds_addr(tile + piece * 512)), voff);
   }

@@ -115,9 +115,12 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) ka_off[kb][t] = qidx<D>(32 * kb + l32, 16 * t + 8 * half);
   const int trow = 4 * (g16 >> 1) + (r16 >> 2);
-  int ta_off[FB];
+  int ta_off[FB][2];
 #pragma unroll
-  for (int f = 0; f < FB; ++f) ta_off[f] = qidx<D>(trow, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      ta_off[f][e] = qidx<D>(trow + 8 * e, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
 
   dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
   dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
@@ -226,8 +229,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         // A = V^T: feature 32f + l32, keys 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
-        const int o = ta_off[f] + 16 * t * D;
-        const bf16x8 vf = frag2(lds_read_tr(vs + o), lds_read_tr(vs + o + 8 * D));
+        const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
+        const bf16x8 vf = frag2(lds_read_tr(vs + o0), lds_read_tr(vs + o1));
         oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[f], 0, 0, 0);
       }
     }
