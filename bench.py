@@ -24,6 +24,40 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0
 
+# HBM traffic of a kernel per launch, from two rocprofv3 --pmc passes over
+# `bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration`
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+# counter reads for a plain device copy of 256 MiB (FETCH_SIZE reads half the
+# bytes: x2.0; WRITE_SIZE all of them: x1.0).  Summary and commands:
+# profiles/bwd_dkdv_gpt2s_hbm_traffic.md.  The figures hold only for the
+# kernel sources they were taken on (SHA-256 over csrc/); otherwise the
+# report says null.
+MEASURED_TRAFFIC = {
+    "bwd_dkdv": {
+        "sources_sha256": "b32212824f6a7dd85f23bff89d33c4b2db2febbb2d6f77bbd3cbc04087df35b8",
+        "fetch_kib": 64250.0, "write_kib": 51670.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+}
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "flashattention_fa_fwd_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    m = MEASURED_TRAFFIC.get(kernel)
+    if m is None or m["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return int(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -93,14 +127,23 @@ def main():
     ms_step = timed(step, args.steps, args.warmup)
     print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations (HIP events on the launch stream)
-    n_rep = max(20, args.steps)
-    ms_fwd = timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw), n_rep, 3)
+    # ---- per-kernel durations: the same steps again, with HIP events on the
+    # launch stream between the kernels (attn_bwd is its two stages: dQ, dK/dV)
     delta = bout["delta"]
-    ms_dkdv = timed(lambda: fa.attn_bwd_dkdv(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
-                                             bout["dk"], bout["dv"]), n_rep, 3)
-    ms_dq = timed(lambda: fa.attn_bwd_dq(p, q, k, v, fout["o"], do, fout["row_m"], fout["row_l"],
-                                         bout["dq"], delta), n_rep, 3)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
+        e[1].record(stream)
+        fa.attn_bwd_dq(p, q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], bout["dq"], delta)
+        e[2].record(stream)
+        fa.attn_bwd_dkdv(p, q, k, v, do, fout["row_m"], fout["row_l"], delta, bout["dk"], bout["dv"])
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    ms_fwd, ms_dq, ms_dkdv = (sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j in range(3))
+    n_rep = max(20, args.steps)
     other = "none" if args.guard != "none" else "beta"
     fo2 = {}
     ms_fwd_other = timed(lambda: fa.attn_fwd(q, k, v, causal=wl.causal, guard=other, out=fo2), n_rep, 3)
@@ -164,7 +207,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom),  # HBM bytes per launch
         },
     }
 
