@@ -2,7 +2,7 @@
 
 Compiles every translation unit under csrc/ in one hipcc invocation into a
 shared library next to this file.  Packed-fp32 instructions are disabled
-(-packed-fp32-ops); floating-point atomics use the hardware instruction.
+(-packed-fp32-ops).
 """
 import os
 import subprocess
@@ -19,7 +19,6 @@ def hipcc_cmd(out: str) -> list:
     return [
         "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-munsafe-fp-atomics",
         # keep matrix-instruction accumulators in ordinary VGPRs: the softmax
         # and rescale work on them every step, and AGPRs would need copies
         "-mllvm", "-amdgpu-mfma-vgpr-form",
