@@ -53,7 +53,7 @@ __device__ __forceinline__ void top2_merge(float& a, float& a2, float b, float b
 }
 
 template <int D, bool CAUSAL, int GUARD, bool OBAR_F32>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs a) {
   constexpr int BN = kFwdBlockN;
   constexpr int NT = D / kMfmaK; // matrix steps along d for S
   constexpr int FB = D / 32;     // 32-feature blocks of O^T
@@ -122,12 +122,22 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     for (int e = 0; e < 2; ++e)
       ta_off[f][e] = qidx<D>(trow + 8 * e, 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3));
 
+  // Steps this wave computes: under the causal mask a wave's rows see no key
+  // at or past q0 + 32.  Every wave still takes part in the copies and
+  // barriers of the workgroup's remaining steps (second loop below); keeping
+  // those in a loop of their own lets the accumulators stay in one register
+  // set across the computing steps.
+  const int jc = !wave_live ? 0 : (CAUSAL ? min(kend, q0 + 32) : kend);
+
   dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
   dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  for (int j0 = 0; j0 < kend; j0 += BN) {
+  int j0 = 0;
+  for (; j0 < jc; j0 += BN) {
     const int cur = (j0 / BN) & 1;
-    // tile j0 is complete; every wave is done with the previous tile
+    // this wave's copies of tile j0 have landed (a no-op when none are in
+    // flight); after the barrier the whole tile is, and every wave is done
+    // with the previous tile
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     const bool more = j0 + BN < kend;
     if (more) {
@@ -136,12 +146,6 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     }
     const uint16_t* ks = Ks[cur];
     const uint16_t* vs = Vs[cur];
-
-    // a wave whose rows all lie above this block's first key has nothing here
-    if (!wave_live || (CAUSAL && j0 > q0 + 31)) {
-      if (more) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      continue;
-    }
 
     // ---- S^T = K Q^T for the 64 keys: two 32-key blocks
     f32x16 s[2];
@@ -198,11 +202,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     if (GUARD == kGuardBeta && tie) mn = (rt > 0.0f) ? a.beta * rt : 0.0f;
     if (GUARD == kGuardEps && tie) mn = rt + a.shift_eps;
 
-    // ---- rescale by c = exp(m_old - m_new) where the shift moved
-    if (j0 == 0) {
-      m = mn;
-    } else if (__any(mn != m)) {
-      const float c = (mn != m) ? __builtin_amdgcn_exp2f((m - mn) * kLog2e) : 1.0f;
+    // ---- rescale by c = exp(m_old - m_new); c = 1 exactly where the shift
+    // did not move (and on the first step), so multiplying unconditionally
+    // changes nothing there and keeps the accumulator in one register set
+    {
+      const float c = (j0 == 0 || mn == m) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
       lsum *= c;
 #pragma unroll
       for (int f = 0; f < FB; ++f)
@@ -243,9 +247,18 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[f][i] = bf16_round(oacc[f][i]);
     }
-    // the copies must land before the next barrier publishes the tile
-    if (more) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
+  for (; j0 < kend; j0 += BN) {
+    const int cur = (j0 / BN) & 1;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (j0 + BN < kend) {
+      dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, Ks[cur ^ 1]);
+      dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, Vs[cur ^ 1]);
+    }
+  }
+  // no copy may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   if (!wave_live) return;
   // ---- epilogue: O = bf16(Ō / ℓ); row outputs
