@@ -147,8 +147,14 @@ def main():
     other = "none" if args.guard != "none" else "beta"
     fo2 = {}
     ms_fwd_other = timed(lambda: fa.attn_fwd(q, k, v, causal=wl.causal, guard=other, out=fo2), n_rep, 3)
+    # the backward with delta = rowsum(dP∘P) (a first sweep over the keys in
+    # the dQ kernel instead of rowsum(dO∘O)): its cost next to the default
+    bo2 = {}
+    ms_bwd_dp = timed(lambda: fa.attn_bwd(q, k, v, None, do, fout["row_m"], fout["row_l"],
+                                          delta="dp_p", out=bo2, **kw), n_rep, 3)
     print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_dq {ms_dq:.4f}, bwd_dkdv {ms_dkdv:.4f}; "
-          f"fwd with guard={other}: {ms_fwd_other:.4f}", file=sys.stderr, flush=True)
+          f"fwd with guard={other}: {ms_fwd_other:.4f}; bwd with delta=rowsum(dP*P): "
+          f"{ms_bwd_dp:.4f}", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
@@ -200,6 +206,7 @@ def main():
         "kernel_ms": {"attn_fwd": round(ms_fwd, 5), "bwd_dq": round(ms_dq, 5),
                       "bwd_dkdv": round(ms_dkdv, 5)},
         "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
+        "bwd_ms_delta": {"rowsum(dO*O)": round(ms_dq + ms_dkdv, 5), "rowsum(dP*P)": round(ms_bwd_dp, 5)},
         "roofline": {
             "kernel": dom,
             "bound": "mfma",

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 CAUSAL = 0x1
 GUARD_NONE, GUARD_BETA, GUARD_EPS = 0x0, 0x2, 0x4
 OBAR_FP32 = 0x8
+DELTA_DP = 0x10
 ROW_TIE, ROW_ZERO_DENOM, ROW_GUARD_APPLIED = 0x1, 0x2, 0x4
 _GUARDS = {"none": GUARD_NONE, "beta": GUARD_BETA, "eps": GUARD_EPS}
 
@@ -79,8 +80,12 @@ def attn_strerror(code: int) -> str:
 
 def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guard="beta",
                 beta=2.0, tie_eps=1e-3, shift_eps=2.0 ** -5, obar_fp32=False,
-                softmax_scale=None) -> Params:
+                softmax_scale=None, delta="do_o") -> Params:
+    """delta: "do_o" (rowsum(dO∘O), the default) or "dp_p" (rowsum(dP∘P))."""
+    if delta not in ("do_o", "dp_p"):
+        raise ValueError(f"delta must be 'do_o' or 'dp_p', not {delta!r}")
     flags = (CAUSAL if causal else 0) | _GUARDS[guard] | (OBAR_FP32 if obar_fp32 else 0)
+    flags |= DELTA_DP if delta == "dp_p" else 0
     return Params(batch, heads_q, heads_kv, seqlen, head_dim,
                   0.0 if softmax_scale is None else float(softmax_scale),
                   float(beta), float(tie_eps), float(shift_eps), flags)
@@ -151,13 +156,17 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
 
 
 def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=2.0,
-             tie_eps=1e-3, shift_eps=2.0 ** -5, softmax_scale=None, out=None, stream=None):
-    """Backward.  Returns a dict: dq, dk, dv (bf16) and delta (fp32)."""
+             tie_eps=1e-3, shift_eps=2.0 ** -5, softmax_scale=None, delta="do_o", out=None,
+             stream=None):
+    """Backward.  Returns a dict: dq, dk, dv (bf16) and delta (fp32).
+    delta="dp_p" forms delta = rowsum(dP∘P) (o is then not read; it may be None)."""
     for n_, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t is None and n_ == "o" and delta == "dp_p":
+            continue
         _check_bf16(n_, t)
     B, Hq, N, d = q.shape
     p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
-                     shift_eps=shift_eps, softmax_scale=softmax_scale)
+                     shift_eps=shift_eps, softmax_scale=softmax_scale, delta=delta)
     res = out if out is not None else {}
     if "dq" not in res:
         res["dq"] = torch.empty_like(q)

@@ -24,7 +24,7 @@ int check_params(const attn_params* p) {
     return ATTN_E_SHAPE;
   if (p->heads_q % p->heads_kv != 0) return ATTN_E_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return ATTN_E_UNSUPPORTED;
-  const uint32_t known = ATTN_CAUSAL | ATTN_GUARD_MASK | ATTN_OBAR_FP32;
+  const uint32_t known = ATTN_CAUSAL | ATTN_GUARD_MASK | ATTN_OBAR_FP32 | ATTN_DELTA_DP;
   if (p->flags & ~known) return ATTN_E_PARAM;
   const uint32_t g = p->flags & ATTN_GUARD_MASK;
   if (g == ATTN_GUARD_MASK) return ATTN_E_PARAM;  // two guards at once
@@ -74,6 +74,9 @@ attn::BwdArgs bwd_args(const attn_params* p, const void* q, const void* k, const
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+// O is read by the backward only for delta = rowsum(dO∘O).
+bool needs_o(const attn_params* p) { return (p->flags & ATTN_DELTA_DP) == 0; }
 
 }  // namespace
 
@@ -158,13 +161,14 @@ int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* 
                 void* stream) {
   const int rc = check_params(p);
   if (rc) return rc;
-  if (!q || !k || !v || !o || !dout || !row_m || !row_l || !dq || !delta) return ATTN_E_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(dq))
+  if (!q || !k || !v || (!o && needs_o(p)) || !dout || !row_m || !row_l || !dq || !delta)
+    return ATTN_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) ||
+      !aligned16(dout) || !aligned16(dq))
     return ATTN_E_UNSUPPORTED;
   const attn::BwdArgs a = bwd_args(p, q, k, v, o, dout, row_m, row_l, dq, nullptr, nullptr, delta);
   return hip_status(attn::launch_bwd_dq(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
-                                        (hipStream_t)stream));
+                                        (p->flags & ATTN_DELTA_DP) != 0, (hipStream_t)stream));
 }
 
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
@@ -172,10 +176,11 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
              void* dv, float* delta, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
-  if (!q || !k || !v || !o || !dout || !row_m || !row_l || !dq || !dk || !dv || !delta)
+  if (!q || !k || !v || (!o && needs_o(p)) || !dout || !row_m || !row_l || !dq || !dk || !dv ||
+      !delta)
     return ATTN_E_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_E_UNSUPPORTED;
   rc = attn_bwd_dq(p, q, k, v, o, dout, row_m, row_l, dq, delta, stream);
   if (rc) return rc;

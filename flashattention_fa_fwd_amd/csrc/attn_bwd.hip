@@ -381,7 +381,68 @@ __device__ __forceinline__ void dq_step(
   }
 }
 
+// One streaming step of the first sweep of the dQ kernel in the
+// delta = rowsum(dP∘P) mode ([R] method, paper §3.2; [S] "Key claims"):
+// S^T and dP^T for the 64 keys as in dq_step, P = exp2(s * alpha*log2(e) -
+// lse2), and acc += P dP over the lane's visible keys (in fp32, in key
+// order; the other half of the row's keys is in lane ^ 32).
 template <int D, bool CAUSAL>
+__device__ __forceinline__ void dq_delta_step(
+    const BwdArgs& a, float& acc, const bf16x8 (&qf)[D / kMfmaK], const bf16x8 (&gf)[D / kMfmaK],
+    const int (&ka_off)[2][D / kMfmaK], const uint16_t* __restrict__ ks,
+    const uint16_t* __restrict__ vs, uint16_t* __restrict__ ks_next,
+    uint16_t* __restrict__ vs_next, i32x4 rk, i32x4 rv, bool more, int j0, int wave, int lane,
+    bool wave_live, int q0, int qrow, int half, float lse2) {
+  constexpr int BN = kDqKeys;
+  constexpr int NT = D / kMfmaK;
+  const int N = a.N;
+  if (more) {
+    dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, ks_next);
+    dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, vs_next);
+  }
+  if (wave_live && !(CAUSAL && j0 > q0 + 31)) {
+    f32x16 sv[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[kb][i] = 0.0f;
+        dp[kb][i] = 0.0f;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 kf = *(const bf16x8*)(&ks[ka_off[kb][t]]);
+        sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sv[kb], 0, 0, 0);
+        const bf16x8 vf = *(const bf16x8*)(&vs[ka_off[kb][t]]);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[t], dp[kb], 0, 0, 0);
+      }
+    }
+    float pv[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pv[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][i], a.c1, -lse2));
+    const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > q0);
+    if (__builtin_expect(edge, 0)) {
+      asm volatile("");
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - j0 - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) pv[kb][i] = 0.0f;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc = __builtin_fmaf(pv[kb][i], dp[kb][i], acc);
+  }
+}
+
+// DELTA_DP: delta = rowsum(dP∘P) from a first sweep over the keys instead
+// of rowsum(dO∘O) from the bf16 O.
+template <int D, bool CAUSAL, bool DELTA_DP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = kDqKeys;
   constexpr int NT = D / kMfmaK;     // 16-wide steps along d
@@ -422,7 +483,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // delta = rowsum(dO∘O) of this lane's row: its 32 features here, the
   // other 32 (d = 64) in lane ^ 32 (every lane returns the full sum)
   float lse2 = 0.0f, del = 0.0f;
-  {
+  if (qrow < N) {
+    const size_t ridx = (size_t)(b * a.Hq + hq) * N + qrow;
+    lse2 = row_lse2(a.row_m[ridx], a.row_l[ridx]);
+  }
+  if constexpr (!DELTA_DP) {
     float part = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -439,11 +504,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
     del = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (qrow < N) {
-      const size_t ridx = (size_t)(b * a.Hq + hq) * N + qrow;
-      lse2 = row_lse2(a.row_m[ridx], a.row_l[ridx]);
-      if (half == 0) a.delta[ridx] = del;
-    }
+    if (qrow < N && half == 0) a.delta[(size_t)(b * a.Hq + hq) * N + qrow] = del;
   }
 
   f32x16 dq[FB];
@@ -467,6 +528,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int kend = CAUSAL ? min(N, (mb + 1) * kDqRows) : N;
   const bool wave_live = q0 < N;
+
+  if constexpr (DELTA_DP) {
+    // first sweep: delta = rowsum(dP∘P) over the keys the row sees
+    dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
+    dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    float acc = 0.0f;
+    for (int j0 = 0; j0 < kend; j0 += BN) {
+      const int cur = (j0 / BN) & 1;
+      __syncthreads();
+      const bool more = j0 + BN < kend;
+      dq_delta_step<D, CAUSAL>(a, acc, qf, gf, ka_off, Ks[cur], Vs[cur], Ks[cur ^ 1], Vs[cur ^ 1],
+                               rk, rv, more, j0, wave, lane, wave_live, q0, qrow, half, lse2);
+      if (more) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+    del = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (qrow < N && half == 0) a.delta[(size_t)(b * a.Hq + hq) * N + qrow] = del;
+    // every wave is done with the last tile before stage 0 is refilled
+    __syncthreads();
+  }
 
   dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
   dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
@@ -516,20 +598,25 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, hipStream_t s) {
+template <bool DELTA_DP>
+hipError_t launch_dq_t(const BwdArgs& a, int d, bool causal, hipStream_t s) {
   const dim3 grid((unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.Hq * a.B));
   if (d == 64) {
     if (causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
   } else {
     if (causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, true, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, false, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, bool delta_dp, hipStream_t s) {
+  return delta_dp ? launch_dq_t<true>(a, d, causal, s) : launch_dq_t<false>(a, d, causal, s);
 }
 
 }  // namespace attn

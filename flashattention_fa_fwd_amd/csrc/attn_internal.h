@@ -80,7 +80,7 @@ __device__ __forceinline__ void xcd_map(int L, int heads, int& head, int& blk) {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
                       hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s);
-hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, bool delta_dp, hipStream_t s);
 
 // Query rows per inner step of the dK/dV kernel.
 constexpr int kBwdBlockM = 32;

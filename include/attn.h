@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -45,6 +45,7 @@ extern "C" {
 #define ATTN_GUARD_EPS 0x4u       /* tie rows: m = r + shift_eps                */
 #define ATTN_GUARD_MASK 0x6u
 #define ATTN_OBAR_FP32 0x8u       /* keep Ō in fp32 (default: bf16 per block)   */
+#define ATTN_DELTA_DP 0x10u       /* backward: delta = rowsum(dP∘P), not dO∘O   */
 
 /* per-row flag bits written by attn_fwd */
 #define ATTN_ROW_TIE 0x1u           /* the row maximum recurs within tie_eps   */
@@ -70,7 +71,8 @@ typedef struct {
   float beta;        /* beta-guard multiplier, > 1 (the pages use 2..8)      */
   float tie_eps;     /* tie window, >= 0: tie iff fl32(r - r2) <= tie_eps    */
   float shift_eps;   /* eps-guard extra shift, > 0 (the pages use 2^-5)      */
-  uint32_t flags;    /* ATTN_CAUSAL | one ATTN_GUARD_* | ATTN_OBAR_FP32      */
+  uint32_t flags;    /* ATTN_CAUSAL | one ATTN_GUARD_* | ATTN_OBAR_FP32 |
+                        ATTN_DELTA_DP                                        */
 } attn_params;
 
 /*
@@ -109,6 +111,11 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
  *   q, k, v, o (bf16), dout [B,Hq,N,d] bf16, row_m, row_l from attn_fwd (in)
  *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d] bf16                  (out)
  *   delta [B,Hq,N] fp32 = rowsum(dO∘O)                      (out, required)
+ * With ATTN_DELTA_DP, delta = rowsum(dP∘P) instead: the pages' other form
+ * of the same quantity, which never reads the bf16 O ([R] method, paper
+ * §3.2: computing it this way also stabilised training; [S] "Key claims").
+ * It costs a first sweep over the keys (S and dP once more) in
+ * attn_bwd_dq; o is not read and may be NULL.
  * dK and dV sum over the heads_q/heads_kv query heads sharing a KV head.
  * No scratch memory: every output element is written once, by one
  * workgroup, so results are bitwise reproducible.
@@ -120,8 +127,10 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
 /* attn_bwd's stages, callable one by one (same arguments and rules), in
  * this order:
  *   attn_bwd_dq: per query row, delta = rowsum(dO∘O) in fp32 from the bf16
- *     O ([R] "Core idea"/method: the delta term, paper §3.2), written to
- *     delta; then over every key the row sees, S, P = exp(t - row_m)/row_l,
+ *     O ([R] "Core idea"/method: the delta term, paper §3.2), or with
+ *     ATTN_DELTA_DP delta = rowsum(dP∘P) in fp32 from a first sweep over
+ *     the row's keys, written to delta; then over every key the row sees,
+ *     S, P = exp(t - row_m)/row_l,
  *     dP = dO V^T, dS = P∘(dP - delta) and dQ = alpha dS K ([R] "Core
  *     idea", Eq. 1-2).
  *   attn_bwd_dkdv: per key, over every query row that sees it, the same S,

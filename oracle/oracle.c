@@ -589,6 +589,62 @@ int orc_bwd_rows_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   return 0;
 }
 
+/* The other form of the backward's delta, written out as the pages give it:
+ * delta_i = sum_j P_ij dP_ij with P the exact softmax row and dP_ij =
+ * dO_i . V_j ([R] method, paper §3.2: rowsum(dP∘P) is mathematically the
+ * same as rowsum(dO∘O); [S] "Key claims").  All in double. */
+typedef struct {
+  const orc_problem* p;
+  const uint16_t *q, *k, *v, *dout;
+  const int32_t *qheads, *rows;
+  double* delta;
+} deltadp_ctx;
+
+static void deltadp_item(void* c, int32_t item) {
+  deltadp_ctx* x = (deltadp_ctx*)c;
+  const orc_problem* p = x->p;
+  int32_t qh = x->qheads[item], i = x->rows[item];
+  int32_t d = p->head_dim;
+  const uint16_t* qi = x->q + q_head_offset(p, qh) + (size_t)i * d;
+  const uint16_t* doi = x->dout + q_head_offset(p, qh) + (size_t)i * d;
+  const uint16_t* K = x->k + kv_head_offset(p, qh);
+  const uint16_t* V = x->v + kv_head_offset(p, qh);
+  int32_t n = visible(p, i);
+  double* P = (double*)malloc(sizeof(double) * (size_t)n);
+  double mx = -INFINITY;
+  for (int32_t j = 0; j < n; ++j) {
+    P[j] = (double)p->alpha * dot_bf16(qi, K + (size_t)j * d, d);
+    if (P[j] > mx) mx = P[j];
+  }
+  double z = 0.0;
+  for (int32_t j = 0; j < n; ++j) {
+    P[j] = exp(P[j] - mx);
+    z += P[j];
+  }
+  double delta = 0.0;
+  for (int32_t j = 0; j < n; ++j) {
+    double dp = dot_bf16(doi, V + (size_t)j * d, d);
+    delta += (P[j] / z) * dp;
+  }
+  x->delta[item] = delta;
+  free(P);
+}
+
+int orc_delta_dp_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                          const int32_t* rows, int32_t n, double* delta, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout || !qheads || !rows || !delta) return -1;
+  for (int32_t i = 0; i < n; ++i) {
+    if (qheads[i] < 0 || qheads[i] >= p->batch * p->heads_q) return -2;
+    if (rows[i] < 0 || rows[i] >= p->seqlen) return -2;
+  }
+  deltadp_ctx c = {p, q, k, v, dout, qheads, rows, delta};
+  run_pool(deltadp_item, &c, n, nthreads);
+  return 0;
+}
+
 /* ======================================================================
  * The repeated-maximum guard.
  * [R] "Core idea", the fix (paper §4): a row whose maximum r recurs (within

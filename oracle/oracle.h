@@ -125,6 +125,13 @@ int orc_bwd_rows_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
                      const int32_t* rows, int32_t n, const double* o_in, int32_t round_ops,
                      double* delta, double* dq, int32_t nthreads);
 
+/* delta_i = sum_j P_ij dP_ij (exact softmax row P, dP_ij = dO_i . V_j) for
+ * single rows: row rows[i] of query head qheads[i]; in double.  [R] method
+ * (paper §3.2): the form of delta that does not use the low-precision O. */
+int orc_delta_dp_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                          const int32_t* rows, int32_t n, double* delta, int32_t nthreads);
+
 /* Row statistics on the fp32 scaled logits t = fl32(alpha * fl32(s)):
  * r = max, r2 = second largest (multiset), tie flag, final shift m.
  * flag_cert[i] = 1 when the kernel's score error (orc_schedule's model of

@@ -14,12 +14,12 @@ from _util import (MAX_REL, MEAN_EXCESS, MEAN_REL, dev, f32, make, problem, rel_
 pytestmark = pytest.mark.gpu
 
 
-def _fwd_bwd(x, guard, beta=2.0, obar_fp32=False):
+def _fwd_bwd(x, guard, beta=2.0, obar_fp32=False, delta="do_o"):
     wl = x["workload"]
     q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"])
     f = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard, beta=beta, obar_fp32=obar_fp32)
-    b = fa.attn_bwd(q, k, v, f["o"], do, f["row_m"], f["row_l"], causal=wl.causal, guard=guard,
-                    beta=beta)
+    b = fa.attn_bwd(q, k, v, None if delta == "dp_p" else f["o"], do, f["row_m"], f["row_l"],
+                    causal=wl.causal, guard=guard, beta=beta, delta=delta)
     torch.cuda.synchronize()
     return f, b
 
@@ -43,12 +43,16 @@ def _check(name, gpu, ref, floor=None):
     return out
 
 
-def _floors(p, x, ref, obar_fp32=False, kv_heads=None, qheads=None, kvsel=None):
+def _floors(p, x, ref, obar_fp32=False, kv_heads=None, qheads=None, kvsel=None, delta="do_o"):
     """The method's own deviation from FP64 for dq, dk, dv, delta: the
-    oracle's backward replay with delta from the oracle's emulated bf16 O."""
-    e = orc.fwd_emu(p, schedule(p, obar_fp32, certify=False), x["q"], x["k"], x["v"], heads=qheads,
-                    nthreads=threads())
-    rep = orc.bwd_emu(p, x["q"], x["k"], x["v"], x["do"], o_in=e["o"], round_ops=True,
+    oracle's backward replay with delta from the oracle's emulated bf16 O
+    (delta = rowsum(dO∘O)), or the exact delta (delta = rowsum(dP∘P), whose
+    only rounding is the kernel's fp32 sum)."""
+    o_in = None
+    if delta == "do_o":
+        o_in = orc.fwd_emu(p, schedule(p, obar_fp32, certify=False), x["q"], x["k"], x["v"],
+                           heads=qheads, nthreads=threads())["o"]
+    rep = orc.bwd_emu(p, x["q"], x["k"], x["v"], x["do"], o_in=o_in, round_ops=True,
                       kv_heads=kv_heads, nthreads=threads())
     wl = x["workload"]
     qs = (-1, wl.seqlen, wl.head_dim)
@@ -191,3 +195,66 @@ def test_stages_equal_fused_and_deterministic():
     # every output element is written once by one workgroup: bitwise equal
     assert torch.equal(delta, b1["delta"])
     assert torch.equal(dk, b1["dk"]) and torch.equal(dv, b1["dv"]) and torch.equal(dq, b1["dq"])
+
+
+# delta = rowsum(dP∘P) ([R] method, paper §3.2): computed in fp32 from the
+# recomputed P and dP, it carries no bf16 rounding of O, so it must sit far
+# closer to the FP64 delta than the default rowsum(dO∘O) does.
+DP_DELTA_MAX, DP_DELTA_MEAN = 1e-4, 2e-5
+
+
+def _check_delta_dp(gpu, ref, gpu_default):
+    mx, mean = rel_errors(gpu, ref)
+    dmx, dmean = rel_errors(gpu_default, ref)
+    assert mx <= DP_DELTA_MAX and mean <= DP_DELTA_MEAN, ("delta dP∘P", mx, mean)
+    # (where O is exact in bf16, e.g. a single visible key, both are exact)
+    assert mean < 0.1 * dmean or dmean <= DP_DELTA_MEAN, ("delta dP∘P not closer than dO∘O", mean, dmean)
+    return {"delta_dp_max": f"{mx:.2e}", "delta_dp_mean": f"{mean:.2e}",
+            "delta_doo_max": f"{dmx:.2e}", "delta_doo_mean": f"{dmean:.2e}"}
+
+
+@pytest.mark.parametrize("name,shape,guard", [
+    ("tiny", None, "none"), ("tiny", None, "beta"),
+    ("ragged", (1, 4, 1, 257, 128, True), "beta"), ("ragged", (2, 4, 2, 65, 64, False), "eps"),
+    ("ragged", (1, 1, 1, 1, 64, True), "beta"),
+])
+def test_delta_dp_mode(name, shape, guard):
+    if name == "ragged":
+        B, Hq, Hkv, N, d, causal = shape
+        wl = W.Workload("ragged", B, Hq, Hkv, N, d, causal, 1.0, 1.0, "const", -0.3,
+                        4.0 if N > 2 else 0.0, 0.1, 0.0, 16.0, 79)
+        x = W.make_custom(wl)
+    else:
+        x = make(name)
+        wl = x["workload"]
+    p = problem(wl, guard)
+    ref = orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], nthreads=threads())
+    fl = _floors(p, x, ref, delta="dp_p")
+    _, b = _fwd_bwd(x, guard, delta="dp_p")
+    _, b0 = _fwd_bwd(x, guard)
+    out = _check_delta_dp(b["delta"].cpu().numpy(), ref["delta"], b0["delta"].cpu().numpy())
+    if wl.seqlen > 1:
+        out.update(_check("dq", f32(b["dq"]), ref["dq"], fl["dq"]))
+        out.update(_check("dk", f32(b["dk"]), ref["dk"], fl["dk"]))
+    out.update(_check("dv", f32(b["dv"]), ref["dv"], fl["dv"]))
+    report(f"bwd delta=dP∘P {name} {shape or ''} {guard}", **out)
+
+
+def test_delta_dp_full_size_sampled_heads():
+    """GPT-2 Small, the benchmark's shape: two whole KV heads."""
+    x = make("gpt2s")
+    wl = x["workload"]
+    p = problem(wl, "beta")
+    kv_heads = [7, 150]
+    ref = orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], kv_heads=kv_heads, nthreads=threads())
+    fl = _floors(p, x, ref, kv_heads=kv_heads, qheads=kv_heads, kvsel=kv_heads, delta="dp_p")
+    qs = (-1, wl.seqlen, wl.head_dim)
+    _, b = _fwd_bwd(x, "beta", delta="dp_p")
+    _, b0 = _fwd_bwd(x, "beta")
+    sel = lambda t: t.cpu().numpy().reshape(-1, wl.seqlen)[kv_heads]
+    out = _check_delta_dp(sel(b["delta"]), ref["delta"].reshape(-1, wl.seqlen)[kv_heads],
+                          sel(b0["delta"]))
+    for key in ("dq", "dk", "dv"):
+        out.update(_check(key, f32(b[key]).reshape(qs)[kv_heads], ref[key].reshape(qs)[kv_heads],
+                          fl[key]))
+    report("bwd delta=dP∘P gpt2s beta", **out)

@@ -76,6 +76,45 @@ def test_delta_identity(orc):
     assert np.max(np.abs(r["delta"] - alt)) < 1e-12 * np.max(np.abs(alt))
 
 
+@pytest.mark.parametrize("causal,Hq,Hkv,N,d", [(True, 4, 2, 40, 64), (False, 2, 1, 23, 128)])
+def test_delta_dp_rows(orc, causal, Hq, Hkv, N, d):
+    """The oracle's rowsum(dP∘P) ([R] method, paper §3.2), row by row: equal to
+    the materialised (dP∘P).sum of torch float64 and to the oracle's own
+    rowsum(dO∘O) from the exact O (a different formula), over every row of
+    every query head (GQA head mapping included)."""
+    p, q, k, v, do = _rand_problem(orc, 9, 1, Hq, Hkv, N, d, causal)
+    qh = np.repeat(np.arange(Hq), N)
+    rows = np.tile(np.arange(N), Hq)
+    got = orc.delta_dp_rows_f64(p, q, k, v, do, qh, rows).reshape(1, Hq, N)
+    P, V = _torch_attention(p, q, k, v)
+    ref = ((_t64(do) @ V.transpose(-1, -2)) * P).sum(-1).numpy()
+    scale = np.max(np.abs(ref))
+    assert np.max(np.abs(got - ref)) < 1e-12 * scale
+    r = orc.bwd_f64(p, q, k, v, do)
+    assert np.max(np.abs(got - r["delta"])) < 1e-12 * scale
+
+
+def test_delta_dp_special_cases(orc):
+    """Causal row 0 sees one key (P = 1): delta = dO_0 . V_0.  A logit shift
+    common to every key of a row (a feature that is 1 in every query and c
+    in every key) leaves P, and so delta, unchanged."""
+    p, q, k, v, do = _rand_problem(orc, 10, 1, 1, 1, 16, 64, True)
+    d0 = orc.delta_dp_rows_f64(p, q, k, v, do, [0], [0])[0]
+    exact = float(np.dot(W.bits_to_f32(do[0, 0, 0]).astype(np.float64),
+                         W.bits_to_f32(v[0, 0, 0]).astype(np.float64)))
+    assert abs(d0 - exact) <= 1e-15 * abs(exact)
+    p, q, k, v, do = _rand_problem(orc, 11, 1, 1, 1, 30, 64, False)
+    rows = np.arange(30)
+    base_q, base_k = q.copy(), k.copy()
+    base_q[..., 63] = W.to_bf16_bits(np.ones(1, np.float32))[0]
+    base_k[..., 63] = 0
+    shifted_k = base_k.copy()
+    shifted_k[..., 63] = W.to_bf16_bits(np.full(1, 24.0, np.float32))[0]
+    a = orc.delta_dp_rows_f64(p, base_q, base_k, v, do, np.zeros(30, int), rows)
+    b = orc.delta_dp_rows_f64(p, base_q, shifted_k, v, do, np.zeros(30, int), rows)
+    assert np.max(np.abs(a - b)) < 1e-13 * np.max(np.abs(a))
+
+
 def test_gradient_structure(orc):
     """Softmax shift invariance makes every row of dS sum to zero, so the key
     gradients of a head sum to zero; rows of P sum to one, so sum_j dV_j =
