@@ -61,9 +61,9 @@ def lib():
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p]
         L.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for n in ("attn_schedule", "attn_fwd", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -156,10 +156,11 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
 
 
 def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=2.0,
-             tie_eps=1e-3, shift_eps=2.0 ** -5, softmax_scale=None, delta="do_o", out=None,
-             stream=None):
-    """Backward.  Returns a dict: dq, dk, dv (bf16) and delta (fp32).
-    delta="dp_p" forms delta = rowsum(dP∘P) (o is then not read; it may be None)."""
+             tie_eps=1e-3, shift_eps=2.0 ** -5, softmax_scale=None, delta="do_o",
+             row_dsum=False, out=None, stream=None):
+    """Backward.  Returns a dict: dq, dk, dv (bf16) and delta (fp32), and with
+    row_dsum=True the row sums of dS (fp32, without alpha).  delta="dp_p"
+    forms delta = rowsum(dP∘P) (o is then not read; it may be None)."""
     for n_, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if t is None and n_ == "o" and delta == "dp_p":
             continue
@@ -173,9 +174,12 @@ def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=
         res["dk"] = torch.empty_like(k)
         res["dv"] = torch.empty_like(v)
         res["delta"] = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if row_dsum and "row_dsum" not in res:
+        res["row_dsum"] = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _call("attn_bwd", lib().attn_bwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
-        _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["delta"]), _stream(stream)))
+        _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["delta"]),
+        _ptr(res.get("row_dsum") if row_dsum else None), _stream(stream)))
     return res
 
 
@@ -185,10 +189,10 @@ def attn_bwd_dkdv(p: Params, q, k, v, dout, row_m, row_l, delta, dk, dv, stream=
         _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
-def attn_bwd_dq(p: Params, q, k, v, o, dout, row_m, row_l, dq, delta, stream=None):
+def attn_bwd_dq(p: Params, q, k, v, o, dout, row_m, row_l, dq, delta, row_dsum=None, stream=None):
     _call("attn_bwd_dq", lib().attn_bwd_dq(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
-        _ptr(dq), _ptr(delta), _stream(stream)))
+        _ptr(dq), _ptr(delta), _ptr(row_dsum), _stream(stream)))
 
 
 def default_scale(head_dim: int) -> float:

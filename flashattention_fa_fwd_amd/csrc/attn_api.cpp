@@ -158,7 +158,7 @@ int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void
 
 int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* row_m, const float* row_l, void* dq, float* delta,
-                void* stream) {
+                float* row_dsum, void* stream) {
   const int rc = check_params(p);
   if (rc) return rc;
   if (!q || !k || !v || (!o && needs_o(p)) || !dout || !row_m || !row_l || !dq || !delta)
@@ -166,14 +166,15 @@ int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) ||
       !aligned16(dout) || !aligned16(dq))
     return ATTN_E_UNSUPPORTED;
-  const attn::BwdArgs a = bwd_args(p, q, k, v, o, dout, row_m, row_l, dq, nullptr, nullptr, delta);
+  attn::BwdArgs a = bwd_args(p, q, k, v, o, dout, row_m, row_l, dq, nullptr, nullptr, delta);
+  a.row_dsum = row_dsum;
   return hip_status(attn::launch_bwd_dq(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
                                         (p->flags & ATTN_DELTA_DP) != 0, (hipStream_t)stream));
 }
 
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
              const void* dout, const float* row_m, const float* row_l, void* dq, void* dk,
-             void* dv, float* delta, void* stream) {
+             void* dv, float* delta, float* row_dsum, void* stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if (!q || !k || !v || (!o && needs_o(p)) || !dout || !row_m || !row_l || !dq || !dk || !dv ||
@@ -182,7 +183,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o)) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_E_UNSUPPORTED;
-  rc = attn_bwd_dq(p, q, k, v, o, dout, row_m, row_l, dq, delta, stream);
+  rc = attn_bwd_dq(p, q, k, v, o, dout, row_m, row_l, dq, delta, row_dsum, stream);
   if (rc) return rc;
   return attn_bwd_dkdv(p, q, k, v, dout, row_m, row_l, delta, dk, dv, stream);
 }

@@ -304,9 +304,9 @@ constexpr int kDqKeys = 64;   // keys per streaming step
 // One streaming step of the dQ kernel for one wave (keys j0..j0+63), after
 // the barrier that published the step's K/V tiles: the copy of the next
 // tiles first, then S^T, dP^T, dS^T and the dQ^T product.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DSUM>
 __device__ __forceinline__ void dq_step(
-    const BwdArgs& a, f32x16 (&dq)[D / 32], const bf16x8 (&qf)[D / kMfmaK],
+    const BwdArgs& a, f32x16 (&dq)[D / 32], float& dsum, const bf16x8 (&qf)[D / kMfmaK],
     const bf16x8 (&gf)[D / kMfmaK], const int (&ka_off)[2][D / kMfmaK], const int (&ta_off)[D / 32][2],
     const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs,
     uint16_t* __restrict__ ks_next, uint16_t* __restrict__ vs_next, i32x4 rk,
@@ -357,6 +357,12 @@ __device__ __forceinline__ void dq_step(
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) dsv[kb][i] = 0.0f;
+    }
+    if constexpr (DSUM) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dsum += dsv[kb][i];
     }
     // dS^T in bf16 as the B operand of dQ^T += K^T dS^T: product t covers
     // keys 16t..16t+15, its k index 8*half + j is key 16t + 8(j/4) +
@@ -441,8 +447,9 @@ __device__ __forceinline__ void dq_delta_step(
 }
 
 // DELTA_DP: delta = rowsum(dP∘P) from a first sweep over the keys instead
-// of rowsum(dO∘O) from the bf16 O.
-template <int D, bool CAUSAL, bool DELTA_DP>
+// of rowsum(dO∘O) from the bf16 O.  DSUM: also the row sums of dS (fp32,
+// before the bf16 rounding of the dQ operand, without the factor alpha).
+template <int D, bool CAUSAL, bool DELTA_DP, bool DSUM>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = kDqKeys;
   constexpr int NT = D / kMfmaK;     // 16-wide steps along d
@@ -554,15 +561,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  float dsum = 0.0f;
   for (int j0 = 0; j0 < kend; j0 += BN) {
     const int cur = (j0 / BN) & 1;
     // tile j0 is complete; every wave is done with the previous tile
     __syncthreads();
     const bool more = j0 + BN < kend;
-    dq_step<D, CAUSAL>(a, dq, qf, gf, ka_off, ta_off, Ks[cur], Vs[cur], Ks[cur ^ 1], Vs[cur ^ 1], rk,
-                       rv, more, j0, wave, lane, wave_live, q0, qrow, half, lse2, del);
+    dq_step<D, CAUSAL, DSUM>(a, dq, dsum, qf, gf, ka_off, ta_off, Ks[cur], Vs[cur], Ks[cur ^ 1],
+                             Vs[cur ^ 1], rk, rv, more, j0, wave, lane, wave_live, q0, qrow, half,
+                             lse2, del);
     // the copies must land before the next barrier publishes the tile
     if (more) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+  if constexpr (DSUM) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dsum), __float_as_uint(dsum), false, false);
+    if (qrow < N && half == 0)
+      a.row_dsum[(size_t)(b * a.Hq + hq) * N + qrow] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
 
   // ---- dQ = bf16(alpha * dQ): lane = row, register i of block f = feature
@@ -598,25 +612,28 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <bool DELTA_DP>
+template <bool DELTA_DP, bool DSUM>
 hipError_t launch_dq_t(const BwdArgs& a, int d, bool causal, hipStream_t s) {
   const dim3 grid((unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.Hq * a.B));
   if (d == 64) {
     if (causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<64, true, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true, DELTA_DP, DSUM>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<64, false, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false, DELTA_DP, DSUM>), grid, dim3(kThreads), 0, s, a);
   } else {
     if (causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<128, true, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, true, DELTA_DP, DSUM>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<128, false, DELTA_DP>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, false, DELTA_DP, DSUM>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, bool delta_dp, hipStream_t s) {
-  return delta_dp ? launch_dq_t<true>(a, d, causal, s) : launch_dq_t<false>(a, d, causal, s);
+  const bool dsum = a.row_dsum != nullptr;
+  if (delta_dp)
+    return dsum ? launch_dq_t<true, true>(a, d, causal, s) : launch_dq_t<true, false>(a, d, causal, s);
+  return dsum ? launch_dq_t<false, true>(a, d, causal, s) : launch_dq_t<false, false>(a, d, causal, s);
 }
 
 }  // namespace attn

@@ -49,6 +49,7 @@ struct BwdArgs {
   const float* row_m;
   const float* row_l;
   float* delta;
+  float* row_dsum;  // nullable: row sums of dS (dQ kernel)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -116,13 +116,20 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
  * §3.2: computing it this way also stabilised training; [S] "Key claims").
  * It costs a first sweep over the keys (S and dP once more) in
  * attn_bwd_dq; o is not read and may be NULL.
+ *   row_dsum [B,Hq,N] fp32 (out, nullable): sum_j P_ij (dP_ij - delta_i),
+ * the row sum of dS without the factor alpha, in fp32 over the fp32 values
+ * (before their bf16 rounding as the dQ operand).  In exact arithmetic it is
+ * rowsum(dP∘P) - delta: zero with ATTN_DELTA_DP, and minus the error of the
+ * low-precision delta otherwise -- the per-token coefficient through which
+ * that error enters the query gradient ([R] "Core idea", equations, paper
+ * Eq. 1-2).  Not computed (no cost) when NULL.
  * dK and dV sum over the heads_q/heads_kv query heads sharing a KV head.
  * No scratch memory: every output element is written once, by one
  * workgroup, so results are bitwise reproducible.
  */
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
              const void* o, const void* dout, const float* row_m, const float* row_l,
-             void* dq, void* dk, void* dv, float* delta, void* stream);
+             void* dq, void* dk, void* dv, float* delta, float* row_dsum, void* stream);
 
 /* attn_bwd's stages, callable one by one (same arguments and rules), in
  * this order:
@@ -138,7 +145,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v,
  *     dK = alpha dS^T Q ([R] "Core idea", Eq. 1-2).                        */
 int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v,
                 const void* o, const void* dout, const float* row_m, const float* row_l,
-                void* dq, float* delta, void* stream);
+                void* dq, float* delta, float* row_dsum, void* stream);
 int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void* v,
                   const void* dout, const float* row_m, const float* row_l,
                   const float* delta, void* dk, void* dv, void* stream);

@@ -140,6 +140,8 @@ def lib():
                                        f64p, ctypes.c_int32, f64p, f64p, ctypes.c_int32]
         L.orc_delta_dp_rows_f64.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
                                             f64p, ctypes.c_int32]
+        L.orc_dsum_rows_f64.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
+                                        f64p, f64p, f64p, ctypes.c_int32]
         L.orc_fwd_emu_rows.argtypes = [pp, sp, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
                                        f64p, f32p, f32p, u8p, ctypes.c_int32]
         L.orc_row_stats.argtypes = [pp, sp, u16p, u16p, i32p, ctypes.c_int32,
@@ -149,7 +151,7 @@ def lib():
                                   f64p, u8p, f64p, f32p, f32p, u8p, u8p, u8p, ctypes.c_int32]
         for name in ("orc_fwd_f64", "orc_bwd_f64", "orc_bwd_rows_f64", "orc_row_stats",
                      "orc_obar_f64", "orc_fwd_emu", "orc_bwd_emu", "orc_bwd_rows_emu",
-                     "orc_fwd_emu_rows", "orc_delta_dp_rows_f64"):
+                     "orc_fwd_emu_rows", "orc_delta_dp_rows_f64", "orc_dsum_rows_f64"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -290,6 +292,25 @@ def delta_dp_rows_f64(p: Problem, q, k, v, dout, qheads, rows, nthreads=None):
                                        _ptr(delta, ctypes.c_double), _threads(nthreads)),
            "orc_delta_dp_rows_f64")
     return delta
+
+
+def dsum_rows_f64(p: Problem, q, k, v, dout, qheads, rows, delta_in, nthreads=None):
+    """Row sums of dS for the given delta (double, without alpha): returns
+    (sum_j P (dP - delta), sum_j P |dP - delta|) per row ([R] Eq. 1-2)."""
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    qh = np.ascontiguousarray(np.asarray(qheads, dtype=np.int32))
+    rw = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    n = int(qh.size)
+    di = np.ascontiguousarray(np.asarray(delta_in, np.float64).reshape(-1))
+    assert di.size == n
+    dsum = np.zeros(n, np.float64); wsum = np.zeros(n, np.float64)
+    pc = p.c()
+    _check(lib().orc_dsum_rows_f64(ctypes.byref(pc), _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                   _ptr(v, ctypes.c_uint16), _ptr(dout, ctypes.c_uint16),
+                                   _ptr(qh, ctypes.c_int32), _ptr(rw, ctypes.c_int32), n,
+                                   _ptr(di, ctypes.c_double), _ptr(dsum, ctypes.c_double),
+                                   _ptr(wsum, ctypes.c_double), _threads(nthreads)), "orc_dsum_rows_f64")
+    return dsum, wsum
 
 
 def bwd_emu(p: Problem, q, k, v, dout, o_in=None, round_ops=True, kv_heads=None, nthreads=None):

@@ -645,6 +645,68 @@ int orc_delta_dp_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_
   return 0;
 }
 
+/* Row sums of dS for a given delta, written out: sum_j P_ij (dP_ij -
+ * delta_i) with P the exact softmax row and dP_ij = dO_i . V_j, and the
+ * magnitude sum_j P_ij |dP_ij - delta_i| of its terms.  [R] "Core idea",
+ * equations (paper Eq. 1-2): dS = alpha P∘(dP - delta); the rows of P sum to
+ * one, so the row sum is rowsum(dP∘P) - delta (zero for the exact delta).
+ * All in double; alpha is left out. */
+typedef struct {
+  const orc_problem* p;
+  const uint16_t *q, *k, *v, *dout;
+  const int32_t *qheads, *rows;
+  const double* delta_in;
+  double *dsum, *wsum;
+} dsum_ctx;
+
+static void dsum_item(void* c, int32_t item) {
+  dsum_ctx* x = (dsum_ctx*)c;
+  const orc_problem* p = x->p;
+  int32_t qh = x->qheads[item], i = x->rows[item];
+  int32_t d = p->head_dim;
+  const uint16_t* qi = x->q + q_head_offset(p, qh) + (size_t)i * d;
+  const uint16_t* doi = x->dout + q_head_offset(p, qh) + (size_t)i * d;
+  const uint16_t* K = x->k + kv_head_offset(p, qh);
+  const uint16_t* V = x->v + kv_head_offset(p, qh);
+  int32_t n = visible(p, i);
+  double* P = (double*)malloc(sizeof(double) * (size_t)n);
+  double mx = -INFINITY;
+  for (int32_t j = 0; j < n; ++j) {
+    P[j] = (double)p->alpha * dot_bf16(qi, K + (size_t)j * d, d);
+    if (P[j] > mx) mx = P[j];
+  }
+  double z = 0.0;
+  for (int32_t j = 0; j < n; ++j) {
+    P[j] = exp(P[j] - mx);
+    z += P[j];
+  }
+  double sum = 0.0, mag = 0.0;
+  for (int32_t j = 0; j < n; ++j) {
+    double t = (P[j] / z) * (dot_bf16(doi, V + (size_t)j * d, d) - x->delta_in[item]);
+    sum += t;
+    mag += fabs(t);
+  }
+  x->dsum[item] = sum;
+  x->wsum[item] = mag;
+  free(P);
+}
+
+int orc_dsum_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                      const int32_t* rows, int32_t n, const double* delta_in, double* dsum,
+                      double* wsum, int32_t nthreads) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !dout || !qheads || !rows || !delta_in || !dsum || !wsum) return -1;
+  for (int32_t i = 0; i < n; ++i) {
+    if (qheads[i] < 0 || qheads[i] >= p->batch * p->heads_q) return -2;
+    if (rows[i] < 0 || rows[i] >= p->seqlen) return -2;
+  }
+  dsum_ctx c = {p, q, k, v, dout, qheads, rows, delta_in, dsum, wsum};
+  run_pool(dsum_item, &c, n, nthreads);
+  return 0;
+}
+
 /* ======================================================================
  * The repeated-maximum guard.
  * [R] "Core idea", the fix (paper §4): a row whose maximum r recurs (within

@@ -132,6 +132,15 @@ int orc_delta_dp_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_
                           const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
                           const int32_t* rows, int32_t n, double* delta, int32_t nthreads);
 
+/* Row sums of dS for a given delta (delta_in[i] for row i): dsum[i] =
+ * sum_j P_ij (dP_ij - delta_in[i]) and wsum[i] = sum_j P_ij |dP_ij -
+ * delta_in[i]|, exact softmax P, in double, without alpha.  [R] "Core idea",
+ * equations (paper Eq. 1-2). */
+int orc_dsum_rows_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const uint16_t* dout, const int32_t* qheads,
+                      const int32_t* rows, int32_t n, const double* delta_in, double* dsum,
+                      double* wsum, int32_t nthreads);
+
 /* Row statistics on the fp32 scaled logits t = fl32(alpha * fl32(s)):
  * r = max, r2 = second largest (multiset), tie flag, final shift m.
  * flag_cert[i] = 1 when the kernel's score error (orc_schedule's model of

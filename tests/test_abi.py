@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 4
+    assert fa.attn_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -101,24 +101,24 @@ def test_backward_argument_errors(L):
     """The backward stages validate before enqueueing anything (no GPU needed)."""
     vp = ctypes.c_void_p
     p = fa.make_params(2, 4, 2, 100, 64)
-    args = [vp(FAKE)] * 11
+    args = [vp(FAKE)] * 11 + [None]  # ..., delta, row_dsum (optional)
     assert L.attn_bwd(ctypes.byref(p), *[None] + args[1:], None) == -1          # q missing
     assert L.attn_bwd(ctypes.byref(p), *[vp(FAKE + 2)] + args[1:], None) == -3  # misaligned
     assert L.attn_bwd_dkdv(ctypes.byref(p), *[vp(FAKE)] * 8, None, None) == -1  # dv missing
-    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 8, None, None) == -1  # delta missing
-    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 7, vp(FAKE + 8), vp(FAKE), None) == -3
+    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 8, None, None, None) == -1  # delta missing
+    assert L.attn_bwd_dq(ctypes.byref(p), *[vp(FAKE)] * 7, vp(FAKE + 8), vp(FAKE), None, None) == -3
     bad = fa.make_params(1, 3, 2, 10, 64)
-    assert L.attn_bwd_dq(ctypes.byref(bad), *[vp(FAKE)] * 9, None) == -2
+    assert L.attn_bwd_dq(ctypes.byref(bad), *[vp(FAKE)] * 9, None, None) == -2
     huge = fa.make_params(1, 1, 1, 1 << 24, 64)  # one head past a 32-bit byte range
     assert L.attn_bwd_dkdv(ctypes.byref(huge), *[vp(FAKE)] * 9, None) == -2
     # O is required for delta = rowsum(dO∘O) only; when given it must be aligned
-    no_o = [vp(FAKE)] * 4 + [None] + [vp(FAKE)] * 6
+    no_o = [vp(FAKE)] * 4 + [None] + [vp(FAKE)] * 6 + [None]
     assert L.attn_bwd(ctypes.byref(p), *no_o, None) == -1
     dp = fa.make_params(2, 4, 2, 100, 64, delta="dp_p")
     assert dp.flags & fa.DELTA_DP
-    bad_o = [vp(FAKE)] * 4 + [vp(FAKE + 8)] + [vp(FAKE)] * 6
+    bad_o = [vp(FAKE)] * 4 + [vp(FAKE + 8)] + [vp(FAKE)] * 6 + [None]
     assert L.attn_bwd(ctypes.byref(dp), *bad_o, None) == -3
-    assert L.attn_bwd_dq(ctypes.byref(dp), *[vp(FAKE)] * 3, vp(FAKE + 8), *[vp(FAKE)] * 5, None) == -3
+    assert L.attn_bwd_dq(ctypes.byref(dp), *[vp(FAKE)] * 3, vp(FAKE + 8), *[vp(FAKE)] * 5, None, None) == -3
     with pytest.raises(ValueError):
         fa.make_params(1, 1, 1, 64, 64, delta="o")
 

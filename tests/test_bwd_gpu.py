@@ -258,3 +258,82 @@ def test_delta_dp_full_size_sampled_heads():
         out.update(_check(key, f32(b[key]).reshape(qs)[kv_heads], ref[key].reshape(qs)[kv_heads],
                           fl[key]))
     report("bwd delta=dP∘P gpt2s beta", **out)
+
+
+def _dsum_case(name, shape):
+    if name == "ragged":
+        B, Hq, Hkv, N, d, causal = shape
+        wl = W.Workload("ragged", B, Hq, Hkv, N, d, causal, 1.0, 1.0, "const", -0.3,
+                        4.0 if N > 2 else 0.0, 0.1, 0.0, 16.0, 80)
+        return W.make_custom(wl)
+    return make(name)
+
+
+@pytest.mark.parametrize("name,shape,guard,delta", [
+    ("tiny", None, "beta", "do_o"), ("tiny", None, "none", "dp_p"),
+    ("ragged", (1, 4, 1, 257, 128, True), "beta", "do_o"),
+    ("ragged", (2, 4, 2, 65, 64, False), "eps", "dp_p"), ("gpt2s", None, "beta", "do_o"),
+])
+def test_row_dsum(name, shape, guard, delta):
+    """Row sums of dS from the dQ kernel ([R] "Core idea", equations, paper
+    Eq. 1-2; without alpha).  Since the rows of P sum to one, sum_j P (dP -
+    delta) = rowsum(dP∘P) - delta for whatever delta the kernel used, so
+    row_dsum + delta (both from the kernel) must equal the oracle's exact
+    rowsum(dP∘P), per row, to |err| <= 1e-5 sum_j P|dP - delta| + 2e-6 |delta|
+    (fp32 sums of the recomputed P and dP: about sqrt(N) unit roundoffs of
+    the terms' magnitude, below the N-roundoff worst case at N <= 1024).
+    With delta = rowsum(dP∘P) the row sums themselves are zero to the same
+    bound."""
+    x = _dsum_case(name, shape)
+    wl = x["workload"]
+    p = problem(wl, guard)
+    nq = wl.batch * wl.heads_q
+    qheads = list(range(nq)) if name != "gpt2s" else [3, 120]
+    qh = np.repeat(qheads, wl.seqlen)
+    rows = np.tile(np.arange(wl.seqlen), len(qheads))
+    exact = orc.delta_dp_rows_f64(p, x["q"], x["k"], x["v"], x["do"], qh, rows, nthreads=threads())
+    _, wsum = orc.dsum_rows_f64(p, x["q"], x["k"], x["v"], x["do"], qh, rows, exact, nthreads=threads())
+    _, b = _fwd_bwd_dsum(x, guard, delta)
+    pick = lambda t: t.cpu().numpy().reshape(nq, wl.seqlen)[qheads].reshape(-1).astype(np.float64)
+    got, dgpu = pick(b["row_dsum"]), pick(b["delta"])
+    tol = 1e-5 * wsum + 2e-6 * np.abs(exact) + 1e-7
+    err = np.abs(got + dgpu - exact)
+    assert np.all(err <= tol), (np.max(err / tol), int(np.argmax(err / tol)))
+    out = {"max_err_over_tol": f"{np.max(err / tol):.2e}", "mean_abs_dsum": f"{np.mean(np.abs(got)):.2e}",
+           "mean_wsum": f"{np.mean(wsum):.2e}"}
+    if delta == "dp_p":  # the exact value is zero
+        assert np.all(np.abs(got) <= tol), np.max(np.abs(got) / tol)
+    report(f"row dsum {name} {shape or ''} {guard} {delta}", **out)
+
+
+def _fwd_bwd_dsum(x, guard, delta):
+    wl = x["workload"]
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"])
+    f = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard)
+    b = fa.attn_bwd(q, k, v, None if delta == "dp_p" else f["o"], do, f["row_m"], f["row_l"],
+                    causal=wl.causal, guard=guard, delta=delta, row_dsum=True)
+    torch.cuda.synchronize()
+    return f, b
+
+
+def test_row_dsum_is_minus_the_delta_error():
+    """The dS row sums of the default backward are rowsum(dP∘P) - delta_lp in
+    exact arithmetic: the per-token coefficient of the pages' Eq. 2 with the
+    sign turned.  Checked against the delta of the rowsum(dP∘P) backward at
+    the GPT-2 Small shape (a property at full size); the gradients of the
+    two modes are otherwise computed alike, so dS row sums also vanish in
+    the second."""
+    x = make("gpt2s")
+    _, b = _fwd_bwd_dsum(x, "beta", "do_o")
+    _, bp = _fwd_bwd_dsum(x, "beta", "dp_p")
+    ddelta = (b["delta"] - bp["delta"]).double()       # delta_lp - delta_hp
+    resid = b["row_dsum"].double() + ddelta
+    scale = ddelta.abs().mean().item()
+    assert resid.abs().mean().item() < 0.02 * scale, (resid.abs().mean().item(), scale)
+    assert bp["row_dsum"].double().abs().mean().item() < 0.02 * scale
+    # the pages' Eq. 3 coefficient per head: sum over tokens of the delta error
+    per_head = ddelta.sum(-1).flatten()
+    report("delta error (gpt2s, beta)", mean=f"{ddelta.mean().item():+.3e}",
+           mean_abs=f"{scale:.3e}", eq3_sum_mean=f"{per_head.mean().item():+.3e}",
+           eq3_positive_heads=f"{int((per_head > 0).sum())}/{per_head.numel()}",
+           resid_mean_abs=f"{resid.abs().mean().item():.2e}")

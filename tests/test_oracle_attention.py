@@ -115,6 +115,30 @@ def test_delta_dp_special_cases(orc):
     assert np.max(np.abs(a - b)) < 1e-13 * np.max(np.abs(a))
 
 
+def test_dsum_rows(orc):
+    """Row sums of dS ([R] Eq. 1-2, without alpha): zero for the exact delta
+    (rows of P sum to one); minus c when delta is off by c; equal to the
+    materialised torch float64 (P∘(dP - delta)).sum for any delta."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 33, 64
+    p, q, k, v, do = _rand_problem(orc, 12, B, Hq, Hkv, N, d, True)
+    qh = np.repeat(np.arange(Hq), N)
+    rows = np.tile(np.arange(N), Hq)
+    exact = orc.bwd_f64(p, q, k, v, do)["delta"].reshape(-1)
+    s0, w0 = orc.dsum_rows_f64(p, q, k, v, do, qh, rows, exact)
+    assert np.all(np.abs(s0) <= 1e-13 * w0 + 1e-300)
+    c = np.linspace(-0.5, 0.7, qh.size)
+    s1, _ = orc.dsum_rows_f64(p, q, k, v, do, qh, rows, exact + c)
+    assert np.max(np.abs(s1 + c)) < 1e-12
+    P, V = _torch_attention(p, q, k, v)
+    dP = _t64(do) @ V.transpose(-1, -2)
+    din = torch.from_numpy((exact + c).reshape(B, Hq, N, 1))
+    ref = (P * (dP - din)).sum(-1).numpy().reshape(-1)
+    wref = (P * (dP - din)).abs().sum(-1).numpy().reshape(-1)
+    assert np.max(np.abs(s1 - ref)) < 1e-12 * np.max(wref)
+    _, w1 = orc.dsum_rows_f64(p, q, k, v, do, qh, rows, exact + c)
+    assert np.max(np.abs(w1 - wref)) < 1e-12 * np.max(wref)
+
+
 def test_gradient_structure(orc):
     """Softmax shift invariance makes every row of dS sum to zero, so the key
     gradients of a head sum to zero; rows of P sum to one, so sum_j dV_j =
