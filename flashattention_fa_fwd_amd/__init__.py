@@ -24,6 +24,9 @@ CAUSAL = 0x1
 GUARD_NONE, GUARD_BETA, GUARD_EPS = 0x0, 0x2, 0x4
 OBAR_FP32 = 0x8
 DELTA_DP = 0x10
+SCHED_FA2_OPS = 0x20
+SCHED_UNTILED = 0x40
+_SCHEDULES = {"stream": 0, "fa2_ops": SCHED_FA2_OPS, "untiled": SCHED_UNTILED}
 ROW_TIE, ROW_ZERO_DENOM, ROW_GUARD_APPLIED = 0x1, 0x2, 0x4
 _GUARDS = {"none": GUARD_NONE, "beta": GUARD_BETA, "eps": GUARD_EPS}
 
@@ -59,7 +62,7 @@ def lib():
         L.attn_abi_version.restype = ctypes.c_int
         L.attn_strerror.argtypes = [ctypes.c_int]
         L.attn_strerror.restype = ctypes.c_char_p
-        L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p]
+        L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p, i32p]
         L.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -80,12 +83,16 @@ def attn_strerror(code: int) -> str:
 
 def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guard="beta",
                 beta=2.0, tie_eps=1e-3, shift_eps=2.0 ** -5, obar_fp32=False,
-                softmax_scale=None, delta="do_o") -> Params:
-    """delta: "do_o" (rowsum(dO∘O), the default) or "dp_p" (rowsum(dP∘P))."""
+                softmax_scale=None, delta="do_o", schedule="stream") -> Params:
+    """delta: "do_o" (rowsum(dO∘O), the default) or "dp_p" (rowsum(dP∘P)).
+    schedule: the forward's rounding schedule, "stream" (default), "fa2_ops"
+    (512-key blocks, bf16 block product) or "untiled" (one block a row)."""
     if delta not in ("do_o", "dp_p"):
         raise ValueError(f"delta must be 'do_o' or 'dp_p', not {delta!r}")
+    if schedule not in _SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(_SCHEDULES)}, not {schedule!r}")
     flags = (CAUSAL if causal else 0) | _GUARDS[guard] | (OBAR_FP32 if obar_fp32 else 0)
-    flags |= DELTA_DP if delta == "dp_p" else 0
+    flags |= (DELTA_DP if delta == "dp_p" else 0) | _SCHEDULES[schedule]
     return Params(batch, heads_q, heads_kv, seqlen, head_dim,
                   0.0 if softmax_scale is None else float(softmax_scale),
                   float(beta), float(tie_eps), float(shift_eps), flags)
@@ -120,23 +127,26 @@ def _call(name, rc):
 
 
 def attn_schedule(p: Params):
-    bm, bn, rn, ch = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    bm, bn, rn, ch, bb = (ctypes.c_int32() for _ in range(5))
     _call("attn_schedule", lib().attn_schedule(ctypes.byref(p), ctypes.byref(bm), ctypes.byref(bn),
-                                               ctypes.byref(rn), ctypes.byref(ch)))
-    return dict(block_m=bm.value, block_n=bn.value, round_n=rn.value, chunk=ch.value)
+                                               ctypes.byref(rn), ctypes.byref(ch), ctypes.byref(bb)))
+    return dict(block_m=bm.value, block_n=bn.value, round_n=rn.value, chunk=ch.value,
+                block_bf16=bb.value)
 
 
 def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
-             shift_eps=2.0 ** -5, obar_fp32=False, softmax_scale=None,
+             shift_eps=2.0 ** -5, obar_fp32=False, softmax_scale=None, schedule="stream",
              return_obar=False, return_row_max=False, out=None, stream=None):
-    """Guarded streaming forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16.
+    """Guarded forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16.  schedule:
+    "stream" (the streaming kernel), "fa2_ops" or "untiled" (see make_params).
     Returns a dict: o, row_m, row_l, row_flags (+ obar, row_max on request)."""
     _check_bf16("q", q)
     B, Hq, N, d = q.shape
     _check_bf16("k", k, (B, k.shape[1], N, d))
     _check_bf16("v", v, k.shape)
     p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
-                     shift_eps=shift_eps, obar_fp32=obar_fp32, softmax_scale=softmax_scale)
+                     shift_eps=shift_eps, obar_fp32=obar_fp32, softmax_scale=softmax_scale,
+                     schedule=schedule)
     dev = q.device
     res = out if out is not None else {}
     if "o" not in res:

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_block.hip", "attn_bwd.hip"]
 
 
 def hipcc_cmd(out: str) -> list:

@@ -24,8 +24,10 @@ int check_params(const attn_params* p) {
     return ATTN_E_SHAPE;
   if (p->heads_q % p->heads_kv != 0) return ATTN_E_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return ATTN_E_UNSUPPORTED;
-  const uint32_t known = ATTN_CAUSAL | ATTN_GUARD_MASK | ATTN_OBAR_FP32 | ATTN_DELTA_DP;
+  const uint32_t known =
+      ATTN_CAUSAL | ATTN_GUARD_MASK | ATTN_OBAR_FP32 | ATTN_DELTA_DP | ATTN_SCHED_MASK;
   if (p->flags & ~known) return ATTN_E_PARAM;
+  if ((p->flags & ATTN_SCHED_MASK) == ATTN_SCHED_MASK) return ATTN_E_PARAM;  // two schedules
   const uint32_t g = p->flags & ATTN_GUARD_MASK;
   if (g == ATTN_GUARD_MASK) return ATTN_E_PARAM;  // two guards at once
   if (!std::isfinite(p->softmax_scale)) return ATTN_E_PARAM;
@@ -97,13 +99,22 @@ const char* attn_strerror(int code) {
 }
 
 int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n, int32_t* round_n,
-                  int32_t* chunk) {
+                  int32_t* chunk, int32_t* block_bf16) {
   const int rc = check_params(p);
   if (rc) return rc;
+  int32_t bn = attn::kFwdBlockN, rn = attn::kFwdRoundN, bb = 0;
+  if (p->flags & ATTN_SCHED_FA2_OPS) {
+    bn = rn = attn::kFwdOpsBlockN;
+    bb = 1;
+  } else if (p->flags & ATTN_SCHED_UNTILED) {
+    bn = rn = 0;
+    bb = 1;
+  }
   if (block_m) *block_m = attn::kFwdBlockM;
-  if (block_n) *block_n = attn::kFwdBlockN;
-  if (round_n) *round_n = attn::kFwdRoundN;
+  if (block_n) *block_n = bn;
+  if (round_n) *round_n = rn;
   if (chunk) *chunk = attn::kMfmaK;
+  if (block_bf16) *block_bf16 = bb;
   return ATTN_OK;
 }
 
@@ -136,8 +147,12 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.beta = p->beta;
   a.tie_eps = p->tie_eps;
   a.shift_eps = p->shift_eps;
-  return hip_status(attn::launch_fwd(a, p->head_dim, (p->flags & ATTN_CAUSAL) != 0,
-                                     guard_of(p->flags), (p->flags & ATTN_OBAR_FP32) != 0,
+  const bool causal = (p->flags & ATTN_CAUSAL) != 0, obar_f32 = (p->flags & ATTN_OBAR_FP32) != 0;
+  if (p->flags & ATTN_SCHED_MASK)
+    return hip_status(attn::launch_fwd_block(a, p->head_dim, causal, guard_of(p->flags), obar_f32,
+                                             (p->flags & ATTN_SCHED_UNTILED) != 0,
+                                             (hipStream_t)stream));
+  return hip_status(attn::launch_fwd(a, p->head_dim, causal, guard_of(p->flags), obar_f32,
                                      (hipStream_t)stream));
 }
 

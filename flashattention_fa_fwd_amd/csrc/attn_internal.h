@@ -21,6 +21,8 @@ enum Guard { kGuardNone = 0, kGuardBeta = 1, kGuardEps = 2 };
 constexpr int kFwdBlockM = 128;
 constexpr int kFwdBlockN = 64;
 constexpr int kFwdRoundN = 512;
+// Block size of the FA2-as-tensor-operations schedule (attn_fwd_block.hip).
+constexpr int kFwdOpsBlockN = 512;
 // Products per matrix instruction along every contraction.
 constexpr int kMfmaK = 16;
 
@@ -80,6 +82,8 @@ __device__ __forceinline__ void xcd_map(int L, int heads, int& head, int& blk) {
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
                       hipStream_t s);
+hipError_t launch_fwd_block(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
+                            bool untiled, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool causal, bool delta_dp, hipStream_t s);
 

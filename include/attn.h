@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -46,6 +46,10 @@ extern "C" {
 #define ATTN_GUARD_MASK 0x6u
 #define ATTN_OBAR_FP32 0x8u       /* keep Ō in fp32 (default: bf16 per block)   */
 #define ATTN_DELTA_DP 0x10u       /* backward: delta = rowsum(dP∘P), not dO∘O   */
+/* forward rounding schedule (at most one; default: the streaming kernel) */
+#define ATTN_SCHED_FA2_OPS 0x20u  /* 512-key blocks, bf16 block product P̄V     */
+#define ATTN_SCHED_UNTILED 0x40u  /* one block holding the whole row            */
+#define ATTN_SCHED_MASK 0x60u
 
 /* per-row flag bits written by attn_fwd */
 #define ATTN_ROW_TIE 0x1u           /* the row maximum recurs within tie_eps   */
@@ -72,7 +76,7 @@ typedef struct {
   float tie_eps;     /* tie window, >= 0: tie iff fl32(r - r2) <= tie_eps    */
   float shift_eps;   /* eps-guard extra shift, > 0 (the pages use 2^-5)      */
   uint32_t flags;    /* ATTN_CAUSAL | one ATTN_GUARD_* | ATTN_OBAR_FP32 |
-                        ATTN_DELTA_DP                                        */
+                        ATTN_DELTA_DP | one ATTN_SCHED_*                     */
 } attn_params;
 
 /*
@@ -96,6 +100,16 @@ typedef struct {
  *   obar_out [B,Hq,N,d]: final Ō, bf16 (or fp32 with ATTN_OBAR_FP32) (nullable)
  *   row_max [B,Hq,N] fp32: r, the row maximum of t          (nullable)
  * row_m and row_l are what attn_bwd needs to recompute P = exp(t - m)/ℓ.
+ * Other schedules (the rest as above):
+ *   ATTN_SCHED_FA2_OPS: FlashAttention-2 as tensor operations, the
+ *     implementation the pages analyse ([R] "Points to doubt": block size
+ *     512, the block product P̄V kept in bf16): per 512-key block the
+ *     decision and shift over the block, then B = sum P̄_bf16 V (fp32) and
+ *     Ō = bf16(cŌ + bf16(B)).
+ *   ATTN_SCHED_UNTILED: one block per row ([S] "Key claims": disabling
+ *     tiling still fails): the shift from all the row's keys, Ō =
+ *     bf16(sum P̄_bf16 V) rounded once.
+ * attn_schedule() reports each schedule's block_n / round_n.
  */
 int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
              void* o, float* row_m, float* row_l, uint8_t* row_flags,
@@ -153,13 +167,15 @@ int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void
 /*
  * attn_schedule -- the rounding schedule attn_fwd uses for these params, so
  * that a reference can replay it: block_m query rows per workgroup, block_n
- * keys per streaming step (tie decision and shift), round_n keys per bf16
- * rounding of Ō (bf16 mode), chunk = products per matrix instruction along
- * each contraction.  Returns ATTN_OK or an error code for invalid params.
+ * keys per streaming step (tie decision and shift; 0 = the whole row),
+ * round_n keys per bf16 rounding of Ō (bf16 mode; 0 = the whole row),
+ * chunk = products per matrix instruction along each contraction,
+ * block_bf16 = 1 when each block's product is rounded to bf16 before it is
+ * added to Ō.  Returns ATTN_OK or an error code for invalid params.
  * Pointers may be NULL.
  */
 int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n,
-                  int32_t* round_n, int32_t* chunk);
+                  int32_t* round_n, int32_t* chunk, int32_t* block_bf16);
 
 const char* attn_strerror(int code);
 int attn_abi_version(void);

@@ -43,6 +43,7 @@ class _Schedule(ctypes.Structure):
         ("obar_fp32", ctypes.c_int32), ("certify", ctypes.c_int32),
         ("ftz", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("chunk_err", ctypes.c_double), ("exp_rel_err", ctypes.c_double),
+        ("block_bf16", ctypes.c_int32),
     ]
 
 
@@ -83,6 +84,8 @@ class Schedule:
     terms (error model in oracle.c, chain_bound), scaled by the safety factor
     chunk_err; chunk=0 falls back to the any-order fp32 bound.
     exp_rel_err: relative error bound of the kernel's exp.
+    block_bf16: bf16 mode rounds each block's product sum to bf16 before it is
+    added to Ō (FA2 as tensor operations; needs round_n == block_n).
     """
     block_n: int = 64
     round_n: int = 0
@@ -92,11 +95,12 @@ class Schedule:
     chunk: int = 16
     chunk_err: float = 2.0
     exp_rel_err: float = 2.0 ** -22
+    block_bf16: bool = False
 
     def c(self) -> _Schedule:
         return _Schedule(self.block_n, self.round_n, int(bool(self.obar_fp32)),
                          int(bool(self.certify)), int(bool(self.ftz)),
-                         self.chunk, self.chunk_err, self.exp_rel_err)
+                         self.chunk, self.chunk_err, self.exp_rel_err, int(bool(self.block_bf16)))
 
 
 def build(verbose: bool = False) -> str:

@@ -1048,6 +1048,27 @@ static void emu_head(void* c, int32_t item) {
           terms[j - j0] = pb[j - j0] * vv; /* exact: 8-bit x 8-bit mantissas */
           vmax = fmax(vmax, fabs(vv));
         }
+        if (sc->block_bf16 && !sc->obar_fp32) {
+          /* the block's own product sum, rounded to bf16, then added to the
+           * rescaled Ō and rounded again (every block is a rounding point) */
+          dd_t bacc = {0.0, 0.0};
+          for (int32_t j = 0; j < nt; ++j) dd_add(&bacc, terms[j]);
+          double bexact = bacc.hi + bacc.lo;
+          double bb = cert_on ? chain_bound(sc, 0.0, terms, nt) + flush_slack * vmax : 0.0;
+          uint16_t bh = dd_to_bf16(bacc);
+          double bv = (double)orc_f32_from_bf16(bh);
+          dd_t sum = {0.0, 0.0};
+          dd_add(&sum, ob[f]);
+          dd_add(&sum, bv);
+          double sexact = sum.hi + sum.lo;
+          uint16_t hb = dd_to_bf16(sum);
+          if (!dec_cert || !val_cert || orc_bf16_boundary_distance(bexact) <= bb ||
+              orc_bf16_boundary_distance(sexact) <= obb[f] + 2.0 * U24 * fabs(sexact))
+            oc[f] = 0;
+          ob[f] = (double)orc_f32_from_bf16(hb);
+          obb[f] = 0.0;
+          continue;
+        }
         if (cert_on) obb[f] += chain_bound(sc, ob[f], terms, nt) + flush_slack * vmax;
         dd_t acc = {0.0, 0.0};
         dd_add(&acc, ob[f]);

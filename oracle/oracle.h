@@ -69,6 +69,12 @@ typedef struct {
   int32_t chunk;
   double chunk_err;
   double exp_rel_err;     /* bound on the relative error of the kernel's exp   */
+  /* bf16 mode, 1: at each rounding point the product sum of the keys since
+   * the previous one is itself rounded to bf16 and then added to the
+   * (rescaled) Ō, the sum rounded again -- FA2 written as tensor operations
+   * that keep the block product P̄V in bf16 ([R] "Points to doubt": the
+   * analysed implementation, block size 512).  Needs round_n == block_n.   */
+  int32_t block_bf16;
 } orc_schedule;
 
 int orc_version(void);

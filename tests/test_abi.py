@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 5
+    assert fa.attn_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -43,7 +43,15 @@ def test_version_and_strings(L):
 
 def test_schedule(L):
     p = fa.make_params(1, 1, 1, 128, 64)
-    assert fa.attn_schedule(p) == dict(block_m=128, block_n=64, round_n=512, chunk=16)
+    assert fa.attn_schedule(p) == dict(block_m=128, block_n=64, round_n=512, chunk=16, block_bf16=0)
+    p = fa.make_params(1, 1, 1, 128, 64, schedule="fa2_ops")
+    assert fa.attn_schedule(p) == dict(block_m=128, block_n=512, round_n=512, chunk=16, block_bf16=1)
+    p = fa.make_params(1, 1, 1, 128, 64, schedule="untiled")
+    assert fa.attn_schedule(p) == dict(block_m=128, block_n=0, round_n=0, chunk=16, block_bf16=1)
+    p.flags |= fa.SCHED_FA2_OPS  # two schedules at once
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    with pytest.raises(ValueError):
+        fa.make_params(1, 1, 1, 64, 64, schedule="blocked")
 
 
 FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced

@@ -145,3 +145,77 @@ def test_repeat_is_deterministic():
     b = _run_fwd(x, "beta")
     for key in ("o", "row_m", "row_l", "row_flags", "obar"):
         assert torch.equal(a[key], b[key]), key
+
+
+# ---- the other rounding schedules: FA2 as tensor operations (512-key
+# blocks, bf16 block product; [R] "Points to doubt") and no tiling (one
+# block a row; [S] "Key claims"), against the oracle replaying the schedule
+# that attn_schedule reports for them
+
+SCHED_CASES = [  # name, shape (B, Hq, Hkv, N, d, causal) for the ragged ones
+    ("tiny", None), ("ragged", (1, 2, 1, 1100, 64, True)), ("ragged", (2, 4, 2, 600, 128, False)),
+    ("ragged", (1, 1, 1, 1, 64, True)),
+]
+
+
+@pytest.mark.parametrize("sched", ["fa2_ops", "untiled"])
+@pytest.mark.parametrize("guard", ["none", "beta", "eps"])
+@pytest.mark.parametrize("name,shape", SCHED_CASES)
+def test_other_schedules_bit_exact(sched, guard, name, shape):
+    if name == "ragged":
+        B, Hq, Hkv, N, d, causal = shape
+        wl = W.Workload("ragged", B, Hq, Hkv, N, d, causal, 1.0, 1.0, "const", -0.3,
+                        4.0 if N > 2 else 0.0, 0.1, 0.0, 16.0, 81)
+        x = W.make_custom(wl)
+    else:
+        x = make(name)
+        wl = x["workload"]
+    p = problem(wl, guard)
+    sc = schedule(p, sched=sched)
+    e = orc.fwd_emu(p, sc, x["q"], x["k"], x["v"], nthreads=threads())
+    o64, _ = orc.fwd_f64(p, x["q"], x["k"], x["v"], nthreads=threads())
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    r = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard, schedule=sched, return_obar=True,
+                    return_row_max=True)
+    torch.cuda.synchronize()
+    flags = r["row_flags"].cpu().numpy()
+    fc = e["flag_cert"].astype(bool)
+    assert np.array_equal(flags[fc], e["flags"][fc])
+    errs = check_o(f32(r["o"]), o64, e["o"], False)
+    assert np.allclose(r["row_m"].cpu().numpy()[fc], e["m"][fc], rtol=1e-6, atol=1e-6)
+    ob_gpu = bits(r["obar"])
+    ob_emu = orc.bf16_from_f32(e["obar"].astype(np.float32))
+    cert = e["obar_cert"].astype(bool)
+    assert np.array_equal(ob_gpu[cert], ob_emu[cert])
+    rows = np.broadcast_to(fc[..., None], cert.shape)
+    unc = ~cert & rows
+    # uncertified elements: distance in bf16 steps at the larger magnitude
+    a_, b_ = f32(r["obar"])[unc].astype(np.float64), e["obar"][unc]
+    steps = np.abs(a_ - b_) / np.array([orc.bf16_ulp(max(abs(u), abs(w))) for u, w in zip(a_, b_)] or [1.0])
+    if name == "tiny":  # one block: one (double) rounding apart at most
+        assert np.all(steps <= 1.0 + 1e-9)
+    report(f"schedule {sched} {name} {shape or ''} {guard}", ties=int((flags & 1).sum()),
+           cert=f"{cert.mean():.3f}", uncertified_differing=int((ob_gpu[unc] != ob_emu[unc]).sum()),
+           max_steps=f"{steps.max() if steps.size else 0:.0f}", **errs)
+
+
+@pytest.mark.parametrize("sched", ["fa2_ops", "untiled"])
+def test_other_schedules_full_size(sched):
+    """GPT-2 Small, sampled heads: O against FP64 and the replayed schedule."""
+    x = make("gpt2s")
+    wl = x["workload"]
+    p = problem(wl, "beta")
+    heads = [1, 150]
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    r = fa.attn_fwd(q, k, v, causal=True, guard="beta", schedule=sched, return_obar=True)
+    torch.cuda.synchronize()
+    shp = (-1, wl.seqlen, wl.head_dim)
+    e = orc.fwd_emu(p, schedule(p, sched=sched), x["q"], x["k"], x["v"], heads=heads,
+                    nthreads=threads())
+    o64 = orc.fwd_f64(p, x["q"], x["k"], x["v"], heads=heads, nthreads=threads())[0].reshape(shp)[heads]
+    errs = check_o(f32(r["o"]).reshape(shp)[heads], o64, e["o"].reshape(shp)[heads], False)
+    cert = e["obar_cert"].reshape(shp)[heads].astype(bool)
+    ob_gpu = bits(r["obar"]).reshape(shp)[heads]
+    ob_emu = orc.bf16_from_f32(e["obar"].astype(np.float32)).reshape(shp)[heads]
+    assert np.array_equal(ob_gpu[cert], ob_emu[cert])
+    report(f"schedule {sched} gpt2s beta", cert=f"{cert.mean():.3f}", **errs)

@@ -24,17 +24,18 @@ from _util import dev, make, problem, report, schedule, threads
 pytestmark = pytest.mark.gpu
 
 
-def _signed_errors(name, guard, obar_fp32, heads):
+def _signed_errors(name, guard, obar_fp32, heads, sched="stream"):
     x = make(name)
     wl = x["workload"]
     p = problem(wl, guard)
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    r = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard, obar_fp32=obar_fp32, return_obar=True)
+    r = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard, obar_fp32=obar_fp32, return_obar=True,
+                    schedule=sched)
     torch.cuda.synchronize()
     ob = r["obar"].float().cpu().numpy().astype(np.float64)
     shp = (-1, wl.seqlen, wl.head_dim)
     ob = ob.reshape(shp)[heads]
-    st = orc.row_stats(p, x["q"], x["k"], schedule(p), heads=heads, nthreads=threads())
+    st = orc.row_stats(p, x["q"], x["k"], schedule(p, sched=sched), heads=heads, nthreads=threads())
     ob64, l64 = orc.obar_f64(p, x["q"], x["k"], x["v"], st["m"], heads=heads, nthreads=threads())
     ob64 = ob64.reshape(shp)[heads]
     l64 = l64.reshape(-1, wl.seqlen)[heads]
@@ -72,3 +73,23 @@ def test_bias_unguarded_negative_guarded_zero(name, heads):
     assert abs(res[("beta", False)]["neg"][0]) <= 1e-4
     assert abs(res[("none", True)]["neg"][0]) <= 1e-4
     assert abs(res[("beta", True)]["neg"][0]) <= 1e-4
+
+
+@pytest.mark.parametrize("sched", ["fa2_ops", "untiled"])
+def test_bias_under_other_schedules(sched):
+    """The same finding under the analysed implementation's schedule (FA2 as
+    tensor operations, 512-key blocks, bf16 block product; [R] "Points to
+    doubt") and without tiling ([S] "Key claims": disabling tiling still
+    fails): unguarded bf16 Ō is biased negative on the negative-dominated
+    features of tie rows, the beta guard removes it."""
+    heads = list(range(0, 192, 12))
+    res = {}
+    for guard in ("none", "beta"):
+        err, tie, neg = _signed_errors("gpt2s", guard, False, heads, sched)
+        sel_neg = tie[..., None] & neg[:, None, :]
+        res[guard] = _stats(err[sel_neg])
+        report(f"signed error gpt2s schedule={sched} guard={guard}",
+               neg=f"{res[guard][0]:+.3e}±{res[guard][1]:.1e} (n={res[guard][2]})")
+    m, se, n = res["none"]
+    assert n > 10000 and m < -3 * se
+    assert abs(res["beta"][0]) <= 1e-4
