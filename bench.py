@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # report says null.
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
-        "sources_sha256": "b32212824f6a7dd85f23bff89d33c4b2db2febbb2d6f77bbd3cbc04087df35b8",
-        "fetch_kib": 64250.0, "write_kib": 51670.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "26de40d7280dc871b9a427fce4ea09b032051d52bfcebdf9d17cb78bf4072700",
+        "fetch_kib": 63959.0, "write_kib": 50892.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
@@ -127,23 +127,16 @@ def main():
     ms_step = timed(step, args.steps, args.warmup)
     print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations: the same steps again, with HIP events on the
-    # launch stream between the kernels (attn_bwd is its two stages: dQ, dK/dV)
+    # ---- per-kernel durations: each of the step's launches (attn_bwd is its
+    # two stages, dQ then dK/dV) repeated back to back between HIP events on
+    # the launch stream, as a kernel trace averages them
     delta = bout["delta"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        e = ev[i]
-        e[0].record(stream)
-        fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
-        e[1].record(stream)
-        fa.attn_bwd_dq(p, q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], bout["dq"], delta)
-        e[2].record(stream)
-        fa.attn_bwd_dkdv(p, q, k, v, do, fout["row_m"], fout["row_l"], delta, bout["dk"], bout["dv"])
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    ms_fwd, ms_dq, ms_dkdv = (sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j in range(3))
     n_rep = max(20, args.steps)
+    ms_fwd = timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw), n_rep, 3)
+    ms_dq = timed(lambda: fa.attn_bwd_dq(p, q, k, v, fout["o"], do, fout["row_m"], fout["row_l"],
+                                         bout["dq"], delta), n_rep, 3)
+    ms_dkdv = timed(lambda: fa.attn_bwd_dkdv(p, q, k, v, do, fout["row_m"], fout["row_l"], delta,
+                                             bout["dk"], bout["dv"]), n_rep, 3)
     other = "none" if args.guard != "none" else "beta"
     fo2 = {}
     ms_fwd_other = timed(lambda: fa.attn_fwd(q, k, v, causal=wl.causal, guard=other, out=fo2), n_rep, 3)
