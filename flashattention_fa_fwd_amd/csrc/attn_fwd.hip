@@ -148,17 +148,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
     const uint16_t* vs = Vs[cur];
 
     // ---- S^T = K Q^T for the 64 keys: two 32-key blocks
+    // (the two blocks' chains interleaved: consecutive products are
+    // independent)
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *(const bf16x8*)(&ks[ka_off[kb][t]]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
       }
-    }
     // key of s[kb][i] in this lane: j0 + 32kb + 8(i/4) + 4*half + i%4; only
     // the block holding the diagonal (causal) or the sequence end masks
     const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > q0);
@@ -227,11 +230,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
         pf[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
       }
 
-    // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order
+    // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order (the feature
+    // blocks' chains interleaved)
 #pragma unroll
-    for (int f = 0; f < FB; ++f) {
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int f = 0; f < FB; ++f) {
         // A = V^T: feature 32f + l32, keys 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
         const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
         const bf16x8 vf = frag2(lds_read_tr(vs + o0), lds_read_tr(vs + o1));
