@@ -175,9 +175,9 @@ __device__ __forceinline__ void dkdv_step(
     // the k index 8*half + j of product t is row 16t + 8(j/4) + 4*half +
     // j%4, so the B operand is two transpose reads of 4 rows each
 #pragma unroll
-    for (int f = 0; f < FB; ++f) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int f = 0; f < FB; ++f) {
         // rows 16t + trow and 16t + 8 + trow (the swizzle ignores bit 4 and up)
         const int o0 = tb_off[f][0] + 16 * t * D, o1 = tb_off[f][1] + 16 * t * D;
         const bf16x8 gb = frag2(lds_read_tr(gs + o0), lds_read_tr(gs + o1));
@@ -326,20 +326,21 @@ __device__ __forceinline__ void dq_step(
     // register i of block kb = key j0 + 32kb + 8(i/4) + 4*half + i%4
     f32x16 sv[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sv[kb][i] = 0.0f;
         dp[kb][i] = 0.0f;
       }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *(const bf16x8*)(&ks[ka_off[kb][t]]);
         sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sv[kb], 0, 0, 0);
         const bf16x8 vf = *(const bf16x8*)(&vs[ka_off[kb][t]]);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[t], dp[kb], 0, 0, 0);
       }
-    }
     // ---- dS = P (dP - delta), P = exp2(s * alpha*log2(e) - lse2)
     float dsv[2][16];
 #pragma unroll
@@ -375,9 +376,9 @@ __device__ __forceinline__ void dq_step(
                                                     pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])));
     }
 #pragma unroll
-    for (int f = 0; f < FB; ++f) {
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int f = 0; f < FB; ++f) {
         // keys 16t + trow and 16t + 8 + trow (the swizzle ignores bit 4 and up)
         const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
         const bf16x8 kt = frag2(lds_read_tr(ks + o0), lds_read_tr(ks + o1));
