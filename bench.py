@@ -145,6 +145,15 @@ def main():
     bo2 = {}
     ms_bwd_dp = timed(lambda: fa.attn_bwd(q, k, v, None, do, fout["row_m"], fout["row_l"],
                                           delta="dp_p", out=bo2, **kw), n_rep, 3)
+    # the forward's study variants at the same shape: the FP8 product (row
+    # or fixed operand scale) and the two other rounding schedules
+    variants = {}
+    for name, vkw in (("pv_fp8_row", dict(pv_fp8="row")), ("pv_fp8_fixed", dict(pv_fp8="fixed")),
+                      ("sched_fa2_ops", dict(schedule="fa2_ops")), ("sched_untiled", dict(schedule="untiled"))):
+        fo3 = {}
+        variants[name] = round(timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fo3, **vkw, **kw),
+                                     n_rep, 3), 5)
+    print(f"[bench] forward variants (ms): {variants}", file=sys.stderr, flush=True)
     print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_dq {ms_dq:.4f}, bwd_dkdv {ms_dkdv:.4f}; "
           f"fwd with guard={other}: {ms_fwd_other:.4f}; bwd with delta=rowsum(dP*P): "
           f"{ms_bwd_dp:.4f}", file=sys.stderr, flush=True)
@@ -199,6 +208,7 @@ def main():
         "kernel_ms": {"attn_fwd": round(ms_fwd, 5), "bwd_dq": round(ms_dq, 5),
                       "bwd_dkdv": round(ms_dkdv, 5)},
         "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
+        "fwd_ms_variants": variants,
         "bwd_ms_delta": {"rowsum(dO*O)": round(ms_dq + ms_dkdv, 5), "rowsum(dP*P)": round(ms_bwd_dp, 5)},
         "roofline": {
             "kernel": dom,

@@ -30,6 +30,19 @@
 //     O^T = V^T P̄^T, whose accumulator has the same lane-to-row ownership,
 //     so the rescale by exp(m_old - m) is a per-lane scalar; the A operand
 //     V^T comes from the row-major V tile through the LDS transpose read.
+//
+// FP8 variant of the P̄V product (the pages leave open how the bias behaves
+// with fewer mantissa bits: [R] "Open questions"): P̄ * 2^k and V are rounded
+// to OCP E4M3 (v_cvt_pk_fp8_f32, round to nearest even) and multiplied on
+// v_mfma_f32_32x32x16_fp8_fp8 with the same operand layout; the accumulator
+// holds 2^k Ō, exact scaling through every fp32 and bf16 rounding, and the
+// scale is taken out at the end.  k is per row and per step: 7 -
+// floor((r - m) log2 e), which puts the row's largest P̄ = exp(r - m) in
+// [128, 256) -- the top binade below E4M3's 448 -- whatever the shift (the
+// beta guard's shift makes that P̄ as small as exp(-(beta-1) r), below E4M3's
+// range for a fixed scale); when k changes the accumulator is rescaled by
+// the power of two along with exp(m_old - m).  A fixed k = 8 is the other
+// option.  ℓ stays the sum of the fp32 P̄.
 #include "attn_device.h"
 
 namespace attn {
@@ -44,6 +57,17 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// Four bf16 values (two per word, low half first) to four E4M3 bytes in the
+// same order: bf16 -> fp32 is exact, the conversion rounds to nearest even.
+__device__ __forceinline__ uint32_t fp8x4_from_bf16x4(uint2 w) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u), r, true);
+  return (uint32_t)r;
+}
+
+// 2^e as a float for -126 <= e <= 127 (built from the exponent field).
+__device__ __forceinline__ float pow2i(int e) { return __int_as_float((127 + e) << 23); }
+
 // Top-two merge of (a, a2) and (b, b2), each with first >= second; the
 // result keeps multiset semantics (equal maxima give r2 == r).
 __device__ __forceinline__ void top2_merge(float& a, float& a2, float b, float b2) {
@@ -52,8 +76,12 @@ __device__ __forceinline__ void top2_merge(float& a, float& a2, float b, float b
   a2 = fmaxf(lo, fmaxf(a2, b2));
 }
 
-template <int D, bool CAUSAL, int GUARD, bool OBAR_F32>
+template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, bool PV_FP8>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs a) {
+  // every fp32 operation as written: no multiply is fused into a later add
+  // (a fused alpha*R - m would turn r - m = 0 into the rounding error of
+  // alpha*R and move decisions taken on it); fused steps are explicit fmaf
+#pragma clang fp contract(off)
   constexpr int BN = kFwdBlockN;
   constexpr int NT = D / kMfmaK; // matrix steps along d for S
   constexpr int FB = D / 32;     // 32-feature blocks of O^T
@@ -101,6 +129,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
   float m = 0.0f, m2 = 0.0f, rt = -INFINITY;
   float lsum = 0.0f;
   bool tie = false;
+  int pk = 8;  // FP8 product: exponent of the operand scale 2^k
 
   const int kend = CAUSAL ? min(N, (mb + 1) * kFwdBlockM) : N;
   const bool wave_live = q0 < N;
@@ -207,27 +236,51 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
 
     // ---- rescale by c = exp(m_old - m_new); c = 1 exactly where the shift
     // did not move (and on the first step), so multiplying unconditionally
-    // changes nothing there and keeps the accumulator in one register set
+    // changes nothing there and keeps the accumulator in one register set.
+    // FP8 product: the operand scale 2^k for this step (r - m <= 0 under
+    // every guard, so k >= 7), the accumulator moved to it exactly
     {
       const float c = (j0 == 0 || mn == m) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
       lsum *= c;
+      float co = c;
+      if (PV_FP8) {
+        int kn = 8;
+        if (!a.pv_fixed_scale) kn = 7 - (int)fmaxf(floorf((rt - mn) * kLog2e), -113.0f);
+        co = c * pow2i(kn - pk);  // exact: a power of two
+        pk = kn;
+      }
 #pragma unroll
       for (int f = 0; f < FB; ++f)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[f][i] *= c;
+        for (int i = 0; i < 16; ++i) oacc[f][i] *= co;
       m = mn;
     }
+    const float psc = PV_FP8 ? pow2i(pk) : 1.0f;
     m2 = m * kLog2e;
 
-    // ---- P̄ = exp(t - m) = exp2(s * alpha*log2e - m*log2e); row sum; bf16
+    // ---- P̄ = exp(t - m) = exp2(s * alpha*log2e - m*log2e); row sum; the
+    // matrix operand in bf16, or 2^k P̄ in E4M3
     bf16x8 pf[4];
+    uint32_t pf8[4][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], a.c1, -m2));
-        lsum += p;
-        pf[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], a.c1, -m2));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], a.c1, -m2));
+        lsum += p0;
+        lsum += p1;
+        const int t = 2 * kb + (i >> 3), u = i & 7;
+        if (PV_FP8) {
+          uint32_t& w = pf8[t][u >> 2];
+          if (u & 2)
+            w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p0 * psc, p1 * psc, (int)w, true);
+          else
+            w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p0 * psc, p1 * psc, 0, false);
+        } else {
+          pf[t][u] = (__bf16)p0;
+          pf[t][u + 1] = (__bf16)p1;
+        }
       }
 
     // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order (the feature
@@ -238,8 +291,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
       for (int f = 0; f < FB; ++f) {
         // A = V^T: feature 32f + l32, keys 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
         const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
-        const bf16x8 vf = frag2(lds_read_tr(vs + o0), lds_read_tr(vs + o1));
-        oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], oacc[f], 0, 0, 0);
+        const uint2 v0 = lds_read_tr(vs + o0), v1 = lds_read_tr(vs + o1);
+        if (PV_FP8) {
+          const long va = (long)(((uint64_t)fp8x4_from_bf16x4(v1) << 32) | fp8x4_from_bf16x4(v0));
+          const long pb = (long)(((uint64_t)pf8[t][1] << 32) | pf8[t][0]);
+          oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(va, pb, oacc[f], 0, 0, 0);
+        } else {
+          oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag2(v0, v1), pf[t], oacc[f], 0, 0, 0);
+        }
       }
     }
     // bf16 mode: round the accumulator after every kFwdRoundN keys and
@@ -268,6 +327,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
   // ---- epilogue: O = bf16(Ō / ℓ); row outputs
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (qrow >= N) return;
+  if (PV_FP8) {
+    const float un = pow2i(-pk);  // exact
+#pragma unroll
+    for (int f = 0; f < FB; ++f)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[f][i] *= un;
+  }
   uint16_t* orow = a.o + qoff + (size_t)qrow * D;
 #pragma unroll
   for (int f = 0; f < FB; ++f)
@@ -303,35 +369,44 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
   }
 }
 
-template <int D, bool CAUSAL, int GUARD, bool OBAR_F32>
+template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, bool PV_FP8>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
   dim3 grid((unsigned)(nmb * a.Hq * a.B));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, GUARD, OBAR_F32>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, GUARD, OBAR_F32, PV_FP8>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int GUARD>
+template <int D, bool CAUSAL, int GUARD, bool PV_FP8>
 hipError_t launch_o(const FwdArgs& a, bool obar_f32, hipStream_t s) {
-  return obar_f32 ? launch_t<D, CAUSAL, GUARD, true>(a, s) : launch_t<D, CAUSAL, GUARD, false>(a, s);
+  return obar_f32 ? launch_t<D, CAUSAL, GUARD, true, PV_FP8>(a, s)
+                  : launch_t<D, CAUSAL, GUARD, false, PV_FP8>(a, s);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PV_FP8>
 hipError_t launch_g(const FwdArgs& a, int guard, bool obar_f32, hipStream_t s) {
   switch (guard) {
-    case kGuardBeta: return launch_o<D, CAUSAL, kGuardBeta>(a, obar_f32, s);
-    case kGuardEps: return launch_o<D, CAUSAL, kGuardEps>(a, obar_f32, s);
-    default: return launch_o<D, CAUSAL, kGuardNone>(a, obar_f32, s);
+    case kGuardBeta: return launch_o<D, CAUSAL, kGuardBeta, PV_FP8>(a, obar_f32, s);
+    case kGuardEps: return launch_o<D, CAUSAL, kGuardEps, PV_FP8>(a, obar_f32, s);
+    default: return launch_o<D, CAUSAL, kGuardNone, PV_FP8>(a, obar_f32, s);
   }
+}
+
+template <bool PV_FP8>
+hipError_t launch_d(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32, hipStream_t s) {
+  if (d == 64)
+    return causal ? launch_g<64, true, PV_FP8>(a, guard, obar_f32, s)
+                  : launch_g<64, false, PV_FP8>(a, guard, obar_f32, s);
+  return causal ? launch_g<128, true, PV_FP8>(a, guard, obar_f32, s)
+                : launch_g<128, false, PV_FP8>(a, guard, obar_f32, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32, bool pv_fp8,
                       hipStream_t s) {
-  if (d == 64)
-    return causal ? launch_g<64, true>(a, guard, obar_f32, s) : launch_g<64, false>(a, guard, obar_f32, s);
-  return causal ? launch_g<128, true>(a, guard, obar_f32, s) : launch_g<128, false>(a, guard, obar_f32, s);
+  return pv_fp8 ? launch_d<true>(a, d, causal, guard, obar_f32, s)
+                : launch_d<false>(a, d, causal, guard, obar_f32, s);
 }
 
 }  // namespace attn

@@ -40,6 +40,10 @@ __device__ __forceinline__ void top2_merge(float& a, float& a2, float b, float b
 
 template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, bool UNTILED>
 __global__ __launch_bounds__(kThreads) void fwd_block_kernel(FwdArgs a) {
+  // every fp32 operation as written: no multiply is fused into a later add
+  // (a fused alpha*R - m would turn r - m = 0 into the rounding error of
+  // alpha*R and move decisions taken on it); fused steps are explicit fmaf
+#pragma clang fp contract(off)
   constexpr int BN = kFwdBlockN;  // keys per tile
   constexpr int NT = D / kMfmaK;
   constexpr int FB = D / 32;

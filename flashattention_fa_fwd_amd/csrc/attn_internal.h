@@ -40,6 +40,7 @@ struct FwdArgs {
   float alpha;     // softmax scale (fp32)
   float c1;        // fl32(alpha * log2(e))
   float beta, tie_eps, shift_eps;
+  int pv_fixed_scale;  // FP8 product: 1 = operand scale fixed at 2^8
 };
 
 struct BwdArgs {
@@ -81,7 +82,7 @@ __device__ __forceinline__ void xcd_map(int L, int heads, int& head, int& blk) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
-                      hipStream_t s);
+                      bool pv_fp8, hipStream_t s);
 hipError_t launch_fwd_block(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
                             bool untiled, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s);

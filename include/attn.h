@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -50,6 +50,9 @@ extern "C" {
 #define ATTN_SCHED_FA2_OPS 0x20u  /* 512-key blocks, bf16 block product P̄V     */
 #define ATTN_SCHED_UNTILED 0x40u  /* one block holding the whole row            */
 #define ATTN_SCHED_MASK 0x60u
+/* forward: the P̄V product in FP8 E4M3 (streaming schedule only)          */
+#define ATTN_PV_FP8 0x80u
+#define ATTN_PV_FP8_FIXED 0x100u  /* with ATTN_PV_FP8: operand scale 2^8     */
 
 /* per-row flag bits written by attn_fwd */
 #define ATTN_ROW_TIE 0x1u           /* the row maximum recurs within tie_eps   */
@@ -76,7 +79,8 @@ typedef struct {
   float tie_eps;     /* tie window, >= 0: tie iff fl32(r - r2) <= tie_eps    */
   float shift_eps;   /* eps-guard extra shift, > 0 (the pages use 2^-5)      */
   uint32_t flags;    /* ATTN_CAUSAL | one ATTN_GUARD_* | ATTN_OBAR_FP32 |
-                        ATTN_DELTA_DP | one ATTN_SCHED_*                     */
+                        ATTN_DELTA_DP | one ATTN_SCHED_* | ATTN_PV_FP8 (+
+                        ATTN_PV_FP8_FIXED)                                   */
 } attn_params;
 
 /*
@@ -110,6 +114,19 @@ typedef struct {
  *     tiling still fails): the shift from all the row's keys, Ō =
  *     bf16(sum P̄_bf16 V) rounded once.
  * attn_schedule() reports each schedule's block_n / round_n.
+ * ATTN_PV_FP8 (streaming schedule only; ATTN_E_PARAM with another): the
+ *   open question of the bias with fewer mantissa bits ([R] "Open
+ *   questions").  The matrix operands of Ō's product become
+ *   e4m3(2^k exp(t - m)) and e4m3(V), OCP E4M3 (bias 7, largest 448) rounded
+ *   to nearest even, with k = 7 - floor(fl32(fl32(r - m) * fl32(log2 e)))
+ *   per row and block (r the running maximum, m the block's shift): the
+ *   row's largest P̄ lands in [128, 256).  With ATTN_PV_FP8_FIXED, k = 8.
+ *   The products and their fp32 sums carry 2^k, moved exactly with the
+ *   rescale when k changes and removed before Ō is written or divided by
+ *   ℓ.  Rounding points of Ō, ℓ (fp32 exp values) and the shift are
+ *   unchanged.  V entries must round inside E4M3's range (|V| < 464);
+ *   beyond it the result is undefined.  attn_bwd ignores both flags (it
+ *   recomputes P in fp32 and reads O as given).
  */
 int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
              void* o, float* row_m, float* row_l, uint8_t* row_flags,

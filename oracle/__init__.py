@@ -43,7 +43,7 @@ class _Schedule(ctypes.Structure):
         ("obar_fp32", ctypes.c_int32), ("certify", ctypes.c_int32),
         ("ftz", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("chunk_err", ctypes.c_double), ("exp_rel_err", ctypes.c_double),
-        ("block_bf16", ctypes.c_int32),
+        ("block_bf16", ctypes.c_int32), ("pv_fp8", ctypes.c_int32),
     ]
 
 
@@ -86,6 +86,9 @@ class Schedule:
     exp_rel_err: relative error bound of the kernel's exp.
     block_bf16: bf16 mode rounds each block's product sum to bf16 before it is
     added to Ō (FA2 as tensor operations; needs round_n == block_n).
+    pv_fp8: the P̄V product in FP8 E4M3 (P̄ * 2^k and V rounded to E4M3):
+        False, True / "row" (k per row and block: the row's largest P̄ in
+        [128, 256)) or "fixed" (k = 8).
     """
     block_n: int = 64
     round_n: int = 0
@@ -96,11 +99,13 @@ class Schedule:
     chunk_err: float = 2.0
     exp_rel_err: float = 2.0 ** -22
     block_bf16: bool = False
+    pv_fp8: bool | str = False
 
     def c(self) -> _Schedule:
         return _Schedule(self.block_n, self.round_n, int(bool(self.obar_fp32)),
                          int(bool(self.certify)), int(bool(self.ftz)),
-                         self.chunk, self.chunk_err, self.exp_rel_err, int(bool(self.block_bf16)))
+                         self.chunk, self.chunk_err, self.exp_rel_err, int(bool(self.block_bf16)),
+                         {False: 0, True: 1, "row": 1, "fixed": 2}[self.pv_fp8])
 
 
 def build(verbose: bool = False) -> str:
@@ -152,7 +157,13 @@ def lib():
                                     f32p, f32p, f32p, u8p, u8p, ctypes.c_int32]
         L.orc_obar_f64.argtypes = [pp, u16p, u16p, u16p, f32p, i32p, ctypes.c_int32, f64p, f64p, ctypes.c_int32]
         L.orc_fwd_emu.argtypes = [pp, sp, u16p, u16p, u16p, i32p, ctypes.c_int32,
-                                  f64p, u8p, f64p, f32p, f32p, u8p, u8p, u8p, ctypes.c_int32]
+                                  f64p, u8p, f64p, f64p, f32p, f32p, u8p, u8p, u8p, ctypes.c_int32]
+        L.orc_e4m3_round.argtypes = [ctypes.c_double]
+        L.orc_e4m3_round.restype = ctypes.c_double
+        L.orc_e4m3_ulp.argtypes = [ctypes.c_double]
+        L.orc_e4m3_ulp.restype = ctypes.c_double
+        L.orc_e4m3_boundary_distance.argtypes = [ctypes.c_double]
+        L.orc_e4m3_boundary_distance.restype = ctypes.c_double
         for name in ("orc_fwd_f64", "orc_bwd_f64", "orc_bwd_rows_f64", "orc_row_stats",
                      "orc_obar_f64", "orc_fwd_emu", "orc_bwd_emu", "orc_bwd_rows_emu",
                      "orc_fwd_emu_rows", "orc_delta_dp_rows_f64", "orc_dsum_rows_f64"):
@@ -220,6 +231,26 @@ def bf16_ulp(x: float) -> float:
 
 def bf16_boundary_distance(x: float) -> float:
     return float(lib().orc_bf16_boundary_distance(float(x)))
+
+
+def e4m3_round(x: float) -> float:
+    """x rounded to OCP FP8 E4M3 (nearest, ties to even; NaN past 448)."""
+    return float(lib().orc_e4m3_round(float(x)))
+
+
+def e4m3_ulp(x: float) -> float:
+    return float(lib().orc_e4m3_ulp(float(x)))
+
+
+def e4m3_boundary_distance(x: float) -> float:
+    return float(lib().orc_e4m3_boundary_distance(float(x)))
+
+
+def e4m3_array(x):
+    """Elementwise e4m3_round over an array (float64 result)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = np.frompyfunc(lambda t: lib().orc_e4m3_round(float(t)), 1, 1)
+    return f(x).astype(np.float64)
 
 
 def bf16_round_of_sum(terms) -> tuple[int, float]:
@@ -406,11 +437,12 @@ def obar_f64(p: Problem, q, k, v, m, heads=None, nthreads=None):
 
 
 def fwd_emu(p: Problem, sched: Schedule, q, k, v, heads=None, nthreads=None):
-    """Streaming bf16 emulation: dict of obar, obar_cert, o, m, l, flags,
-    flag_cert, ex (see oracle.h)."""
+    """Streaming bf16 emulation: dict of obar, obar_cert, obar_dev, o, m, l,
+    flags, flag_cert, ex (see oracle.h)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     shp = q.shape[:-1]
     ob = np.zeros(q.shape, np.float64); oc = np.zeros(q.shape, np.uint8)
+    od = np.zeros(q.shape, np.float64)
     o = np.zeros(q.shape, np.float64)
     m = np.zeros(shp, np.float32); l = np.zeros(shp, np.float32)
     fl = np.zeros(shp, np.uint8); fc = np.zeros(shp, np.uint8); ex = np.zeros(shp, np.uint8)
@@ -418,8 +450,9 @@ def fwd_emu(p: Problem, sched: Schedule, q, k, v, heads=None, nthreads=None):
     pc, sc = p.c(), sched.c()
     _check(lib().orc_fwd_emu(ctypes.byref(pc), ctypes.byref(sc), _ptr(q, ctypes.c_uint16),
                              _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16), _ptr(h, ctypes.c_int32), nh,
-                             _ptr(ob, ctypes.c_double), _ptr(oc, ctypes.c_uint8), _ptr(o, ctypes.c_double),
+                             _ptr(ob, ctypes.c_double), _ptr(oc, ctypes.c_uint8), _ptr(od, ctypes.c_double),
+                             _ptr(o, ctypes.c_double),
                              _ptr(m, ctypes.c_float), _ptr(l, ctypes.c_float), _ptr(fl, ctypes.c_uint8),
                              _ptr(fc, ctypes.c_uint8), _ptr(ex, ctypes.c_uint8), _threads(nthreads)),
            "orc_fwd_emu")
-    return dict(obar=ob, obar_cert=oc, o=o, m=m, l=l, flags=fl, flag_cert=fc, ex=ex)
+    return dict(obar=ob, obar_cert=oc, obar_dev=od, o=o, m=m, l=l, flags=fl, flag_cert=fc, ex=ex)

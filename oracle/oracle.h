@@ -75,6 +75,11 @@ typedef struct {
    * that keep the block product P̄V in bf16 ([R] "Points to doubt": the
    * analysed implementation, block size 512).  Needs round_n == block_n.   */
   int32_t block_bf16;
+  /* the P̄V product in FP8 E4M3 -- P̄ * 2^k and V rounded to E4M3 (the
+   * scale undone in the sum, exactly); the products are exact.  1: k = 7 -
+   * floor(fl32(fl32(r - m) * fl32(log2 e))) per row and block (the row's
+   * largest P̄ in [128, 256)); 2: k = 8.  0: bf16 operands.                 */
+  int32_t pv_fp8;
 } orc_schedule;
 
 int orc_version(void);
@@ -87,6 +92,10 @@ void orc_bf16_from_f32_array(const float* x, uint16_t* out, int64_t n);
 void orc_f32_from_bf16_array(const uint16_t* h, float* out, int64_t n);
 double orc_bf16_ulp(double x);             /* spacing of the bf16 grid at |x| */
 double orc_bf16_boundary_distance(double x); /* |x - nearest rounding midpoint| */
+/* ---- FP8 E4M3 (OCP: bias 7, 3 mantissa bits, max 448, no infinities) ---- */
+double orc_e4m3_round(double x);           /* RNE to E4M3 (NaN past 448)      */
+double orc_e4m3_ulp(double x);             /* spacing of the E4M3 grid at |x| */
+double orc_e4m3_boundary_distance(double x);
 /* RNE to bf16 of the exact sum of n doubles (the accumulate-then-round step).
  * *exact_out (nullable) receives the exact sum rounded to double.           */
 uint16_t orc_bf16_round_of_sum(const double* terms, int32_t n, double* exact_out);
@@ -167,6 +176,10 @@ int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
  * points of the schedule, plus certification of every bf16 rounding.
  * Outputs (per query row of the listed heads, in [B,Hq,N(,d)] layout):
  *   obar      final Ō (bf16-valued in bf16 mode), obar_cert 1 = certain
+ *   obar_dev  (nullable) bound on |kernel's final Ō - obar| from the error
+ *             bounds, carried through every rounding point (one step of the
+ *             rounding where it is not certain); +inf on rows whose shift
+ *             decision is uncertain; NaN without certification
  *   o         RNE_bf16(Ō/ℓ) as double
  *   m, l      final shift and fp32 denominator; flags = ORC_ROW_* bits
  *   flag_cert 1 = every streaming tie decision of the row (and its zero-
@@ -174,8 +187,8 @@ int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
  *   ex        ORC_EX_* bits                                                 */
 int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
                 const uint16_t* k, const uint16_t* v, const int32_t* heads,
-                int32_t nheads, double* obar, uint8_t* obar_cert, double* o,
-                float* m, float* l, uint8_t* flags, uint8_t* flag_cert,
+                int32_t nheads, double* obar, uint8_t* obar_cert, double* obar_dev,
+                double* o, float* m, float* l, uint8_t* flags, uint8_t* flag_cert,
                 uint8_t* ex, int32_t nthreads);
 
 /* The same emulation for listed rows only (row rows[i] of query head

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 6
+    assert fa.attn_abi_version() == 7
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -50,6 +50,12 @@ def test_schedule(L):
     assert fa.attn_schedule(p) == dict(block_m=128, block_n=0, round_n=0, chunk=16, block_bf16=1)
     p.flags |= fa.SCHED_FA2_OPS  # two schedules at once
     assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    # the FP8 product: streaming schedule only
+    p = fa.make_params(1, 1, 1, 128, 64, pv_fp8=True)
+    assert fa.attn_schedule(p)["block_n"] == 64
+    for sched in ("fa2_ops", "untiled"):
+        p = fa.make_params(1, 1, 1, 128, 64, schedule=sched, pv_fp8=True)
+        assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
     with pytest.raises(ValueError):
         fa.make_params(1, 1, 1, 64, 64, schedule="blocked")
 
