@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # report says null.
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
-        "sources_sha256": "26de40d7280dc871b9a427fce4ea09b032051d52bfcebdf9d17cb78bf4072700",
-        "fetch_kib": 63959.0, "write_kib": 50892.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "fe69c11057ce8688784dc76b45fed01eabc8d2557655345fb3deaf23fb8b1c28",
+        "fetch_kib": 64490.0, "write_kib": 51502.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
