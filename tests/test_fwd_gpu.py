@@ -219,3 +219,21 @@ def test_other_schedules_full_size(sched):
     ob_emu = orc.bf16_from_f32(e["obar"].astype(np.float32)).reshape(shp)[heads]
     assert np.array_equal(ob_gpu[cert], ob_emu[cert])
     report(f"schedule {sched} gpt2s beta", cert=f"{cert.mean():.3f}", **errs)
+
+
+@pytest.mark.parametrize("obar_fp32", [True, False])
+def test_output_is_the_ieee_quotient(obar_fp32):
+    """O = bf16(fl32(Ō/ℓ)) bit for bit, from the kernel's own Ō (fp32 or bf16)
+    and ℓ, with numpy's IEEE fp32 division: the epilogue's reciprocal-based
+    quotient must equal it on every row (GPT-2 Small, every head)."""
+    x = make("gpt2s")
+    wl = x["workload"]
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    r = fa.attn_fwd(q, k, v, causal=True, guard="beta", obar_fp32=obar_fp32, return_obar=True)
+    torch.cuda.synchronize()
+    ob = f32(r["obar"]).astype(np.float32)
+    l = r["row_l"].cpu().numpy().astype(np.float32)[..., None]
+    want = orc.bf16_from_f32(np.ascontiguousarray(ob / l, dtype=np.float32))
+    got = bits(r["o"])
+    assert np.array_equal(got, want), int((got != want).sum())
+    report(f"O = bf16(Ō/ℓ) {'fp32' if obar_fp32 else 'bf16'} Ō", elements=got.size)
