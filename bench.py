@@ -30,31 +30,31 @@ HBM_PEAK_GBS = 8000.0
 # counter reads for a plain device copy of 256 MiB (FETCH_SIZE reads half the
 # bytes: x2.0; WRITE_SIZE all of them: x1.0).  Summary and commands:
 # profiles/bwd_dkdv_gpt2s_hbm_traffic.md.  The figures hold only for the
-# kernel sources they were taken on (SHA-256 over csrc/); otherwise the
-# report says null.
+# sources of that kernel they were taken on (SHA-256 over the files that
+# define it); otherwise the report says null.
+KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd.hip", "attn_device.h", "attn_internal.h")}
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
-        "sources_sha256": "fe69c11057ce8688784dc76b45fed01eabc8d2557655345fb3deaf23fb8b1c28",
+        "sources_sha256": "42c0702aeafb898b2bab7bd9dd462bfd47798753ba9f9c463071102e345afb87",
         "fetch_kib": 64490.0, "write_kib": 51502.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
 
-def kernel_sources_sha256() -> str:
+def kernel_sources_sha256(kernel: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "flashattention_fa_fwd_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
 def measured_traffic(kernel: str):
     m = MEASURED_TRAFFIC.get(kernel)
-    if m is None or m["sources_sha256"] != kernel_sources_sha256():
+    if m is None or m["sources_sha256"] != kernel_sources_sha256(kernel):
         return None
     return int(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]))
 
