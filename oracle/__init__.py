@@ -43,7 +43,7 @@ class _Schedule(ctypes.Structure):
         ("obar_fp32", ctypes.c_int32), ("certify", ctypes.c_int32),
         ("ftz", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("chunk_err", ctypes.c_double), ("exp_rel_err", ctypes.c_double),
-        ("block_bf16", ctypes.c_int32), ("pv_fp8", ctypes.c_int32),
+        ("block_bf16", ctypes.c_int32), ("pv_fp8", ctypes.c_int32), ("pv_mxfp4", ctypes.c_int32),
     ]
 
 
@@ -89,6 +89,8 @@ class Schedule:
     pv_fp8: the P̄V product in FP8 E4M3 (P̄ * 2^k and V rounded to E4M3):
         False, True / "row" (k per row and block: the row's largest P̄ in
         [128, 256)) or "fixed" (k = 8).
+    pv_mxfp4: the P̄V product in MXFP4 (E2M1 elements, one E8M0 scale per 32
+        keys of a 64-key step, the keys split by offset mod 8 below / above 4).
     """
     block_n: int = 64
     round_n: int = 0
@@ -100,12 +102,13 @@ class Schedule:
     exp_rel_err: float = 2.0 ** -22
     block_bf16: bool = False
     pv_fp8: bool | str = False
+    pv_mxfp4: bool = False
 
     def c(self) -> _Schedule:
         return _Schedule(self.block_n, self.round_n, int(bool(self.obar_fp32)),
                          int(bool(self.certify)), int(bool(self.ftz)),
                          self.chunk, self.chunk_err, self.exp_rel_err, int(bool(self.block_bf16)),
-                         {False: 0, True: 1, "row": 1, "fixed": 2}[self.pv_fp8])
+                         {False: 0, True: 1, "row": 1, "fixed": 2}[self.pv_fp8], int(bool(self.pv_mxfp4)))
 
 
 def build(verbose: bool = False) -> str:
@@ -164,6 +167,11 @@ def lib():
         L.orc_e4m3_ulp.restype = ctypes.c_double
         L.orc_e4m3_boundary_distance.argtypes = [ctypes.c_double]
         L.orc_e4m3_boundary_distance.restype = ctypes.c_double
+        for fn in ("orc_e2m1_round", "orc_e2m1_spacing", "orc_e2m1_boundary_distance"):
+            getattr(L, fn).argtypes = [ctypes.c_double]
+            getattr(L, fn).restype = ctypes.c_double
+        L.orc_mx_scale_byte.argtypes = [ctypes.c_double]
+        L.orc_mx_scale_byte.restype = ctypes.c_int
         for name in ("orc_fwd_f64", "orc_bwd_f64", "orc_bwd_rows_f64", "orc_row_stats",
                      "orc_obar_f64", "orc_fwd_emu", "orc_bwd_emu", "orc_bwd_rows_emu",
                      "orc_fwd_emu_rows", "orc_delta_dp_rows_f64", "orc_dsum_rows_f64"):
@@ -244,6 +252,20 @@ def e4m3_ulp(x: float) -> float:
 
 def e4m3_boundary_distance(x: float) -> float:
     return float(lib().orc_e4m3_boundary_distance(float(x)))
+
+
+def e2m1_round(y: float) -> float:
+    """y rounded to FP4 E2M1 (nearest, ties to even, saturating at +-6)."""
+    return float(lib().orc_e2m1_round(float(y)))
+
+
+def e2m1_boundary_distance(y: float) -> float:
+    return float(lib().orc_e2m1_boundary_distance(float(y)))
+
+
+def mx_scale_byte(amax: float) -> int:
+    """E8M0 byte of the MX block scale 2^(floor(log2 amax) - 2) (>= 1)."""
+    return int(lib().orc_mx_scale_byte(float(amax)))
 
 
 def e4m3_array(x):

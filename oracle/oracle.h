@@ -80,6 +80,11 @@ typedef struct {
    * floor(fl32(fl32(r - m) * fl32(log2 e))) per row and block (the row's
    * largest P̄ in [128, 256)); 2: k = 8.  0: bf16 operands.                 */
   int32_t pv_fp8;
+  /* 1: the P̄V product in MXFP4 -- P̄ and V in E2M1 elements with one E8M0
+   * scale 2^(floor(log2 amax) - 2) per 32 keys (each 64-key step split by
+   * key offset mod 8 below / above 4), one scaled matrix instruction per
+   * step.  Streaming schedule with block_n = 64 only.                      */
+  int32_t pv_mxfp4;
 } orc_schedule;
 
 int orc_version(void);
@@ -96,6 +101,11 @@ double orc_bf16_boundary_distance(double x); /* |x - nearest rounding midpoint| 
 double orc_e4m3_round(double x);           /* RNE to E4M3 (NaN past 448)      */
 double orc_e4m3_ulp(double x);             /* spacing of the E4M3 grid at |x| */
 double orc_e4m3_boundary_distance(double x);
+/* ---- FP4 E2M1 and MX block scaling (OCP MX) ---- */
+double orc_e2m1_round(double y);            /* RNE(clamp(y, -6, 6)) on E2M1   */
+double orc_e2m1_spacing(double y);          /* grid spacing at |y|            */
+double orc_e2m1_boundary_distance(double y);
+int orc_mx_scale_byte(double amax);         /* E8M0 byte of the block scale  */
 /* RNE to bf16 of the exact sum of n doubles (the accumulate-then-round step).
  * *exact_out (nullable) receives the exact sum rounded to double.           */
 uint16_t orc_bf16_round_of_sum(const double* terms, int32_t n, double* exact_out);

@@ -216,3 +216,120 @@ def test_fp8_dev_bound_is_finite(orc):
         assert np.all(np.isfinite(dev[fc])) and np.all(dev >= 0)
         cert = e["obar_cert"][0, 0].astype(bool)
         assert np.all(dev[cert] == 0.0)
+
+
+# ---- MXFP4 (OCP MX: E2M1 elements, one E8M0 scale per 32 values)
+
+E2M1 = [(c, (-1.0 if c & 8 else 1.0) * [0, 0.5, 1, 1.5, 2, 3, 4, 6][c & 7]) for c in range(16)]
+
+
+def _nearest_e2m1(y):
+    """Brute force over the 16 codes: nearest after saturating at +-6, ties
+    to the even code (mantissa bit 0)."""
+    y = min(max(y, -6.0), 6.0)
+    best = None
+    for c, v in E2M1:
+        d = abs(v - y)
+        if best is None or d < best[0] or (d == best[0] and (c & 1) == 0):
+            best = (d, c, v)
+    return best[2]
+
+
+def test_e2m1_round_brute_force(orc):
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    ys = []
+    for a, b in zip(mags[:-1], mags[1:]):
+        ys += [a, (a + b) / 2, a + (b - a) / 4, a + 3 * (b - a) / 4]
+    ys += [6.0, 6.5, 7.0, 100.0, 0.1, 0.2499]
+    for y in ys:
+        for sy in (y, -y):
+            assert orc.e2m1_round(sy) == abs(_nearest_e2m1(sy)) * (1 if sy >= 0 else -1) or \
+                (orc.e2m1_round(sy) == 0.0 and _nearest_e2m1(sy) == 0.0), sy
+    assert orc.e2m1_boundary_distance(1.75) == 0.0 and orc.e2m1_boundary_distance(6.0) == 1.0
+
+
+def test_mx_scale_rule(orc):
+    # X = 2^(floor(log2 amax) - 2): amax / X in [4, 8)
+    for amax in (1.0, 0.969, 6.0, 7.99, 0.001, 3.0e-7, 255.0):
+        b = orc.mx_scale_byte(amax)
+        X = 2.0 ** (b - 127)
+        assert 4.0 <= amax / X < 8.0, amax
+    assert orc.mx_scale_byte(1.0) == 125 and orc.mx_scale_byte(0.969) == 124 and orc.mx_scale_byte(0.0) == 1
+
+
+def _mx_quant(v):
+    """numpy reference of one MX block: scale from the largest magnitude."""
+    v = np.asarray(v, np.float64)
+    amax = np.abs(v).max()
+    X = 2.0 ** (np.floor(np.log2(amax)) - 2) if amax > 0 else 2.0 ** -126
+    return np.array([_nearest_e2m1(t / X) for t in v]) * X
+
+
+@pytest.mark.parametrize("guard", ["none", "eps"])
+def test_mxfp4_q0_closed_form(orc, guard):
+    """Q = 0: every P̄ of a row is equal.  No guard: P̄ = 1, X = 1/4, 4 is
+    exact, Ō = sum_j q(V_j).  The eps guard: P̄ = exp(-2^-5) = 0.969, X =
+    1/8, 0.969 * 8 = 7.75 saturates to 6: every operand is 0.75, so Ō is 0.75
+    sum_j q(V_j) while ℓ = N exp(-2^-5) (O 23 % too small).  V's blocks: per
+    feature, the 64-key step's keys split by offset mod 8 below / above 4."""
+    N, d = 40, 64
+    g = {"none": orc.GUARD_NONE, "eps": orc.GUARD_EPS}[guard]
+    p, q, k, v = _q0_case(orc, N, d, g, 5)
+    vf = W.bits_to_f32(v[0, 0]).astype(np.float64)
+    vq = np.zeros_like(vf)
+    for f in range(d):
+        for h in range(2):
+            idx = [j for j in range(N) if ((j & 7) >> 2) == h]
+            vq[idx, f] = _mx_quant(vf[idx, f])
+    pq = 1.0 if guard == "none" else 0.75
+    s = orc.Schedule(block_n=64, round_n=512, obar_fp32=True, certify=False, pv_mxfp4=True)
+    e = orc.fwd_emu(p, s, q, k, v)
+    want = pq * vq.sum(axis=0)
+    assert np.allclose(e["obar"][0, 0], np.broadcast_to(want, (N, d)), rtol=1e-12, atol=1e-12)
+    if guard == "eps":
+        ratio = (want / e["l"][0, 0][:, None]) / (vq.sum(axis=0) / N)
+        assert np.allclose(ratio[:, np.abs(vq.sum(axis=0)) > 1.0], 0.75 / np.exp(-(2.0 ** -5)), rtol=1e-5)
+
+
+def test_mxfp4_single_block_direct(orc):
+    """One 64-key step (N = 56), fp32 Ō: the emulation equals the MX
+    quantization written out with numpy from the row's final shift."""
+    N, d = 56, 64
+    rng = np.random.default_rng(21)
+    q = W.to_bf16_bits(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    k = W.to_bf16_bits(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    v = W.to_bf16_bits((rng.standard_normal((1, 1, N, d)) * 1.5).astype(np.float32))
+    p = orc.Problem(1, 1, 1, N, d, True, orc.GUARD_BETA, tie_eps=0.05)
+    s = orc.Schedule(block_n=64, round_n=512, obar_fp32=True, certify=False, pv_mxfp4=True)
+    e = orc.fwd_emu(p, s, q, k, v)
+    alpha = float(np.float32(1.0 / np.sqrt(d)))
+    qf = W.bits_to_f32(q[0, 0]).astype(np.float64)
+    kf = W.bits_to_f32(k[0, 0]).astype(np.float64)
+    vf = W.bits_to_f32(v[0, 0]).astype(np.float64)
+    vq = np.zeros_like(vf)  # V's blocks span every existing key of the step
+    for f in range(d):
+        for h in range(2):
+            idx = [j for j in range(N) if ((j & 7) >> 2) == h]
+            vq[idx, f] = _mx_quant(vf[idx, f])
+    checked = 0
+    for i in range(N):
+        t = alpha * (kf[: i + 1] @ qf[i])
+        pbar = np.exp(t - float(e["m"][0, 0, i]))
+        pq = np.zeros_like(pbar)
+        ok = True
+        for h in range(2):
+            idx = [j for j in range(i + 1) if ((j & 7) >> 2) == h]
+            if not idx:
+                continue
+            amax = pbar[idx].max()
+            X = 2.0 ** (np.floor(np.log2(amax)) - 2)
+            y = pbar[idx] / X
+            if np.any([orc.e2m1_boundary_distance(float(t)) <= 1e-9 * t for t in y]) or \
+                    0 < abs(np.log2(amax) - np.round(np.log2(amax))) < 1e-9:
+                ok = False
+            pq[idx] = _mx_quant(pbar[idx])
+        if not ok:
+            continue
+        assert np.allclose(e["obar"][0, 0, i], pq @ vq[: i + 1], rtol=1e-12, atol=1e-12)
+        checked += 1
+    assert checked > 0.8 * N
