@@ -146,9 +146,11 @@ def main():
     ms_bwd_dp = timed(lambda: fa.attn_bwd(q, k, v, None, do, fout["row_m"], fout["row_l"],
                                           delta="dp_p", out=bo2, **kw), n_rep, 3)
     # the forward's study variants at the same shape: the FP8 product (row
-    # or fixed operand scale) and the two other rounding schedules
+    # or fixed operand scale), the MXFP4 product and the two other rounding
+    # schedules
     variants = {}
     for name, vkw in (("pv_fp8_row", dict(pv_fp8="row")), ("pv_fp8_fixed", dict(pv_fp8="fixed")),
+                      ("pv_mxfp4", dict(pv_mxfp4=True)),
                       ("sched_fa2_ops", dict(schedule="fa2_ops")), ("sched_untiled", dict(schedule="untiled"))):
         fo3 = {}
         variants[name] = round(timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fo3, **vkw, **kw),

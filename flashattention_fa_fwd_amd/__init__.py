@@ -29,6 +29,7 @@ SCHED_UNTILED = 0x40
 _SCHEDULES = {"stream": 0, "fa2_ops": SCHED_FA2_OPS, "untiled": SCHED_UNTILED}
 PV_FP8 = 0x80
 PV_FP8_FIXED = 0x100
+PV_MXFP4 = 0x200
 _FP8 = {False: 0, None: 0, True: PV_FP8, "row": PV_FP8, "fixed": PV_FP8 | PV_FP8_FIXED}
 ROW_TIE, ROW_ZERO_DENOM, ROW_GUARD_APPLIED = 0x1, 0x2, 0x4
 _GUARDS = {"none": GUARD_NONE, "beta": GUARD_BETA, "eps": GUARD_EPS}
@@ -86,12 +87,14 @@ def attn_strerror(code: int) -> str:
 
 def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guard="beta",
                 beta=2.0, tie_eps=1e-3, shift_eps=2.0 ** -5, obar_fp32=False,
-                softmax_scale=None, delta="do_o", schedule="stream", pv_fp8=False) -> Params:
+                softmax_scale=None, delta="do_o", schedule="stream", pv_fp8=False,
+                pv_mxfp4=False) -> Params:
     """delta: "do_o" (rowsum(dO∘O), the default) or "dp_p" (rowsum(dP∘P)).
     schedule: the forward's rounding schedule, "stream" (default), "fa2_ops"
     (512-key blocks, bf16 block product) or "untiled" (one block a row).
     pv_fp8: the forward's P̄V product in FP8 E4M3 (streaming schedule):
-    True or "row" (operand scale 2^k per row and block) or "fixed" (2^8)."""
+    True or "row" (operand scale 2^k per row and block) or "fixed" (2^8).
+    pv_mxfp4: the same product in MXFP4 (E2M1 with E8M0 scales per 32 keys)."""
     if pv_fp8 not in _FP8:
         raise ValueError(f"pv_fp8 must be False, True, 'row' or 'fixed', not {pv_fp8!r}")
     if delta not in ("do_o", "dp_p"):
@@ -100,6 +103,7 @@ def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guar
         raise ValueError(f"schedule must be one of {sorted(_SCHEDULES)}, not {schedule!r}")
     flags = (CAUSAL if causal else 0) | _GUARDS[guard] | (OBAR_FP32 if obar_fp32 else 0)
     flags |= (DELTA_DP if delta == "dp_p" else 0) | _SCHEDULES[schedule] | _FP8[pv_fp8]
+    flags |= PV_MXFP4 if pv_mxfp4 else 0
     return Params(batch, heads_q, heads_kv, seqlen, head_dim,
                   0.0 if softmax_scale is None else float(softmax_scale),
                   float(beta), float(tie_eps), float(shift_eps), flags)
@@ -143,10 +147,12 @@ def attn_schedule(p: Params):
 
 def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
              shift_eps=2.0 ** -5, obar_fp32=False, softmax_scale=None, schedule="stream",
-             pv_fp8=False, return_obar=False, return_row_max=False, out=None, stream=None):
+             pv_fp8=False, pv_mxfp4=False, return_obar=False, return_row_max=False, out=None,
+             stream=None):
     """Guarded forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16.  schedule:
     "stream" (the streaming kernel), "fa2_ops" or "untiled" (see make_params);
-    pv_fp8: P̄V in FP8 E4M3 (streaming kernel only): True/"row" or "fixed".
+    pv_fp8: P̄V in FP8 E4M3 (streaming kernel only): True/"row" or "fixed";
+    pv_mxfp4: P̄V in MXFP4 (streaming kernel only).
     Returns a dict: o, row_m, row_l, row_flags (+ obar, row_max on request)."""
     _check_bf16("q", q)
     B, Hq, N, d = q.shape
@@ -154,7 +160,7 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
     _check_bf16("v", v, k.shape)
     p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
                      shift_eps=shift_eps, obar_fp32=obar_fp32, softmax_scale=softmax_scale,
-                     schedule=schedule, pv_fp8=pv_fp8)
+                     schedule=schedule, pv_fp8=pv_fp8, pv_mxfp4=pv_mxfp4)
     dev = q.device
     res = out if out is not None else {}
     if "o" not in res:

@@ -43,6 +43,14 @@
 // range for a fixed scale); when k changes the accumulator is rescaled by
 // the power of two along with exp(m_old - m).  A fixed k = 8 is the other
 // option.  ℓ stays the sum of the fp32 P̄.
+//
+// MXFP4 variant (the other format the pages name there): P̄ and V in E2M1
+// elements with one E8M0 scale per 32 keys, 2^(floor(log2 amax) - 2) of the
+// block's largest magnitude (v_cvt_scalef32_pk_fp4_f32 gives RNE(clamp(v /
+// scale)), measured), on v_mfma_scale_f32_32x32x64_f8f6f4: one instruction
+// per feature block and 64-key step.  Its k index 32h + j (h = lane half)
+// takes, in each lane, the 32 keys that half holds (key offset mod 8 in
+// 4h..4h+3), so those are the blocks, for P̄ and for V alike.
 #include "attn_device.h"
 
 namespace attn {
@@ -76,12 +84,35 @@ __device__ __forceinline__ void top2_merge(float& a, float& a2, float b, float b
   a2 = fmaxf(lo, fmaxf(a2, b2));
 }
 
-template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, bool PV_FP8>
-__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs a) {
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// The matrix operands of Ō's product.
+constexpr int kPvBf16 = 0, kPvFp8 = 1, kPvMx = 2;
+
+// Four E2M1 pairs of v / scale (rounded to nearest even, saturating) in
+// the four bytes of a word, low byte first.
+__device__ __forceinline__ uint32_t fp4x8(const float* v, float scale) {
+  uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], scale, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2], v[3], scale, 1);
+  uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[4], v[5], scale, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[6], v[7], scale, 1);
+  return (lo & 0xffffu) | (hi << 16);
+}
+
+// E8M0 byte of the MX scale of a block whose largest magnitude is amax:
+// 2^(floor(log2 amax) - 2), from the exponent field (at least 1).
+__device__ __forceinline__ int mx_scale_byte(float amax) {
+  return max((int)((__float_as_uint(amax) >> 23) & 0xffu) - 2, 1);
+}
+
+template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, int PV>
+__global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kernel(FwdArgs a) {
   // every fp32 operation as written: no multiply is fused into a later add
   // (a fused alpha*R - m would turn r - m = 0 into the rounding error of
   // alpha*R and move decisions taken on it); fused steps are explicit fmaf
 #pragma clang fp contract(off)
+  constexpr bool PV_FP8 = PV == kPvFp8;
+  constexpr bool PV_MX = PV == kPvMx;
   constexpr int BN = kFwdBlockN;
   constexpr int NT = D / kMfmaK; // matrix steps along d for S
   constexpr int FB = D / 32;     // 32-feature blocks of O^T
@@ -262,6 +293,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
     // matrix operand in bf16, or 2^k P̄ in E4M3
     bf16x8 pf[4];
     uint32_t pf8[4][2];
+    float pmx[32];  // MXFP4: the lane's P̄ in k order 16kb + i
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -277,16 +309,59 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
             w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p0 * psc, p1 * psc, (int)w, true);
           else
             w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p0 * psc, p1 * psc, 0, false);
+        } else if (PV_MX) {
+          pmx[16 * kb + i] = p0;
+          pmx[16 * kb + i + 1] = p1;
         } else {
           pf[t][u] = (__bf16)p0;
           pf[t][u + 1] = (__bf16)p1;
         }
       }
+    // MXFP4: one block of 32 P̄ per lane (its row, its half's keys)
+    int sbp = 1;
+    i32x8 pmb = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (PV_MX) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(pmx[j], pmx[j + 1]));
+      sbp = mx_scale_byte(amax);
+      const float xs = __int_as_float(sbp << 23);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pmb[w] = (int)fp4x8(&pmx[8 * w], xs);
+    }
 
     // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order (the feature
-    // blocks' chains interleaved)
+    // blocks' chains interleaved); MXFP4: one step of 64 keys
+    if (PV_MX) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+      for (int f = 0; f < FB; ++f) {
+        // V^T, k order 8t + 4e + u: keys 16t + 8e + 4*half + u of feature 32f + l32
+        float vx[32];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint2 v0 = lds_read_tr(vs + ta_off[f][0] + 16 * t * D);
+          const uint2 v1 = lds_read_tr(vs + ta_off[f][1] + 16 * t * D);
+          const uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            vx[8 * t + 2 * q] = __uint_as_float(w[q] << 16);
+            vx[8 * t + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+          }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(fabsf(vx[j]), fabsf(vx[j + 1])));
+        const int sbv = mx_scale_byte(amax);
+        const float xs = __int_as_float(sbv << 23);
+        i32x8 va = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) va[w] = (int)fp4x8(&vx[8 * w], xs);
+        // formats 4, 4: E2M1 operands; scale bytes in bits 0..7
+        oacc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pmb, oacc[f], 4, 4, 0, sbv, 0, sbp);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < (PV_MX ? 0 : 4); ++t) {
 #pragma unroll
       for (int f = 0; f < FB; ++f) {
         // A = V^T: feature 32f + l32, keys 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
@@ -396,44 +471,47 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void fwd_kernel(FwdArgs 
   }
 }
 
-template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, bool PV_FP8>
+template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, int PV>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   const int nmb = (a.N + kFwdBlockM - 1) / kFwdBlockM;
   dim3 grid((unsigned)(nmb * a.Hq * a.B));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, GUARD, OBAR_F32, PV_FP8>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, GUARD, OBAR_F32, PV>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int GUARD, bool PV_FP8>
+template <int D, bool CAUSAL, int GUARD, int PV>
 hipError_t launch_o(const FwdArgs& a, bool obar_f32, hipStream_t s) {
-  return obar_f32 ? launch_t<D, CAUSAL, GUARD, true, PV_FP8>(a, s)
-                  : launch_t<D, CAUSAL, GUARD, false, PV_FP8>(a, s);
+  return obar_f32 ? launch_t<D, CAUSAL, GUARD, true, PV>(a, s)
+                  : launch_t<D, CAUSAL, GUARD, false, PV>(a, s);
 }
 
-template <int D, bool CAUSAL, bool PV_FP8>
+template <int D, bool CAUSAL, int PV>
 hipError_t launch_g(const FwdArgs& a, int guard, bool obar_f32, hipStream_t s) {
   switch (guard) {
-    case kGuardBeta: return launch_o<D, CAUSAL, kGuardBeta, PV_FP8>(a, obar_f32, s);
-    case kGuardEps: return launch_o<D, CAUSAL, kGuardEps, PV_FP8>(a, obar_f32, s);
-    default: return launch_o<D, CAUSAL, kGuardNone, PV_FP8>(a, obar_f32, s);
+    case kGuardBeta: return launch_o<D, CAUSAL, kGuardBeta, PV>(a, obar_f32, s);
+    case kGuardEps: return launch_o<D, CAUSAL, kGuardEps, PV>(a, obar_f32, s);
+    default: return launch_o<D, CAUSAL, kGuardNone, PV>(a, obar_f32, s);
   }
 }
 
-template <bool PV_FP8>
+template <int PV>
 hipError_t launch_d(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32, hipStream_t s) {
   if (d == 64)
-    return causal ? launch_g<64, true, PV_FP8>(a, guard, obar_f32, s)
-                  : launch_g<64, false, PV_FP8>(a, guard, obar_f32, s);
-  return causal ? launch_g<128, true, PV_FP8>(a, guard, obar_f32, s)
-                : launch_g<128, false, PV_FP8>(a, guard, obar_f32, s);
+    return causal ? launch_g<64, true, PV>(a, guard, obar_f32, s)
+                  : launch_g<64, false, PV>(a, guard, obar_f32, s);
+  return causal ? launch_g<128, true, PV>(a, guard, obar_f32, s)
+                : launch_g<128, false, PV>(a, guard, obar_f32, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32, bool pv_fp8,
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32, int pv,
                       hipStream_t s) {
-  return pv_fp8 ? launch_d<true>(a, d, causal, guard, obar_f32, s)
-                : launch_d<false>(a, d, causal, guard, obar_f32, s);
+  switch (pv) {
+    case 1: return launch_d<kPvFp8>(a, d, causal, guard, obar_f32, s);
+    case 2: return launch_d<kPvMx>(a, d, causal, guard, obar_f32, s);
+    default: return launch_d<kPvBf16>(a, d, causal, guard, obar_f32, s);
+  }
 }
 
 }  // namespace attn

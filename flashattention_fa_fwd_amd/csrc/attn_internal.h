@@ -81,8 +81,9 @@ __device__ __forceinline__ void xcd_map(int L, int heads, int& head, int& blk) {
   }
 }
 
+// pv: the operands of Ō's product, 0 bf16, 1 FP8 E4M3, 2 MXFP4
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
-                      bool pv_fp8, hipStream_t s);
+                      int pv, hipStream_t s);
 hipError_t launch_fwd_block(const FwdArgs& a, int d, bool causal, int guard, bool obar_f32,
                             bool untiled, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int d, bool causal, hipStream_t s);

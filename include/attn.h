@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -53,6 +53,8 @@ extern "C" {
 /* forward: the P̄V product in FP8 E4M3 (streaming schedule only)          */
 #define ATTN_PV_FP8 0x80u
 #define ATTN_PV_FP8_FIXED 0x100u  /* with ATTN_PV_FP8: operand scale 2^8     */
+/* forward: the P̄V product in MXFP4 (streaming schedule only, not with FP8) */
+#define ATTN_PV_MXFP4 0x200u
 
 /* per-row flag bits written by attn_fwd */
 #define ATTN_ROW_TIE 0x1u           /* the row maximum recurs within tie_eps   */
@@ -80,7 +82,7 @@ typedef struct {
   float shift_eps;   /* eps-guard extra shift, > 0 (the pages use 2^-5)      */
   uint32_t flags;    /* ATTN_CAUSAL | one ATTN_GUARD_* | ATTN_OBAR_FP32 |
                         ATTN_DELTA_DP | one ATTN_SCHED_* | ATTN_PV_FP8 (+
-                        ATTN_PV_FP8_FIXED)                                   */
+                        ATTN_PV_FP8_FIXED) or ATTN_PV_MXFP4                  */
 } attn_params;
 
 /*
@@ -127,6 +129,15 @@ typedef struct {
  *   unchanged.  V entries must round inside E4M3's range (|V| < 464);
  *   beyond it the result is undefined.  attn_bwd ignores both flags (it
  *   recomputes P in fp32 and reads O as given).
+ * ATTN_PV_MXFP4 (streaming schedule only, not with ATTN_PV_FP8): the same
+ *   question for the other format the pages name there.  The operands become
+ *   MXFP4 in the OCP MX sense: E2M1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ *   negatives) sharing one E8M0 scale X = 2^(floor(log2 amax) - 2) per
+ *   block, each element RNE(clamp(v / X, -6, 6)).  A block is 32 of the 64
+ *   keys of a streaming step: those at key offsets 0..3 mod 8, or 4..7 mod 8
+ *   -- per query row for P̄, per feature for V (over every key of the step
+ *   that exists).  The scales are applied inside the scaled matrix
+ *   instruction; Ō, ℓ and the shift are as in the bf16 path.
  */
 int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
              void* o, float* row_m, float* row_l, uint8_t* row_flags,

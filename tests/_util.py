@@ -67,14 +67,15 @@ def problem(wl_or_shape, guard="beta", beta=2.0, causal=None):
     return orc.Problem(B, Hq, Hkv, N, d, c, GUARD[guard], beta=beta)
 
 
-def schedule(p: orc.Problem, obar_fp32=False, certify=True, sched="stream", pv_fp8=False) -> orc.Schedule:
+def schedule(p: orc.Problem, obar_fp32=False, certify=True, sched="stream", pv_fp8=False,
+             pv_mxfp4=False) -> orc.Schedule:
     """The oracle replays the rounding schedule the library reports."""
     fp = fa.make_params(p.batch, p.heads_q, p.heads_kv, p.seqlen, p.head_dim, causal=p.causal,
-                        schedule=sched, pv_fp8=pv_fp8)
+                        schedule=sched, pv_fp8=pv_fp8, pv_mxfp4=pv_mxfp4)
     s = fa.attn_schedule(fp)
     return orc.Schedule(block_n=s["block_n"], round_n=s["round_n"], obar_fp32=obar_fp32,
                         chunk=s["chunk"], certify=certify, block_bf16=bool(s["block_bf16"]),
-                        pv_fp8=pv_fp8)
+                        pv_fp8=pv_fp8, pv_mxfp4=pv_mxfp4)
 
 
 def check_o(o_gpu, o64, o_emu=None, obar_fp32=True, rows=None):

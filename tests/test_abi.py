@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 7
+    assert fa.attn_abi_version() == 8
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -54,8 +54,16 @@ def test_schedule(L):
     p = fa.make_params(1, 1, 1, 128, 64, pv_fp8=True)
     assert fa.attn_schedule(p)["block_n"] == 64
     for sched in ("fa2_ops", "untiled"):
-        p = fa.make_params(1, 1, 1, 128, 64, schedule=sched, pv_fp8=True)
-        assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+        for kw in (dict(pv_fp8=True), dict(pv_mxfp4=True)):
+            p = fa.make_params(1, 1, 1, 128, 64, schedule=sched, **kw)
+            assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    p = fa.make_params(1, 1, 1, 128, 64, pv_mxfp4=True)
+    assert fa.attn_schedule(p)["block_n"] == 64
+    p = fa.make_params(1, 1, 1, 128, 64, pv_fp8=True, pv_mxfp4=True)  # two formats
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    p = fa.make_params(1, 1, 1, 128, 64)
+    p.flags |= fa.PV_FP8_FIXED  # the fixed FP8 scale without the FP8 product
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
     with pytest.raises(ValueError):
         fa.make_params(1, 1, 1, 64, 64, schedule="blocked")
 

@@ -10,12 +10,13 @@ certain shift decision is checked against the emulation's carried error
 bound, certified ones bit for bit.
 
 Study: the signed error on tie rows, in output units, against the exact sum
-with the same E4M3 V, projected on the tied keys' V sum.  Prediction made
+with the same E4M3 (or MXFP4) V, projected on the tied keys' V sum.  Prediction made
 before measuring: under the eps guard the tied keys' 2^8 P̄ = 256 exp(-2^-5)
 = 248.1 rounds up to 256 while ℓ keeps exp(-2^-5), so those keys weigh
-1/exp(-2^-5) = 1.031 times too much (coefficient 1 - exp(-2^-5) = 0.0308);
-no guard (P̄ = 1, exact) and the beta guard (a generic value) carry no such
-systematic factor."""
+1/exp(-2^-5) = 1.032 times too much (relative weight error +0.032); no guard
+(P̄ = 1, exact) and the beta guard (a generic value) carry no such
+systematic factor.  MXFP4 (measured after its own prediction for the eps
+guard, -0.226): see the assertions at the end."""
 import numpy as np
 import pytest
 import torch
@@ -35,6 +36,27 @@ def _e4m3_bits(vbits):
     v = torch.from_numpy(W.bits_to_f32(vbits))
     v8 = v.to(torch.float8_e4m3fn).to(torch.float32).numpy()
     return W.to_bf16_bits(v8)
+
+
+def _mx_bits(vbits, N, d):
+    """bf16 bits of V quantized as the MXFP4 product takes it (exact in bf16):
+    per feature, blocks of the 32 keys of a 64-key step at offsets 0..3 or
+    4..7 mod 8, scale 2^(floor(log2 amax) - 2), elements RNE(clamp(v / X))
+    on the E2M1 grid (numpy's round is half-to-even)."""
+    v = W.bits_to_f32(vbits).astype(np.float64).reshape(-1, N, d)
+    out = np.zeros_like(v)
+    keys = np.arange(N)
+    for j0 in range(0, N, 64):
+        for h in range(2):
+            idx = keys[(keys >= j0) & (keys < j0 + 64) & (((keys - j0) & 7) >> 2 == h)]
+            blk = v[:, idx, :]
+            amax = np.abs(blk).max(axis=1, keepdims=True)
+            X = np.where(amax > 0, 2.0 ** (np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2), 2.0 ** -126)
+            a = np.minimum(np.abs(blk / X), 6.0)
+            sp = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+            qv = np.minimum(np.round(a / sp) * sp, 6.0)
+            out[:, idx, :] = np.sign(blk) * qv * X
+    return W.to_bf16_bits(out.astype(np.float32).reshape(vbits.shape))
 
 
 def _ragged(shape, seed=91):
@@ -68,7 +90,11 @@ def _check_against_emulation(e, r, obar_fp32):
                 mean_diff=f"{diff[rows].mean() if n else 0:.2e}", mean_bound=f"{devb[rows].mean() if n else 0:.2e}")
 
 
-@pytest.mark.parametrize("scale", ["row", "fixed"])
+# the product's format: FP8 with the row scale or the fixed 2^8, or MXFP4
+FORMATS = {"row": dict(pv_fp8="row"), "fixed": dict(pv_fp8="fixed"), "mxfp4": dict(pv_mxfp4=True)}
+
+
+@pytest.mark.parametrize("scale", ["row", "fixed", "mxfp4"])
 @pytest.mark.parametrize("obar_fp32", [False, True])
 @pytest.mark.parametrize("guard", ["none", "beta", "eps"])
 @pytest.mark.parametrize("name,shape", FP8_CASES)
@@ -76,10 +102,10 @@ def test_fp8_parity(name, shape, guard, obar_fp32, scale):
     x = make(name) if name == "tiny" else _ragged(shape)
     wl = x["workload"]
     p = problem(wl, guard)
-    e = orc.fwd_emu(p, schedule(p, obar_fp32, pv_fp8=scale), x["q"], x["k"], x["v"], nthreads=threads())
+    fmt = FORMATS[scale]
+    e = orc.fwd_emu(p, schedule(p, obar_fp32, **fmt), x["q"], x["k"], x["v"], nthreads=threads())
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    r = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard, obar_fp32=obar_fp32, pv_fp8=scale,
-                    return_obar=True)
+    r = fa.attn_fwd(q, k, v, causal=wl.causal, guard=guard, obar_fp32=obar_fp32, return_obar=True, **fmt)
     torch.cuda.synchronize()
     flags = r["row_flags"].cpu().numpy()
     fc = e["flag_cert"].astype(bool)
@@ -95,7 +121,8 @@ def test_fp8_parity(name, shape, guard, obar_fp32, scale):
     assert np.all(np.abs(o_gpu - e["o"])[rows] <= tol[rows])
     # accuracy of the variant against FP64 (real V, and the same E4M3 V)
     o64, _ = orc.fwd_f64(p, x["q"], x["k"], x["v"], nthreads=threads())
-    o64v8, _ = orc.fwd_f64(p, x["q"], x["k"], _e4m3_bits(x["v"]), nthreads=threads())
+    o64v8, _ = orc.fwd_f64(p, x["q"], x["k"], _e4m3_bits(x["v"]) if scale != "mxfp4" else x["v"],
+                           nthreads=threads())
     mx, mean = rel_errors(o_gpu, o64)
     mx8, mean8 = rel_errors(o_gpu, o64v8)
     report(f"fp8 {scale} {name} {shape or ''} {guard} {'fp32' if obar_fp32 else 'bf16'}",
@@ -128,22 +155,25 @@ def test_fp8_full_size_sampled(guard):
     report(f"fp8 gpt2s {guard} heads {heads}", **nums, o_max_rel=f"{mx:.2e}", o_mean_rel=f"{mean:.2e}")
 
 
-def _tie_projection(x, wl, heads, err, l64, tie, tie_eps=1e-3, block_n=64):
-    """Per tie row: u = sum of the E4M3 V rows of the keys at the row maximum
-    (exact score equal to the largest) that the kernel reaches at or after
-    the block where the tie is detected (the running top two within
-    tie_eps); a maximum key in an earlier block was taken with P̄ = 1,
-    exactly, and is rescaled in fp32 afterwards.  Returns
-    sum<e, u> / sum<u, u>/ℓ over the rows."""
+def _tie_projection(x, wl, heads, err, l64, tie, m, tie_eps=1e-3, block_n=64, vref=None):
+    """Per tie row: u = sum of the quantized V rows of the keys at the row
+    maximum (exact score equal to the largest) that the kernel reaches at or
+    after the block where the tie is detected (the running top two within
+    tie_eps); a maximum key in an earlier block was taken before the guard
+    moved the shift and is rescaled in fp32 afterwards.  With w = exp(t_max -
+    m) the exact weight of those keys, returns sum<e, u> / sum(w <u, u>/ℓ):
+    the relative error of their weight."""
     g = wl.heads_q // wl.heads_kv
     alpha = wl.alpha
     qf = W.bits_to_f32(x["q"]).astype(np.float64).reshape(-1, wl.seqlen, wl.head_dim)
     kf = W.bits_to_f32(x["k"]).astype(np.float64).reshape(-1, wl.seqlen, wl.head_dim)
-    v8 = W.bits_to_f32(_e4m3_bits(x["v"])).astype(np.float64).reshape(-1, wl.seqlen, wl.head_dim)
+    v8 = W.bits_to_f32(_e4m3_bits(x["v"]) if vref is None else vref).astype(np.float64).reshape(
+        -1, wl.seqlen, wl.head_dim)
     num = den = 0.0
     for a, h in enumerate(heads):
         kvh = (h // wl.heads_q) * wl.heads_kv + (h % wl.heads_q) // g
         s = qf[h] @ kf[kvh].T  # exact: products of bf16 values summed in double
+        mrow = m.reshape(-1, wl.seqlen)[h]
         if wl.causal:
             s = np.where(np.tril(np.ones_like(s, dtype=bool)), s, -np.inf)
         for i in np.nonzero(tie[a])[0]:
@@ -160,8 +190,9 @@ def _tie_projection(x, wl, heads, err, l64, tie, tie_eps=1e-3, block_n=64):
                 continue
             idx = np.nonzero(T)[0]
             u = v8[kvh][idx[idx >= det]].sum(axis=0)
+            w = np.exp(alpha * row.max() - float(mrow[i]))
             num += float(err[a, i] @ u)
-            den += float(u @ u) / l64[a, i]
+            den += w * float(u @ u) / l64[a, i]
     return num / den if den > 0 else float("nan")
 
 
@@ -174,6 +205,7 @@ def test_fp8_bias_study():
     wl = x["workload"]
     heads = list(range(0, 192, 12))
     v8bits = _e4m3_bits(x["v"])
+    vmxbits = _mx_bits(x["v"], wl.seqlen, wl.head_dim)
     res = {}
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     vf8 = W.bits_to_f32(v8bits).astype(np.float64).reshape(-1, wl.seqlen, wl.head_dim)
@@ -181,20 +213,22 @@ def test_fp8_bias_study():
     kvh = [(h // wl.heads_q) * wl.heads_kv + (h % wl.heads_q) // g for h in heads]
     neg = vf8[kvh].mean(axis=1) < 0
     shp = (-1, wl.seqlen, wl.head_dim)
-    for scale in ("row", "fixed"):
+    for scale in ("row", "fixed", "mxfp4"):
+        vref = vmxbits if scale == "mxfp4" else v8bits
         for guard in ("none", "beta", "eps"):
             p = problem(wl, guard)
             st = orc.row_stats(p, x["q"], x["k"], schedule(p), heads=heads, nthreads=threads())
-            ob64, l64 = orc.obar_f64(p, x["q"], x["k"], v8bits, st["m"], heads=heads, nthreads=threads())
+            ob64, l64 = orc.obar_f64(p, x["q"], x["k"], vref, st["m"], heads=heads, nthreads=threads())
             ob64 = ob64.reshape(shp)[heads]
             l64 = l64.reshape(-1, wl.seqlen)[heads]
             tie = (((st["flags"] & orc.ROW_TIE) != 0) & st["flag_cert"].astype(bool)).reshape(-1, wl.seqlen)[heads]
             for f32_ in (False, True):
-                r = fa.attn_fwd(q, k, v, causal=True, guard=guard, obar_fp32=f32_, pv_fp8=scale, return_obar=True)
+                r = fa.attn_fwd(q, k, v, causal=True, guard=guard, obar_fp32=f32_, return_obar=True,
+                                **FORMATS[scale])
                 torch.cuda.synchronize()
                 ob = r["obar"].float().cpu().numpy().astype(np.float64).reshape(shp)[heads]
                 err = (ob - ob64) / l64[..., None]
-                c = _tie_projection(x, wl, heads, err, l64, tie)
+                c = _tie_projection(x, wl, heads, err, l64, tie, st["m"], vref=vref)
                 zero_rows = int((np.abs(ob).max(axis=-1) == 0).sum())
                 sel_neg = tie[..., None] & neg[:, None, :]
                 single = ~tie[..., None] & neg[:, None, :]
@@ -205,7 +239,7 @@ def test_fp8_bias_study():
                        single_neg=f"{err[single].mean():+.3e}±{err[single].std() / np.sqrt(max(single.sum(), 1)):.1e}")
     # the prediction: under the eps guard the tied keys reached after the
     # detection weigh 1/exp(-2^-5) too much; no such factor otherwise
-    want = 1.0 - np.exp(-(2.0 ** -5))
+    want = np.exp(2.0 ** -5) - 1.0
     for scale in ("row", "fixed"):
         for f32_ in (False, True):
             assert abs(res[(scale, "eps", f32_)][0] - want) < 0.25 * want, res
@@ -213,3 +247,12 @@ def test_fp8_bias_study():
     for f32_ in (False, True):
         assert abs(res[("row", "beta", f32_)][0]) < 0.25 * want, res
         assert res[("row", "beta", f32_)][1] == 0 and res[("fixed", "beta", f32_)][1] > 0, res
+    # MXFP4: under the eps guard the tied keys' block scale is 1/8 and 0.969 * 8
+    # saturates to 6, so they weigh 0.75 instead of exp(-2^-5).  Unguarded, the
+    # maximum's P̄ = 1 sits on a scale boundary: the kernel's fp32 exp gives
+    # 1 or a value just below it, whose scale is 1/8 and whose element
+    # saturates (0.75) -- so each such key keeps its weight or loses a quarter
+    want_mx = 0.75 / np.exp(-(2.0 ** -5)) - 1.0
+    for f32_ in (False, True):
+        assert abs(res[("mxfp4", "eps", f32_)][0] - want_mx) < 0.25 * abs(want_mx), res
+        assert -0.27 < res[("mxfp4", "none", f32_)][0] < 0.01, res
