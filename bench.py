@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd.hip", "attn_device.h", "attn_internal.h")}
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
-        "sources_sha256": "42c0702aeafb898b2bab7bd9dd462bfd47798753ba9f9c463071102e345afb87",
-        "fetch_kib": 64490.0, "write_kib": 51502.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "9d56f5d6afa960d9996f00cb1d0e455718f044629e73ad58ed60efd2191241ef",
+        "fetch_kib": 64237.0, "write_kib": 51211.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
