@@ -30,6 +30,7 @@ _SCHEDULES = {"stream": 0, "fa2_ops": SCHED_FA2_OPS, "untiled": SCHED_UNTILED}
 PV_FP8 = 0x80
 PV_FP8_FIXED = 0x100
 PV_MXFP4 = 0x200
+PV_MX_CEIL = 0x400
 _FP8 = {False: 0, None: 0, True: PV_FP8, "row": PV_FP8, "fixed": PV_FP8 | PV_FP8_FIXED}
 ROW_TIE, ROW_ZERO_DENOM, ROW_GUARD_APPLIED = 0x1, 0x2, 0x4
 _GUARDS = {"none": GUARD_NONE, "beta": GUARD_BETA, "eps": GUARD_EPS}
@@ -94,7 +95,8 @@ def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guar
     (512-key blocks, bf16 block product) or "untiled" (one block a row).
     pv_fp8: the forward's P̄V product in FP8 E4M3 (streaming schedule):
     True or "row" (operand scale 2^k per row and block) or "fixed" (2^8).
-    pv_mxfp4: the same product in MXFP4 (E2M1 with E8M0 scales per 32 keys)."""
+    pv_mxfp4: the same product in MXFP4 (E2M1 with E8M0 scales per 32 keys):
+    True or "floor" (the OCP scale rule) or "ceil" (scale rounded up)."""
     if pv_fp8 not in _FP8:
         raise ValueError(f"pv_fp8 must be False, True, 'row' or 'fixed', not {pv_fp8!r}")
     if delta not in ("do_o", "dp_p"):
@@ -103,7 +105,9 @@ def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guar
         raise ValueError(f"schedule must be one of {sorted(_SCHEDULES)}, not {schedule!r}")
     flags = (CAUSAL if causal else 0) | _GUARDS[guard] | (OBAR_FP32 if obar_fp32 else 0)
     flags |= (DELTA_DP if delta == "dp_p" else 0) | _SCHEDULES[schedule] | _FP8[pv_fp8]
-    flags |= PV_MXFP4 if pv_mxfp4 else 0
+    if pv_mxfp4 not in (False, None, True, "floor", "ceil"):
+        raise ValueError(f"pv_mxfp4 must be False, True, 'floor' or 'ceil', not {pv_mxfp4!r}")
+    flags |= (PV_MXFP4 if pv_mxfp4 else 0) | (PV_MX_CEIL if pv_mxfp4 == "ceil" else 0)
     return Params(batch, heads_q, heads_kv, seqlen, head_dim,
                   0.0 if softmax_scale is None else float(softmax_scale),
                   float(beta), float(tie_eps), float(shift_eps), flags)

@@ -26,7 +26,7 @@ int check_params(const attn_params* p) {
   if (p->head_dim != 64 && p->head_dim != 128) return ATTN_E_UNSUPPORTED;
   const uint32_t known =
       ATTN_CAUSAL | ATTN_GUARD_MASK | ATTN_OBAR_FP32 | ATTN_DELTA_DP | ATTN_SCHED_MASK | ATTN_PV_FP8 |
-      ATTN_PV_FP8_FIXED | ATTN_PV_MXFP4;
+      ATTN_PV_FP8_FIXED | ATTN_PV_MXFP4 | ATTN_PV_MX_CEIL;
   if (p->flags & ~known) return ATTN_E_PARAM;
   if ((p->flags & ATTN_SCHED_MASK) == ATTN_SCHED_MASK) return ATTN_E_PARAM;  // two schedules
   // the FP8 product exists in the streaming kernel only
@@ -34,6 +34,7 @@ int check_params(const attn_params* p) {
   if ((p->flags & ATTN_PV_FP8_FIXED) && !(p->flags & ATTN_PV_FP8)) return ATTN_E_PARAM;
   // MXFP4: streaming kernel only, and one low-precision format at a time
   if ((p->flags & ATTN_PV_MXFP4) && (p->flags & (ATTN_SCHED_MASK | ATTN_PV_FP8))) return ATTN_E_PARAM;
+  if ((p->flags & ATTN_PV_MX_CEIL) && !(p->flags & ATTN_PV_MXFP4)) return ATTN_E_PARAM;
   const uint32_t g = p->flags & ATTN_GUARD_MASK;
   if (g == ATTN_GUARD_MASK) return ATTN_E_PARAM;  // two guards at once
   if (!std::isfinite(p->softmax_scale)) return ATTN_E_PARAM;
@@ -154,6 +155,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.tie_eps = p->tie_eps;
   a.shift_eps = p->shift_eps;
   a.pv_fixed_scale = (p->flags & ATTN_PV_FP8_FIXED) != 0;
+  a.pv_mx_ceil = (p->flags & ATTN_PV_MX_CEIL) != 0;
   const bool causal = (p->flags & ATTN_CAUSAL) != 0, obar_f32 = (p->flags & ATTN_OBAR_FP32) != 0;
   if (p->flags & ATTN_SCHED_MASK)
     return hip_status(attn::launch_fwd_block(a, p->head_dim, causal, guard_of(p->flags), obar_f32,

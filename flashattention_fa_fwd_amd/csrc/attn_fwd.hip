@@ -100,9 +100,13 @@ __device__ __forceinline__ uint32_t fp4x8(const float* v, float scale) {
 }
 
 // E8M0 byte of the MX scale of a block whose largest magnitude is amax:
-// 2^(floor(log2 amax) - 2), from the exponent field (at least 1).
-__device__ __forceinline__ int mx_scale_byte(float amax) {
-  return max((int)((__float_as_uint(amax) >> 23) & 0xffu) - 2, 1);
+// 2^(floor(log2 amax) - 2) from the exponent field (at least 1), or with
+// ceil (amax / X in (2, 4]: never saturates) one more unless amax is a
+// power of two.
+__device__ __forceinline__ int mx_scale_byte(float amax, bool ceil) {
+  const uint32_t b = __float_as_uint(amax);
+  const int up = (ceil && (b & 0x7fffffu) != 0u) ? 1 : 0;
+  return max((int)((b >> 23) & 0xffu) - 2 + up, 1);
 }
 
 template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, int PV>
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
       float amax = 0.0f;
 #pragma unroll
       for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(pmx[j], pmx[j + 1]));
-      sbp = mx_scale_byte(amax);
+      sbp = mx_scale_byte(amax, a.pv_mx_ceil != 0);
       const float xs = __int_as_float(sbp << 23);
 #pragma unroll
       for (int w = 0; w < 4; ++w) pmb[w] = (int)fp4x8(&pmx[8 * w], xs);
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
         float amax = 0.0f;
 #pragma unroll
         for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(fabsf(vx[j]), fabsf(vx[j + 1])));
-        const int sbv = mx_scale_byte(amax);
+        const int sbv = mx_scale_byte(amax, a.pv_mx_ceil != 0);
         const float xs = __int_as_float(sbv << 23);
         i32x8 va = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll

@@ -41,6 +41,7 @@ struct FwdArgs {
   float c1;        // fl32(alpha * log2(e))
   float beta, tie_eps, shift_eps;
   int pv_fixed_scale;  // FP8 product: 1 = operand scale fixed at 2^8
+  int pv_mx_ceil;      // MXFP4 product: 1 = block scale from ceil(log2 amax)
 };
 
 struct BwdArgs {

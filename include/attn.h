@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 8
+#define ATTN_ABI_VERSION 9
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -55,6 +55,7 @@ extern "C" {
 #define ATTN_PV_FP8_FIXED 0x100u  /* with ATTN_PV_FP8: operand scale 2^8     */
 /* forward: the P̄V product in MXFP4 (streaming schedule only, not with FP8) */
 #define ATTN_PV_MXFP4 0x200u
+#define ATTN_PV_MX_CEIL 0x400u    /* with ATTN_PV_MXFP4: scales from ceil(log2) */
 
 /* per-row flag bits written by attn_fwd */
 #define ATTN_ROW_TIE 0x1u           /* the row maximum recurs within tie_eps   */
@@ -137,7 +138,10 @@ typedef struct {
  *   keys of a streaming step: those at key offsets 0..3 mod 8, or 4..7 mod 8
  *   -- per query row for P̄, per feature for V (over every key of the step
  *   that exists).  The scales are applied inside the scaled matrix
- *   instruction; Ō, ℓ and the shift are as in the bf16 path.
+ *   instruction; Ō, ℓ and the shift are as in the bf16 path.  With
+ *   ATTN_PV_MX_CEIL the scales are 2^(ceil(log2 amax) - 2) instead (amax / X
+ *   in (2, 4]: no element saturates; equal to the rule above when amax is a
+ *   power of two) -- the rounding-up rule some MX implementations use.
  */
 int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
              void* o, float* row_m, float* row_l, uint8_t* row_flags,

@@ -90,7 +90,8 @@ class Schedule:
         False, True / "row" (k per row and block: the row's largest P̄ in
         [128, 256)) or "fixed" (k = 8).
     pv_mxfp4: the P̄V product in MXFP4 (E2M1 elements, one E8M0 scale per 32
-        keys of a 64-key step, the keys split by offset mod 8 below / above 4).
+        keys of a 64-key step, the keys split by offset mod 8 below / above 4);
+        True / "floor" (the OCP rule) or "ceil" (scale from ceil(log2 amax)).
     """
     block_n: int = 64
     round_n: int = 0
@@ -102,13 +103,13 @@ class Schedule:
     exp_rel_err: float = 2.0 ** -22
     block_bf16: bool = False
     pv_fp8: bool | str = False
-    pv_mxfp4: bool = False
+    pv_mxfp4: bool | str = False
 
     def c(self) -> _Schedule:
         return _Schedule(self.block_n, self.round_n, int(bool(self.obar_fp32)),
                          int(bool(self.certify)), int(bool(self.ftz)),
                          self.chunk, self.chunk_err, self.exp_rel_err, int(bool(self.block_bf16)),
-                         {False: 0, True: 1, "row": 1, "fixed": 2}[self.pv_fp8], int(bool(self.pv_mxfp4)))
+                         {False: 0, True: 1, "row": 1, "fixed": 2}[self.pv_fp8], {False: 0, True: 1, "floor": 1, "ceil": 2}[self.pv_mxfp4])
 
 
 def build(verbose: bool = False) -> str:
@@ -170,8 +171,9 @@ def lib():
         for fn in ("orc_e2m1_round", "orc_e2m1_spacing", "orc_e2m1_boundary_distance"):
             getattr(L, fn).argtypes = [ctypes.c_double]
             getattr(L, fn).restype = ctypes.c_double
-        L.orc_mx_scale_byte.argtypes = [ctypes.c_double]
-        L.orc_mx_scale_byte.restype = ctypes.c_int
+        for fn in ("orc_mx_scale_byte", "orc_mx_scale_byte_ceil"):
+            getattr(L, fn).argtypes = [ctypes.c_double]
+            getattr(L, fn).restype = ctypes.c_int
         for name in ("orc_fwd_f64", "orc_bwd_f64", "orc_bwd_rows_f64", "orc_row_stats",
                      "orc_obar_f64", "orc_fwd_emu", "orc_bwd_emu", "orc_bwd_rows_emu",
                      "orc_fwd_emu_rows", "orc_delta_dp_rows_f64", "orc_dsum_rows_f64"):
@@ -266,6 +268,11 @@ def e2m1_boundary_distance(y: float) -> float:
 def mx_scale_byte(amax: float) -> int:
     """E8M0 byte of the MX block scale 2^(floor(log2 amax) - 2) (>= 1)."""
     return int(lib().orc_mx_scale_byte(float(amax)))
+
+
+def mx_scale_byte_ceil(amax: float) -> int:
+    """E8M0 byte of the rounded-up MX scale 2^(ceil(log2 amax) - 2) (>= 1)."""
+    return int(lib().orc_mx_scale_byte_ceil(float(amax)))
 
 
 def e4m3_array(x):

@@ -193,6 +193,15 @@ int orc_mx_scale_byte(double amax) {
   return b < 1 ? 1 : (b > 254 ? 254 : b);
 }
 
+/* The same with ceil(log2 amax): one more unless amax is a power of two. */
+int orc_mx_scale_byte_ceil(double amax) {
+  if (!(amax > 0.0)) return 1;
+  int e;
+  double f = frexp(amax, &e); /* f in [0.5, 1) */
+  int b = 127 + (e - 1) - 2 + (f != 0.5 ? 1 : 0);
+  return b < 1 ? 1 : (b > 254 ? 254 : b);
+}
+
 /* Error-free transformation of a + b (Knuth's TwoSum). */
 static void two_sum(double a, double b, double* s, double* e) {
   double x = a + b;
@@ -1258,13 +1267,14 @@ static void emu_head(void* c, int32_t item) {
               amax = fmax(amax, pex[j - j0]);
               rmax = fmax(rmax, prho[j - j0]);
             }
-          const int sbyte = orc_mx_scale_byte(amax);
+          int (*sbf)(double) = sc->pv_mxfp4 == 2 ? orc_mx_scale_byte_ceil : orc_mx_scale_byte;
+          const int sbyte = sbf(amax);
           const double X = ldexp(1.0, sbyte - 127);
           /* the kernel's amax is within rmax of this one: its scale may
            * be the neighbouring power of two */
           const int s_amb = cert_on && amax > 0.0 &&
-                            (orc_mx_scale_byte(amax * (1.0 - rmax - 2.0 * U24)) != sbyte ||
-                             orc_mx_scale_byte(amax * (1.0 + rmax + 2.0 * U24)) != sbyte);
+                            (sbf(amax * (1.0 - rmax - 2.0 * U24)) != sbyte ||
+                             sbf(amax * (1.0 + rmax + 2.0 * U24)) != sbyte);
           if (s_amb) val_cert = 0;
           for (int32_t j = j0; j < j1; ++j) {
             if ((((j - j0) & 7) >> 2) != h) continue;
@@ -1300,7 +1310,8 @@ static void emu_head(void* c, int32_t item) {
             const int h = ((j - j0) & 7) >> 2;
             va[h] = fmax(va[h], fabs((double)orc_f32_from_bf16(V[(size_t)j * d + f])));
           }
-          for (int h = 0; h < 2; ++h) vx[h] = ldexp(1.0, orc_mx_scale_byte(va[h]) - 127);
+          for (int h = 0; h < 2; ++h)
+            vx[h] = ldexp(1.0, (sc->pv_mxfp4 == 2 ? orc_mx_scale_byte_ceil(va[h]) : orc_mx_scale_byte(va[h])) - 127);
         }
         for (int32_t j = j0; j < j1; ++j) {
           double vv = (double)orc_f32_from_bf16(V[(size_t)j * d + f]);

@@ -83,7 +83,8 @@ typedef struct {
   /* 1: the P̄V product in MXFP4 -- P̄ and V in E2M1 elements with one E8M0
    * scale 2^(floor(log2 amax) - 2) per 32 keys (each 64-key step split by
    * key offset mod 8 below / above 4), one scaled matrix instruction per
-   * step.  Streaming schedule with block_n = 64 only.                      */
+   * step.  Streaming schedule with block_n = 64 only.  2: the scales from
+   * ceil(log2 amax) instead of floor.                                      */
   int32_t pv_mxfp4;
 } orc_schedule;
 
@@ -106,6 +107,7 @@ double orc_e2m1_round(double y);            /* RNE(clamp(y, -6, 6)) on E2M1   */
 double orc_e2m1_spacing(double y);          /* grid spacing at |y|            */
 double orc_e2m1_boundary_distance(double y);
 int orc_mx_scale_byte(double amax);         /* E8M0 byte of the block scale  */
+int orc_mx_scale_byte_ceil(double amax);    /* the same with ceil(log2 amax) */
 /* RNE to bf16 of the exact sum of n doubles (the accumulate-then-round step).
  * *exact_out (nullable) receives the exact sum rounded to double.           */
 uint16_t orc_bf16_round_of_sum(const double* terms, int32_t n, double* exact_out);

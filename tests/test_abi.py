@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 8
+    assert fa.attn_abi_version() == 9
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -64,6 +64,11 @@ def test_schedule(L):
     p = fa.make_params(1, 1, 1, 128, 64)
     p.flags |= fa.PV_FP8_FIXED  # the fixed FP8 scale without the FP8 product
     assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    p = fa.make_params(1, 1, 1, 128, 64)
+    p.flags |= fa.PV_MX_CEIL  # the MX rule without the MXFP4 product
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    p = fa.make_params(1, 1, 1, 128, 64, pv_mxfp4="ceil")
+    assert fa.attn_schedule(p)["block_n"] == 64
     with pytest.raises(ValueError):
         fa.make_params(1, 1, 1, 64, 64, schedule="blocked")
 

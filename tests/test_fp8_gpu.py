@@ -38,7 +38,7 @@ def _e4m3_bits(vbits):
     return W.to_bf16_bits(v8)
 
 
-def _mx_bits(vbits, N, d):
+def _mx_bits(vbits, N, d, ceil=False):
     """bf16 bits of V quantized as the MXFP4 product takes it (exact in bf16):
     per feature, blocks of the 32 keys of a 64-key step at offsets 0..3 or
     4..7 mod 8, scale 2^(floor(log2 amax) - 2), elements RNE(clamp(v / X))
@@ -51,7 +51,8 @@ def _mx_bits(vbits, N, d):
             idx = keys[(keys >= j0) & (keys < j0 + 64) & (((keys - j0) & 7) >> 2 == h)]
             blk = v[:, idx, :]
             amax = np.abs(blk).max(axis=1, keepdims=True)
-            X = np.where(amax > 0, 2.0 ** (np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2), 2.0 ** -126)
+            rnd = np.ceil if ceil else np.floor
+            X = np.where(amax > 0, 2.0 ** (rnd(np.log2(np.where(amax > 0, amax, 1.0))) - 2), 2.0 ** -126)
             a = np.minimum(np.abs(blk / X), 6.0)
             sp = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
             qv = np.minimum(np.round(a / sp) * sp, 6.0)
@@ -91,10 +92,11 @@ def _check_against_emulation(e, r, obar_fp32):
 
 
 # the product's format: FP8 with the row scale or the fixed 2^8, or MXFP4
-FORMATS = {"row": dict(pv_fp8="row"), "fixed": dict(pv_fp8="fixed"), "mxfp4": dict(pv_mxfp4=True)}
+FORMATS = {"row": dict(pv_fp8="row"), "fixed": dict(pv_fp8="fixed"), "mxfp4": dict(pv_mxfp4=True),
+           "mxfp4_ceil": dict(pv_mxfp4="ceil")}
 
 
-@pytest.mark.parametrize("scale", ["row", "fixed", "mxfp4"])
+@pytest.mark.parametrize("scale", ["row", "fixed", "mxfp4", "mxfp4_ceil"])
 @pytest.mark.parametrize("obar_fp32", [False, True])
 @pytest.mark.parametrize("guard", ["none", "beta", "eps"])
 @pytest.mark.parametrize("name,shape", FP8_CASES)
@@ -121,7 +123,7 @@ def test_fp8_parity(name, shape, guard, obar_fp32, scale):
     assert np.all(np.abs(o_gpu - e["o"])[rows] <= tol[rows])
     # accuracy of the variant against FP64 (real V, and the same E4M3 V)
     o64, _ = orc.fwd_f64(p, x["q"], x["k"], x["v"], nthreads=threads())
-    o64v8, _ = orc.fwd_f64(p, x["q"], x["k"], _e4m3_bits(x["v"]) if scale != "mxfp4" else x["v"],
+    o64v8, _ = orc.fwd_f64(p, x["q"], x["k"], _e4m3_bits(x["v"]) if scale in ("row", "fixed") else x["v"],
                            nthreads=threads())
     mx, mean = rel_errors(o_gpu, o64)
     mx8, mean8 = rel_errors(o_gpu, o64v8)
@@ -130,17 +132,19 @@ def test_fp8_parity(name, shape, guard, obar_fp32, scale):
            o_vs_e4m3V_max_rel=f"{mx8:.2e}", o_vs_e4m3V_mean_rel=f"{mean8:.2e}")
 
 
+@pytest.mark.parametrize("scale", ["row", "mxfp4"])
 @pytest.mark.parametrize("guard", ["beta", "none"])
-def test_fp8_full_size_sampled(guard):
+def test_fp8_full_size_sampled(guard, scale):
     """GPT-2 Small in the benchmark's launch configuration, sampled heads."""
     x = make("gpt2s")
     wl = x["workload"]
     p = problem(wl, guard)
     heads = [3, 140]
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    r = fa.attn_fwd(q, k, v, causal=True, guard=guard, pv_fp8="row", return_obar=True)
+    fmt = FORMATS[scale]
+    r = fa.attn_fwd(q, k, v, causal=True, guard=guard, return_obar=True, **fmt)
     torch.cuda.synchronize()
-    e = orc.fwd_emu(p, schedule(p, pv_fp8="row"), x["q"], x["k"], x["v"], heads=heads, nthreads=threads())
+    e = orc.fwd_emu(p, schedule(p, **fmt), x["q"], x["k"], x["v"], heads=heads, nthreads=threads())
     N, d = wl.seqlen, wl.head_dim
     e = {kk: (vv.reshape(-1, N, d)[heads] if vv.size == q.numel() else vv.reshape(-1, N)[heads])
          for kk, vv in e.items()}
@@ -152,7 +156,7 @@ def test_fp8_full_size_sampled(guard):
     o64 = o64.reshape(-1, wl.seqlen, wl.head_dim)[heads]
     o_gpu = f32(r["o"]).reshape(-1, wl.seqlen, wl.head_dim)[heads]
     mx, mean = rel_errors(o_gpu, o64)
-    report(f"fp8 gpt2s {guard} heads {heads}", **nums, o_max_rel=f"{mx:.2e}", o_mean_rel=f"{mean:.2e}")
+    report(f"{scale} gpt2s {guard} heads {heads}", **nums, o_max_rel=f"{mx:.2e}", o_mean_rel=f"{mean:.2e}")
 
 
 def _tie_projection(x, wl, heads, err, l64, tie, m, tie_eps=1e-3, block_n=64, vref=None):
@@ -206,6 +210,7 @@ def test_fp8_bias_study():
     heads = list(range(0, 192, 12))
     v8bits = _e4m3_bits(x["v"])
     vmxbits = _mx_bits(x["v"], wl.seqlen, wl.head_dim)
+    vmxcbits = _mx_bits(x["v"], wl.seqlen, wl.head_dim, ceil=True)
     res = {}
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     vf8 = W.bits_to_f32(v8bits).astype(np.float64).reshape(-1, wl.seqlen, wl.head_dim)
@@ -213,8 +218,8 @@ def test_fp8_bias_study():
     kvh = [(h // wl.heads_q) * wl.heads_kv + (h % wl.heads_q) // g for h in heads]
     neg = vf8[kvh].mean(axis=1) < 0
     shp = (-1, wl.seqlen, wl.head_dim)
-    for scale in ("row", "fixed", "mxfp4"):
-        vref = vmxbits if scale == "mxfp4" else v8bits
+    for scale in ("row", "fixed", "mxfp4", "mxfp4_ceil"):
+        vref = {"mxfp4": vmxbits, "mxfp4_ceil": vmxcbits}.get(scale, v8bits)
         for guard in ("none", "beta", "eps"):
             p = problem(wl, guard)
             st = orc.row_stats(p, x["q"], x["k"], schedule(p), heads=heads, nthreads=threads())
@@ -256,3 +261,31 @@ def test_fp8_bias_study():
     for f32_ in (False, True):
         assert abs(res[("mxfp4", "eps", f32_)][0] - want_mx) < 0.25 * abs(want_mx), res
         assert -0.27 < res[("mxfp4", "none", f32_)][0] < 0.01, res
+    # The rounded-up scale rule: 0.969 * 4 = 3.88 rounds to 4, so under the
+    # eps guard the tied keys weigh 1 (+0.032, as under FP8); unguarded, the
+    # maximum's P̄ = 1 keeps its weight.  Every MXFP4 coefficient also holds a
+    # common offset near -0.04: the other keys lose weight in E2M1 rounding
+    # (everything under a quarter of the scale goes to zero), and that loss
+    # reaches the tied keys' direction through V's nonzero feature means (the
+    # oracle's emulation with V centred per feature gives +0.031 and 0.000
+    # for the rounded-up rule, -0.224 for the OCP rule under eps).  So each
+    # MXFP4 coefficient (fp32 Ō) must match the oracle's emulation of the
+    # same rule on the same inputs, and the rounded-up rule must lose far
+    # less weight than the OCP rule.
+    p_by = {g: problem(wl, g) for g in ("none", "eps")}
+    for scale, rule in (("mxfp4", "floor"), ("mxfp4_ceil", "ceil")):
+        vref = vmxbits if rule == "floor" else vmxcbits
+        for guard in ("none", "eps"):
+            p = p_by[guard]
+            sc = orc.Schedule(block_n=64, round_n=512, obar_fp32=True, certify=False, chunk=16, pv_mxfp4=rule)
+            e = orc.fwd_emu(p, sc, x["q"], x["k"], x["v"], heads=heads, nthreads=threads())
+            st = orc.row_stats(p, x["q"], x["k"], sc, heads=heads, nthreads=threads())
+            ob64, l64 = orc.obar_f64(p, x["q"], x["k"], vref, st["m"], heads=heads, nthreads=threads())
+            err = (e["obar"].reshape(shp)[heads] - ob64.reshape(shp)[heads]) / l64.reshape(-1, wl.seqlen)[heads][..., None]
+            tie = (((st["flags"] & orc.ROW_TIE) != 0) & st["flag_cert"].astype(bool)).reshape(-1, wl.seqlen)[heads]
+            c_emu = _tie_projection(x, wl, heads, err, l64.reshape(-1, wl.seqlen)[heads], tie, st["m"], vref=vref)
+            report(f"mxfp4 {rule} {guard}: tie-key coefficient", gpu=f"{res[(scale, guard, True)][0]:+.4f}",
+                   emulated=f"{c_emu:+.4f}")
+            assert abs(res[(scale, guard, True)][0] - c_emu) < 0.01, (scale, guard, c_emu, res)
+    for guard in ("none", "eps"):
+        assert abs(res[("mxfp4_ceil", guard, True)][0]) < 0.5 * abs(res[("mxfp4", guard, True)][0]), res

@@ -255,23 +255,33 @@ def test_mx_scale_rule(orc):
         X = 2.0 ** (b - 127)
         assert 4.0 <= amax / X < 8.0, amax
     assert orc.mx_scale_byte(1.0) == 125 and orc.mx_scale_byte(0.969) == 124 and orc.mx_scale_byte(0.0) == 1
+    # the rounded-up rule: amax / X in (2, 4], equal at powers of two
+    for amax in (1.0, 0.969, 6.0, 7.99, 0.001, 3.0e-7, 255.0, 0.5):
+        b = orc.mx_scale_byte_ceil(amax)
+        X = 2.0 ** (b - 127)
+        assert 2.0 < amax / X <= 4.0, amax
+    assert orc.mx_scale_byte_ceil(1.0) == 125 and orc.mx_scale_byte_ceil(0.969) == 125
 
 
-def _mx_quant(v):
+def _mx_quant(v, ceil=False):
     """numpy reference of one MX block: scale from the largest magnitude."""
     v = np.asarray(v, np.float64)
     amax = np.abs(v).max()
-    X = 2.0 ** (np.floor(np.log2(amax)) - 2) if amax > 0 else 2.0 ** -126
+    rnd = np.ceil if ceil else np.floor
+    X = 2.0 ** (rnd(np.log2(amax)) - 2) if amax > 0 else 2.0 ** -126
     return np.array([_nearest_e2m1(t / X) for t in v]) * X
 
 
+@pytest.mark.parametrize("rule", ["floor", "ceil"])
 @pytest.mark.parametrize("guard", ["none", "eps"])
-def test_mxfp4_q0_closed_form(orc, guard):
+def test_mxfp4_q0_closed_form(orc, guard, rule):
     """Q = 0: every P̄ of a row is equal.  No guard: P̄ = 1, X = 1/4, 4 is
     exact, Ō = sum_j q(V_j).  The eps guard: P̄ = exp(-2^-5) = 0.969, X =
     1/8, 0.969 * 8 = 7.75 saturates to 6: every operand is 0.75, so Ō is 0.75
-    sum_j q(V_j) while ℓ = N exp(-2^-5) (O 23 % too small).  V's blocks: per
-    feature, the 64-key step's keys split by offset mod 8 below / above 4."""
+    sum_j q(V_j) while ℓ = N exp(-2^-5) (O 23 % too small).  With the rule
+    rounded up, X = 1/4 and 3.88 rounds to 4: every operand is 1, O 3.2 %
+    too large, as with FP8.  V's blocks: per feature, the 64-key step's keys
+    split by offset mod 8 below / above 4."""
     N, d = 40, 64
     g = {"none": orc.GUARD_NONE, "eps": orc.GUARD_EPS}[guard]
     p, q, k, v = _q0_case(orc, N, d, g, 5)
@@ -280,15 +290,16 @@ def test_mxfp4_q0_closed_form(orc, guard):
     for f in range(d):
         for h in range(2):
             idx = [j for j in range(N) if ((j & 7) >> 2) == h]
-            vq[idx, f] = _mx_quant(vf[idx, f])
-    pq = 1.0 if guard == "none" else 0.75
-    s = orc.Schedule(block_n=64, round_n=512, obar_fp32=True, certify=False, pv_mxfp4=True)
+            vq[idx, f] = _mx_quant(vf[idx, f], ceil=rule == "ceil")
+    pq = 1.0 if guard == "none" or rule == "ceil" else 0.75
+    s = orc.Schedule(block_n=64, round_n=512, obar_fp32=True, certify=False, pv_mxfp4=rule)
     e = orc.fwd_emu(p, s, q, k, v)
     want = pq * vq.sum(axis=0)
     assert np.allclose(e["obar"][0, 0], np.broadcast_to(want, (N, d)), rtol=1e-12, atol=1e-12)
     if guard == "eps":
-        ratio = (want / e["l"][0, 0][:, None]) / (vq.sum(axis=0) / N)
-        assert np.allclose(ratio[:, np.abs(vq.sum(axis=0)) > 1.0], 0.75 / np.exp(-(2.0 ** -5)), rtol=1e-5)
+        cols = np.abs(vq.sum(axis=0)) > 1.0
+        ratio = (want[cols] / e["l"][0, 0][:, None]) / (vq.sum(axis=0)[cols] / N)
+        assert np.allclose(ratio, pq / np.exp(-(2.0 ** -5)), rtol=1e-5)
 
 
 def test_mxfp4_single_block_direct(orc):
