@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd.hip", "attn_device.h", "attn_internal.h")}
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
-        "sources_sha256": "9d56f5d6afa960d9996f00cb1d0e455718f044629e73ad58ed60efd2191241ef",
-        "fetch_kib": 64237.0, "write_kib": 51211.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "adf437863bdfb53ad269d34120cc708390af91bd7a618a5286543234d46517a2",
+        "fetch_kib": 64207.0, "write_kib": 51205.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
