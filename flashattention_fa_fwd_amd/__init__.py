@@ -118,17 +118,28 @@ def _params_from(q, k, **kw) -> Params:
     return make_params(B, Hq, k.shape[1], N, d, **kw)
 
 
-def _check_bf16(name, t, shape=None):
-    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
-        raise TypeError(f"{name} must be a bfloat16 tensor on a HIP device")
+def _check(name, t, dtype, shape=None, device=None):
+    """The library reads and writes through raw device pointers sized from
+    the parameters: every tensor must have exactly the expected dtype, shape
+    and layout, on the device of q."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} tensor on a HIP device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous ([batch, heads, seqlen, head_dim])")
+        raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
+def _check_bf16(name, t, shape=None, device=None):
+    _check(name, t, torch.bfloat16, shape, device)
+
+
+def _stream(stream, device=None):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if device is not None and s.device != device:
+        raise ValueError(f"stream is on {s.device}, the tensors on {device}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -159,27 +170,38 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
     pv_mxfp4: P̄V in MXFP4 (streaming kernel only).
     Returns a dict: o, row_m, row_l, row_flags (+ obar, row_max on request)."""
     _check_bf16("q", q)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [batch, heads, seqlen, head_dim], not {tuple(q.shape)}")
     B, Hq, N, d = q.shape
-    _check_bf16("k", k, (B, k.shape[1], N, d))
-    _check_bf16("v", v, k.shape)
+    dev = q.device
+    _check_bf16("k", k, (B, k.shape[1], N, d) if k.dim() == 4 else None, dev)
+    _check_bf16("v", v, k.shape, dev)
     p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
                      shift_eps=shift_eps, obar_fp32=obar_fp32, softmax_scale=softmax_scale,
                      schedule=schedule, pv_fp8=pv_fp8, pv_mxfp4=pv_mxfp4)
-    dev = q.device
     res = out if out is not None else {}
     if "o" not in res:
         res["o"] = torch.empty_like(q)
         res["row_m"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
         res["row_l"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
         res["row_flags"] = torch.empty((B, Hq, N), dtype=torch.uint8, device=dev)
-        if return_obar:
-            res["obar"] = torch.empty(q.shape, dtype=torch.float32 if obar_fp32 else torch.bfloat16, device=dev)
-        if return_row_max:
-            res["row_max"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    if return_obar and "obar" not in res:
+        res["obar"] = torch.empty(q.shape, dtype=torch.float32 if obar_fp32 else torch.bfloat16, device=dev)
+    if return_row_max and "row_max" not in res:
+        res["row_max"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    rows = (B, Hq, N)
+    _check_bf16("o", res["o"], q.shape, dev)
+    _check("row_m", res["row_m"], torch.float32, rows, dev)
+    _check("row_l", res["row_l"], torch.float32, rows, dev)
+    _check("row_flags", res["row_flags"], torch.uint8, rows, dev)
+    if res.get("obar") is not None:
+        _check("obar", res["obar"], torch.float32 if obar_fp32 else torch.bfloat16, q.shape, dev)
+    if res.get("row_max") is not None:
+        _check("row_max", res["row_max"], torch.float32, rows, dev)
     _call("attn_fwd", lib().attn_fwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(res["o"]), _ptr(res["row_m"]),
         _ptr(res["row_l"]), _ptr(res["row_flags"]), _ptr(res.get("obar")), _ptr(res.get("row_max")),
-        _stream(stream)))
+        _stream(stream, dev)))
     return res
 
 
@@ -189,11 +211,19 @@ def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=
     """Backward.  Returns a dict: dq, dk, dv (bf16) and delta (fp32), and with
     row_dsum=True the row sums of dS (fp32, without alpha).  delta="dp_p"
     forms delta = rowsum(dP∘P) (o is then not read; it may be None)."""
-    for n_, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if t is None and n_ == "o" and delta == "dp_p":
-            continue
-        _check_bf16(n_, t)
+    _check_bf16("q", q)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [batch, heads, seqlen, head_dim], not {tuple(q.shape)}")
     B, Hq, N, d = q.shape
+    dev = q.device
+    _check_bf16("k", k, (B, k.shape[1], N, d) if k.dim() == 4 else None, dev)
+    _check_bf16("v", v, k.shape, dev)
+    if not (o is None and delta == "dp_p"):
+        _check_bf16("o", o, q.shape, dev)
+    _check_bf16("dout", dout, q.shape, dev)
+    rows = (B, Hq, N)
+    _check("row_m", row_m, torch.float32, rows, dev)
+    _check("row_l", row_l, torch.float32, rows, dev)
     p = _params_from(q, k, causal=causal, guard=guard, beta=beta, tie_eps=tie_eps,
                      shift_eps=shift_eps, softmax_scale=softmax_scale, delta=delta)
     res = out if out is not None else {}
@@ -201,26 +231,57 @@ def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=
         res["dq"] = torch.empty_like(q)
         res["dk"] = torch.empty_like(k)
         res["dv"] = torch.empty_like(v)
-        res["delta"] = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        res["delta"] = torch.empty(rows, dtype=torch.float32, device=dev)
     if row_dsum and "row_dsum" not in res:
-        res["row_dsum"] = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        res["row_dsum"] = torch.empty(rows, dtype=torch.float32, device=dev)
+    _check_bf16("dq", res["dq"], q.shape, dev)
+    _check_bf16("dk", res["dk"], k.shape, dev)
+    _check_bf16("dv", res["dv"], k.shape, dev)
+    _check("delta", res["delta"], torch.float32, rows, dev)
+    if row_dsum:
+        _check("row_dsum", res["row_dsum"], torch.float32, rows, dev)
     _call("attn_bwd", lib().attn_bwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
         _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["delta"]),
-        _ptr(res.get("row_dsum") if row_dsum else None), _stream(stream)))
+        _ptr(res.get("row_dsum") if row_dsum else None), _stream(stream, dev)))
     return res
 
 
+def _stage_shapes(p: Params):
+    qs = (p.batch, p.heads_q, p.seqlen, p.head_dim)
+    ks = (p.batch, p.heads_kv, p.seqlen, p.head_dim)
+    return qs, ks, (p.batch, p.heads_q, p.seqlen)
+
+
 def attn_bwd_dkdv(p: Params, q, k, v, dout, row_m, row_l, delta, dk, dv, stream=None):
+    """The backward's dK/dV stage (delta from attn_bwd_dq)."""
+    qs, ks, rows = _stage_shapes(p)
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    for n_, t, sh in (("q", q, qs), ("k", k, ks), ("v", v, ks), ("dout", dout, qs), ("dk", dk, ks), ("dv", dv, ks)):
+        _check_bf16(n_, t, sh, dev)
+    for n_, t in (("row_m", row_m), ("row_l", row_l), ("delta", delta)):
+        _check(n_, t, torch.float32, rows, dev)
     _call("attn_bwd_dkdv", lib().attn_bwd_dkdv(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(row_m), _ptr(row_l),
-        _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream)))
+        _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream, dev)))
 
 
 def attn_bwd_dq(p: Params, q, k, v, o, dout, row_m, row_l, dq, delta, row_dsum=None, stream=None):
+    """The backward's dQ stage; it also writes delta (o unused, may be None,
+    when p.flags holds DELTA_DP)."""
+    qs, ks, rows = _stage_shapes(p)
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    for n_, t, sh in (("q", q, qs), ("k", k, ks), ("v", v, ks), ("dout", dout, qs), ("dq", dq, qs)):
+        _check_bf16(n_, t, sh, dev)
+    if not (o is None and p.flags & DELTA_DP):
+        _check_bf16("o", o, qs, dev)
+    for n_, t in (("row_m", row_m), ("row_l", row_l), ("delta", delta)):
+        _check(n_, t, torch.float32, rows, dev)
+    if row_dsum is not None:
+        _check("row_dsum", row_dsum, torch.float32, rows, dev)
     _call("attn_bwd_dq", lib().attn_bwd_dq(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
-        _ptr(dq), _ptr(delta), _ptr(row_dsum), _stream(stream)))
+        _ptr(dq), _ptr(delta), _ptr(row_dsum), _stream(stream, dev)))
 
 
 def default_scale(head_dim: int) -> float:

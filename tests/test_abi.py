@@ -156,3 +156,20 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_lib", None)
     with pytest.raises(ImportError):
         fa.lib()
+
+
+def test_binding_rejects_host_and_mistyped_tensors():
+    """The binding checks dtype, device and layout before any pointer reaches
+    the library (host tensors here, so no library call is made)."""
+    import torch
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        fa.attn_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        fa.attn_fwd(q.float(), q, q)
+    m = torch.zeros((1, 1, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        fa.attn_bwd(q, q, q, q, q, m, m)
+    p = fa.make_params(1, 1, 1, 64, 64)
+    with pytest.raises(TypeError):
+        fa.attn_bwd_dkdv(p, q, q, q, q, m, m, m, q, q)

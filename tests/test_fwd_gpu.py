@@ -237,3 +237,20 @@ def test_output_is_the_ieee_quotient(obar_fp32):
     got = bits(r["o"])
     assert np.array_equal(got, want), int((got != want).sum())
     report(f"O = bf16(Ō/ℓ) {'fp32' if obar_fp32 else 'bf16'} Ō", elements=got.size)
+
+
+def test_binding_rejects_mismatched_outputs():
+    """Output and statistics tensors of the wrong shape or dtype are refused
+    before the library is called (it would write past them)."""
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    r = fa.attn_fwd(q, q, q)
+    bad = dict(r)
+    bad["row_m"] = torch.empty((1, 2, 32), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fa.attn_fwd(q, q, q, out=bad)
+    with pytest.raises(TypeError):
+        fa.attn_bwd(q, q, q, r["o"], q, r["row_m"].double(), r["row_l"])
+    with pytest.raises(ValueError):
+        fa.attn_bwd(q, q[:, :1].contiguous(), q, r["o"], q, r["row_m"], r["row_l"])
+    with pytest.raises(ValueError):
+        fa.attn_bwd(q, q, q, r["o"], q, r["row_m"][:, :1].contiguous(), r["row_l"])
