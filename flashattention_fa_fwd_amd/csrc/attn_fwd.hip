@@ -122,6 +122,9 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
   constexpr int FB = D / 32;     // 32-feature blocks of O^T
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
+  // FP8 product: the step's V^T operand in E4M3, in operand order ([16-key
+  // group t][feature block f][lane], 8 keys a lane); wave w converts group w
+  __shared__ __attribute__((aligned(16))) uint2 Vf8[PV == kPvFp8 ? 4 * (D / 32) * 64 : 1];
 
   const int tid = threadIdx.x;
   // the wave index is uniform over the wave: keeping it scalar makes every
@@ -193,6 +196,17 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
   // set across the computing steps.
   const int jc = !wave_live ? 0 : (CAUSAL ? min(kend, q0 + 32) : kend);
 
+  // FP8 product: this wave's share (keys 16*wave .. 16*wave + 15) of the
+  // step's E4M3 V^T operand, written for every wave to read after a barrier
+  auto convert_v = [&](const uint16_t* vs) {
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      const int o0 = ta_off[f][0] + 16 * wave * D, o1 = ta_off[f][1] + 16 * wave * D;
+      const uint2 v0 = lds_read_tr(vs + o0), v1 = lds_read_tr(vs + o1);
+      Vf8[(wave * FB + f) * 64 + lane] = make_uint2(fp8x4_from_bf16x4(v0), fp8x4_from_bf16x4(v1));
+    }
+  };
+
   dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
   dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
   int j0 = 0;
@@ -226,6 +240,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
         const bf16x8 kf = *(const bf16x8*)(&ks[ka_off[kb][t]]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
       }
+    if constexpr (PV_FP8) convert_v(vs);
     // key of s[kb][i] in this lane: j0 + 32kb + 8(i/4) + 4*half + i%4; only
     // the block holding the diagonal (causal) or the sequence end masks
     const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > q0);
@@ -364,18 +379,21 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
         oacc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pmb, oacc[f], 4, 4, 0, sbv, 0, sbp);
       }
     }
+    // every wave's share of the E4M3 operand is in LDS
+    if constexpr (PV_FP8) __syncthreads();
 #pragma unroll
     for (int t = 0; t < (PV_MX ? 0 : 4); ++t) {
 #pragma unroll
       for (int f = 0; f < FB; ++f) {
         // A = V^T: feature 32f + l32, keys 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
-        const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
-        const uint2 v0 = lds_read_tr(vs + o0), v1 = lds_read_tr(vs + o1);
         if (PV_FP8) {
-          const long va = (long)(((uint64_t)fp8x4_from_bf16x4(v1) << 32) | fp8x4_from_bf16x4(v0));
+          const uint2 w = Vf8[(t * FB + f) * 64 + lane];
+          const long va = (long)(((uint64_t)w.y << 32) | w.x);
           const long pb = (long)(((uint64_t)pf8[t][1] << 32) | pf8[t][0]);
           oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(va, pb, oacc[f], 0, 0, 0);
         } else {
+          const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
+          const uint2 v0 = lds_read_tr(vs + o0), v1 = lds_read_tr(vs + o1);
           oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag2(v0, v1), pf[t], oacc[f], 0, 0, 0);
         }
       }
@@ -397,6 +415,11 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
     if (j0 + BN < kend) {
       dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, Ks[cur ^ 1]);
       dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, Vs[cur ^ 1]);
+    }
+    // FP8 product: the waves still computing need this wave's share
+    if constexpr (PV_FP8) {
+      convert_v(Vs[cur]);
+      __syncthreads();
     }
   }
   // no copy may still be writing LDS when the workgroup ends
