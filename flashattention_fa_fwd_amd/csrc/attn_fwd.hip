@@ -125,6 +125,11 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
   // FP8 product: the step's V^T operand in E4M3, in operand order ([16-key
   // group t][feature block f][lane], 8 keys a lane); wave w converts group w
   __shared__ __attribute__((aligned(16))) uint2 Vf8[PV == kPvFp8 ? 4 * (D / 32) * 64 : 1];
+  // MXFP4 product: the step's V^T operand (E2M1 elements of the lane's 32
+  // keys, [feature block f][lane]) and its E8M0 scale bytes; wave w converts
+  // the feature blocks f = w, w + 4, ...
+  __shared__ __attribute__((aligned(16))) uint4 Vmx[PV == kPvMx ? (D / 32) * 64 : 1];
+  __shared__ __attribute__((aligned(16))) int Smx[PV == kPvMx ? (D / 32) * 64 : 1];
 
   const int tid = threadIdx.x;
   // the wave index is uniform over the wave: keeping it scalar makes every
@@ -198,6 +203,34 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
 
   // FP8 product: this wave's share (keys 16*wave .. 16*wave + 15) of the
   // step's E4M3 V^T operand, written for every wave to read after a barrier
+  // MXFP4 product: this wave's feature blocks of the step's V^T operand,
+  // quantized (per lane: one feature, the 32 keys of its half) into LDS
+  auto convert_mx = [&](const uint16_t* vs) {
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      if (f % kWaves != wave) continue;  // uniform: static register indices below
+      // V^T, k order 8t + 4e + u: keys 16t + 8e + 4*half + u of feature 32f + l32
+      float vx[32];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint2 v0 = lds_read_tr(vs + ta_off[f][0] + 16 * t * D);
+        const uint2 v1 = lds_read_tr(vs + ta_off[f][1] + 16 * t * D);
+        const uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          vx[8 * t + 2 * q] = __uint_as_float(w[q] << 16);
+          vx[8 * t + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(fabsf(vx[j]), fabsf(vx[j + 1])));
+      const int sbv = mx_scale_byte(amax, a.pv_mx_ceil != 0);
+      const float xs = __int_as_float(sbv << 23);
+      Vmx[f * 64 + lane] = make_uint4(fp4x8(&vx[0], xs), fp4x8(&vx[8], xs), fp4x8(&vx[16], xs), fp4x8(&vx[24], xs));
+      Smx[f * 64 + lane] = sbv;
+    }
+  };
   auto convert_v = [&](const uint16_t* vs) {
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
@@ -241,6 +274,7 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
       }
     if constexpr (PV_FP8) convert_v(vs);
+    if constexpr (PV_MX) convert_mx(vs);
     // key of s[kb][i] in this lane: j0 + 32kb + 8(i/4) + 4*half + i%4; only
     // the block holding the diagonal (causal) or the sequence end masks
     const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > q0);
@@ -351,36 +385,18 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
 
     // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order (the feature
     // blocks' chains interleaved); MXFP4: one step of 64 keys
+    // every wave's share of the low-precision V^T operand is in LDS
+    if constexpr (PV_FP8 || PV_MX) __syncthreads();
     if (PV_MX) {
 #pragma unroll
       for (int f = 0; f < FB; ++f) {
-        // V^T, k order 8t + 4e + u: keys 16t + 8e + 4*half + u of feature 32f + l32
-        float vx[32];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint2 v0 = lds_read_tr(vs + ta_off[f][0] + 16 * t * D);
-          const uint2 v1 = lds_read_tr(vs + ta_off[f][1] + 16 * t * D);
-          const uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            vx[8 * t + 2 * q] = __uint_as_float(w[q] << 16);
-            vx[8 * t + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-          }
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(fabsf(vx[j]), fabsf(vx[j + 1])));
-        const int sbv = mx_scale_byte(amax, a.pv_mx_ceil != 0);
-        const float xs = __int_as_float(sbv << 23);
-        i32x8 va = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) va[w] = (int)fp4x8(&vx[8 * w], xs);
+        const uint4 w = Vmx[f * 64 + lane];
+        const int sbv = Smx[f * 64 + lane];
+        const i32x8 va = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
         // formats 4, 4: E2M1 operands; scale bytes in bits 0..7
         oacc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pmb, oacc[f], 4, 4, 0, sbv, 0, sbp);
       }
     }
-    // every wave's share of the E4M3 operand is in LDS
-    if constexpr (PV_FP8) __syncthreads();
 #pragma unroll
     for (int t = 0; t < (PV_MX ? 0 : 4); ++t) {
 #pragma unroll
@@ -416,11 +432,10 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
       dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, Ks[cur ^ 1]);
       dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, Vs[cur ^ 1]);
     }
-    // FP8 product: the waves still computing need this wave's share
-    if constexpr (PV_FP8) {
-      convert_v(Vs[cur]);
-      __syncthreads();
-    }
+    // low-precision products: the waves still computing need this wave's share
+    if constexpr (PV_FP8) convert_v(Vs[cur]);
+    if constexpr (PV_MX) convert_mx(Vs[cur]);
+    if constexpr (PV_FP8 || PV_MX) __syncthreads();
   }
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
