@@ -201,8 +201,6 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
   // set across the computing steps.
   const int jc = !wave_live ? 0 : (CAUSAL ? min(kend, q0 + 32) : kend);
 
-  // FP8 product: this wave's share (keys 16*wave .. 16*wave + 15) of the
-  // step's E4M3 V^T operand, written for every wave to read after a barrier
   // MXFP4 product: this wave's feature blocks of the step's V^T operand,
   // quantized (per lane: one feature, the 32 keys of its half) into LDS
   auto convert_mx = [&](const uint16_t* vs) {
@@ -231,6 +229,8 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
       Smx[f * 64 + lane] = sbv;
     }
   };
+  // FP8 product: this wave's share (keys 16*wave .. 16*wave + 15) of the
+  // step's E4M3 V^T operand, written for every wave to read after a barrier
   auto convert_v = [&](const uint16_t* vs) {
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
