@@ -78,7 +78,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the attention path runs on one GPU (no cross-GPU sharding is implemented); --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
