@@ -46,6 +46,10 @@ int check_params(const attn_params* p) {
   const double elems = (double)p->batch * p->heads_q * p->seqlen * p->head_dim;
   if (elems > 9.0e15) return ATTN_E_SHAPE;
   if ((double)p->seqlen * p->head_dim * 2.0 >= 2147483648.0) return ATTN_E_SHAPE;
+  // a launch covers at most 2^32 - 1 work-items: 256-thread workgroups of
+  // 128 query rows (forward, dQ) or keys (dK/dV, fewer heads)
+  const double groups = (double)p->batch * p->heads_q * ((p->seqlen + 127) / 128);
+  if (groups > 16777215.0) return ATTN_E_SHAPE;
   return ATTN_OK;
 }
 

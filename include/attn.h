@@ -66,7 +66,9 @@ extern "C" {
 #define ATTN_OK 0
 #define ATTN_E_NULL (-1)        /* a required pointer is NULL                   */
 #define ATTN_E_SHAPE (-2)       /* non-positive size, heads_q % heads_kv != 0,
-                                   or seqlen*head_dim*2 >= 2^31                 */
+                                   seqlen*head_dim*2 >= 2^31, or more than
+                                   2^24 - 1 workgroups of 128 rows
+                                   (batch*heads_q*ceil(seqlen/128))          */
 #define ATTN_E_UNSUPPORTED (-3) /* head_dim not 64/128, misaligned pointer      */
 #define ATTN_E_PARAM (-4)       /* bad beta/tie_eps/shift_eps/flags/scale       */
 #define ATTN_E_HIP (-6)         /* the HIP runtime refused a launch             */

@@ -85,6 +85,8 @@ def _fwd(L, p, ptrs=None, obar=None):
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), -2), (dict(heads_q=3, heads_kv=2), -2), (dict(seqlen=0), -2),
     (dict(head_dim=96), -3), (dict(head_dim=32), -3),
+    # more workgroups of 128 rows than one launch can address (2^24 - 1)
+    (dict(batch=1 << 16, heads_q=256, heads_kv=256, seqlen=129), -2),
 ])
 def test_shape_errors(L, kw, code):
     args = dict(batch=1, heads_q=2, heads_kv=1, seqlen=64, head_dim=64)
