@@ -160,6 +160,28 @@ def main():
           f"fwd with guard={other}: {ms_fwd_other:.4f}; bwd with delta=rowsum(dP*P): "
           f"{ms_bwd_dp:.4f}", file=sys.stderr, flush=True)
 
+    # ---- cold caches: before each step a 1 GiB buffer is written (more than
+    # the 8 XCDs' L2 and the last-level cache hold together), so the step
+    # reads its inputs from HBM; HIP events around the forward and the
+    # backward of each step only (the fill is outside them); medians
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    n_cold = max(20, min(args.steps, 100))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_cold)]
+    for i in range(n_cold):
+        flush.fill_(i & 0xFF)
+        evs[i][0].record(stream)
+        fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
+        evs[i][1].record(stream)
+        fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], out=bout, **kw)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    cold_fwd = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    cold_bwd = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    cold_step = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+    del flush
+    print(f"[bench] cold caches (median of {n_cold}): step {cold_step:.4f} ms, fwd {cold_fwd:.4f}, "
+          f"bwd {cold_bwd:.4f}", file=sys.stderr, flush=True)
+
     if args.copy_calibration:
         src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -212,6 +234,9 @@ def main():
         "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
         "fwd_ms_variants": variants,
         "bwd_ms_delta": {"rowsum(dO*O)": round(ms_dq + ms_dkdv, 5), "rowsum(dP*P)": round(ms_bwd_dp, 5)},
+        "cold": {"ms_per_step": round(cold_step, 5), "tflops": round(fl_step / (cold_step * 1e-3) / 1e12, 2),
+                 "fwd_ms": round(cold_fwd, 5), "bwd_ms": round(cold_bwd, 5), "steps": n_cold,
+                 "flush_bytes": 1 << 30},
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
