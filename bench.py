@@ -250,6 +250,7 @@ def main():
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, wl, args)
+        rec["cpu_emulation"] = cpu_emulation(args)
     print(json.dumps(rec), flush=True)
 
 
@@ -278,6 +279,29 @@ def cpu_baseline(x, wl, args):
         "sample": f"FP64 forward+backward of {len(heads)} of {wl.batch * wl.heads_kv} KV heads "
                   f"({len(heads) * g} query heads) of the {wl.name} workload, {dt:.2f} s wall",
     }
+
+
+def cpu_emulation(args):
+    """The oracle's bit-level BF16 replay of the forward (with its rounding
+    certification) on the tiny workload, one thread: the cost of the check
+    that the bit-exact tests rest on."""
+    import oracle as orc
+    import flashattention_fa_fwd_amd as fa
+    from flashattention_fa_fwd_amd import workloads as W
+
+    xt = W.make("tiny")
+    wt = xt["workload"]
+    p = orc.Problem(wt.batch, wt.heads_q, wt.heads_kv, wt.seqlen, wt.head_dim, wt.causal,
+                    {"none": 0, "beta": 1, "eps": 2}[args.guard])
+    s = fa.attn_schedule(fa.make_params(wt.batch, wt.heads_q, wt.heads_kv, wt.seqlen, wt.head_dim,
+                                        causal=wt.causal))
+    sc = orc.Schedule(block_n=s["block_n"], round_n=s["round_n"], obar_fp32=False, chunk=s["chunk"],
+                      certify=True, block_bf16=bool(s["block_bf16"]))
+    t0 = time.perf_counter()
+    orc.fwd_emu(p, sc, xt["q"], xt["k"], xt["v"], nthreads=1)
+    dt = time.perf_counter() - t0
+    return {"seconds": round(dt, 4), "threads": 1, "kind": "oracle",
+            "sample": f"certified BF16 replay of the forward, {wt.description}"}
 
 
 if __name__ == "__main__":
