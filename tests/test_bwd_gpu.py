@@ -337,3 +337,45 @@ def test_row_dsum_is_minus_the_delta_error():
            mean_abs=f"{scale:.3e}", eq3_sum_mean=f"{per_head.mean().item():+.3e}",
            eq3_positive_heads=f"{int((per_head > 0).sum())}/{per_head.numel()}",
            resid_mean_abs=f"{resid.abs().mean().item():.2e}")
+
+
+def test_step_replays_from_a_hip_graph():
+    """The library launches kernels only (no allocation, no memset, no
+    synchronisation), so a whole forward+backward step can be captured in a
+    HIP graph: every replay, with eager work and synchronisations between
+    the replays, equals the eager step bit for bit."""
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, N, d = 2, 4, 2, 300, 64
+    q = torch.from_numpy(rng.standard_normal((B, Hq, N, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, N, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, N, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    do = torch.from_numpy(rng.standard_normal((B, Hq, N, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    fo, bo = {}, {}
+
+    def step():
+        fa.attn_fwd(q, k, v, causal=True, guard="beta", out=fo)
+        fa.attn_bwd(q, k, v, fo["o"], do, fo["row_m"], fo["row_l"], causal=True, guard="beta", out=bo)
+
+    step()
+    torch.cuda.synchronize()
+    names = ("o", "row_m", "row_l", "row_flags", "dq", "dk", "dv", "delta")
+    outs = lambda: [fo[n] if n in fo else bo[n] for n in names]
+    ref = [t.clone() for t in outs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in outs():
+            t.fill_(0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, a, b in zip(names, ref, outs()):
+            assert torch.equal(a, b), (r, n)
