@@ -67,7 +67,7 @@ def lib():
         L.attn_abi_version.restype = ctypes.c_int
         L.attn_strerror.argtypes = [ctypes.c_int]
         L.attn_strerror.restype = ctypes.c_char_p
-        L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p, i32p]
+        L.attn_schedule.argtypes = [pp, i32p, i32p, i32p, i32p, i32p, i32p]
         L.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -153,11 +153,12 @@ def _call(name, rc):
 
 
 def attn_schedule(p: Params):
-    bm, bn, rn, ch, bb = (ctypes.c_int32() for _ in range(5))
+    bm, bn, rn, ch, bb, pc = (ctypes.c_int32() for _ in range(6))
     _call("attn_schedule", lib().attn_schedule(ctypes.byref(p), ctypes.byref(bm), ctypes.byref(bn),
-                                               ctypes.byref(rn), ctypes.byref(ch), ctypes.byref(bb)))
+                                               ctypes.byref(rn), ctypes.byref(ch), ctypes.byref(bb),
+                                               ctypes.byref(pc)))
     return dict(block_m=bm.value, block_n=bn.value, round_n=rn.value, chunk=ch.value,
-                block_bf16=bb.value)
+                block_bf16=bb.value, pv_chunk=pc.value)
 
 
 def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,

@@ -110,7 +110,7 @@ const char* attn_strerror(int code) {
 }
 
 int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n, int32_t* round_n,
-                  int32_t* chunk, int32_t* block_bf16) {
+                  int32_t* chunk, int32_t* block_bf16, int32_t* pv_chunk) {
   const int rc = check_params(p);
   if (rc) return rc;
   int32_t bn = attn::kFwdBlockN, rn = attn::kFwdRoundN, bb = 0;
@@ -126,6 +126,7 @@ int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n, int3
   if (round_n) *round_n = rn;
   if (chunk) *chunk = attn::kMfmaK;
   if (block_bf16) *block_bf16 = bb;
+  if (pv_chunk) *pv_chunk = (p->flags & (ATTN_PV_FP8 | ATTN_PV_MXFP4)) ? 64 : attn::kMfmaK;
   return ATTN_OK;
 }
 

@@ -110,7 +110,7 @@ __device__ __forceinline__ int mx_scale_byte(float amax, bool ceil) {
 }
 
 template <int D, bool CAUSAL, int GUARD, bool OBAR_F32, int PV>
-__global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd_kernel(FwdArgs a) {
   // every fp32 operation as written: no multiply is fused into a later add
   // (a fused alpha*R - m would turn r - m = 0 into the rounding error of
   // alpha*R and move decisions taken on it); fused steps are explicit fmaf
@@ -387,6 +387,21 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
     // blocks' chains interleaved); MXFP4: one step of 64 keys
     // every wave's share of the low-precision V^T operand is in LDS
     if constexpr (PV_FP8 || PV_MX) __syncthreads();
+    if (PV_FP8) {
+      // one scaled 64-product instruction per feature block (E4M3 operands,
+      // unit scales): the operand tile holds the four 16-key fragments of a
+      // block in sequence and P̄ is packed in the same key order
+      const i32x8 pb = {(int)pf8[0][0], (int)pf8[0][1], (int)pf8[1][0], (int)pf8[1][1],
+                        (int)pf8[2][0], (int)pf8[2][1], (int)pf8[3][0], (int)pf8[3][1]};
+#pragma unroll
+      for (int f = 0; f < FB; ++f) {
+        const uint2 w0 = Vf8[(0 * FB + f) * 64 + lane], w1 = Vf8[(1 * FB + f) * 64 + lane];
+        const uint2 w2 = Vf8[(2 * FB + f) * 64 + lane], w3 = Vf8[(3 * FB + f) * 64 + lane];
+        const i32x8 va = {(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, (int)w3.x, (int)w3.y};
+        // formats 0, 0: E4M3 operands; scale bytes 127 = 2^0
+        oacc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[f], 0, 0, 0, 127, 0, 127);
+      }
+    }
     if (PV_MX) {
 #pragma unroll
       for (int f = 0; f < FB; ++f) {
@@ -398,20 +413,13 @@ __global__ __launch_bounds__(kThreads, D == 64 && PV != 2 ? 4 : 2) void fwd_kern
       }
     }
 #pragma unroll
-    for (int t = 0; t < (PV_MX ? 0 : 4); ++t) {
+    for (int t = 0; t < (PV_MX || PV_FP8 ? 0 : 4); ++t) {
 #pragma unroll
       for (int f = 0; f < FB; ++f) {
         // A = V^T: feature 32f + l32, keys 16t + 4*half + 0..3 and 16t + 8 + 4*half + 0..3
-        if (PV_FP8) {
-          const uint2 w = Vf8[(t * FB + f) * 64 + lane];
-          const long va = (long)(((uint64_t)w.y << 32) | w.x);
-          const long pb = (long)(((uint64_t)pf8[t][1] << 32) | pf8[t][0]);
-          oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(va, pb, oacc[f], 0, 0, 0);
-        } else {
-          const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
-          const uint2 v0 = lds_read_tr(vs + o0), v1 = lds_read_tr(vs + o1);
-          oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag2(v0, v1), pf[t], oacc[f], 0, 0, 0);
-        }
+        const int o0 = ta_off[f][0] + 16 * t * D, o1 = ta_off[f][1] + 16 * t * D;
+        const uint2 v0 = lds_read_tr(vs + o0), v1 = lds_read_tr(vs + o1);
+        oacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag2(v0, v1), pf[t], oacc[f], 0, 0, 0);
       }
     }
     // bf16 mode: round the accumulator after every kFwdRoundN keys and

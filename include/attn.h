@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 9
+#define ATTN_ABI_VERSION 10
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -203,13 +203,15 @@ int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void
  * that a reference can replay it: block_m query rows per workgroup, block_n
  * keys per streaming step (tie decision and shift; 0 = the whole row),
  * round_n keys per bf16 rounding of Ō (bf16 mode; 0 = the whole row),
- * chunk = products per matrix instruction along each contraction,
+ * chunk = products per matrix instruction along each bf16 contraction,
  * block_bf16 = 1 when each block's product is rounded to bf16 before it is
- * added to Ō.  Returns ATTN_OK or an error code for invalid params.
- * Pointers may be NULL.
+ * added to Ō, pv_chunk = products per matrix instruction of the P̄V product
+ * (16 in bf16; 64 with ATTN_PV_FP8 or ATTN_PV_MXFP4: one instruction per
+ * feature block and 64-key step).  Returns ATTN_OK or an error code for
+ * invalid params.  Pointers may be NULL.
  */
 int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n,
-                  int32_t* round_n, int32_t* chunk, int32_t* block_bf16);
+                  int32_t* round_n, int32_t* chunk, int32_t* block_bf16, int32_t* pv_chunk);
 
 const char* attn_strerror(int code);
 int attn_abi_version(void);

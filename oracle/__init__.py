@@ -44,6 +44,7 @@ class _Schedule(ctypes.Structure):
         ("ftz", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("chunk_err", ctypes.c_double), ("exp_rel_err", ctypes.c_double),
         ("block_bf16", ctypes.c_int32), ("pv_fp8", ctypes.c_int32), ("pv_mxfp4", ctypes.c_int32),
+        ("pv_chunk", ctypes.c_int32),
     ]
 
 
@@ -104,12 +105,14 @@ class Schedule:
     block_bf16: bool = False
     pv_fp8: bool | str = False
     pv_mxfp4: bool | str = False
+    pv_chunk: int = 0
 
     def c(self) -> _Schedule:
         return _Schedule(self.block_n, self.round_n, int(bool(self.obar_fp32)),
                          int(bool(self.certify)), int(bool(self.ftz)),
                          self.chunk, self.chunk_err, self.exp_rel_err, int(bool(self.block_bf16)),
-                         {False: 0, True: 1, "row": 1, "fixed": 2}[self.pv_fp8], {False: 0, True: 1, "floor": 1, "ceil": 2}[self.pv_mxfp4])
+                         {False: 0, True: 1, "row": 1, "fixed": 2}[self.pv_fp8], {False: 0, True: 1, "floor": 1, "ceil": 2}[self.pv_mxfp4],
+                         int(self.pv_chunk))
 
 
 def build(verbose: bool = False) -> str:

@@ -86,6 +86,10 @@ typedef struct {
    * step.  Streaming schedule with block_n = 64 only.  2: the scales from
    * ceil(log2 amax) instead of floor.                                      */
   int32_t pv_mxfp4;
+  /* products per matrix instruction of the FP8 P̄V product: 16, or 64 for
+   * the scaled 64-product instruction (its group sums add a term to the
+   * bound, see chain_bound_fp8 in oracle.c); 0 = 16                       */
+  int32_t pv_chunk;
 } orc_schedule;
 
 int orc_version(void);

@@ -75,7 +75,7 @@ def schedule(p: orc.Problem, obar_fp32=False, certify=True, sched="stream", pv_f
     s = fa.attn_schedule(fp)
     return orc.Schedule(block_n=s["block_n"], round_n=s["round_n"], obar_fp32=obar_fp32,
                         chunk=s["chunk"], certify=certify, block_bf16=bool(s["block_bf16"]),
-                        pv_fp8=pv_fp8, pv_mxfp4=pv_mxfp4)
+                        pv_fp8=pv_fp8, pv_mxfp4=pv_mxfp4, pv_chunk=s["pv_chunk"])
 
 
 def check_o(o_gpu, o64, o_emu=None, obar_fp32=True, rows=None):

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 9
+    assert fa.attn_abi_version() == 10
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -43,30 +43,30 @@ def test_version_and_strings(L):
 
 def test_schedule(L):
     p = fa.make_params(1, 1, 1, 128, 64)
-    assert fa.attn_schedule(p) == dict(block_m=128, block_n=64, round_n=512, chunk=16, block_bf16=0)
+    assert fa.attn_schedule(p) == dict(block_m=128, block_n=64, round_n=512, chunk=16, block_bf16=0, pv_chunk=16)
     p = fa.make_params(1, 1, 1, 128, 64, schedule="fa2_ops")
-    assert fa.attn_schedule(p) == dict(block_m=128, block_n=512, round_n=512, chunk=16, block_bf16=1)
+    assert fa.attn_schedule(p) == dict(block_m=128, block_n=512, round_n=512, chunk=16, block_bf16=1, pv_chunk=16)
     p = fa.make_params(1, 1, 1, 128, 64, schedule="untiled")
-    assert fa.attn_schedule(p) == dict(block_m=128, block_n=0, round_n=0, chunk=16, block_bf16=1)
+    assert fa.attn_schedule(p) == dict(block_m=128, block_n=0, round_n=0, chunk=16, block_bf16=1, pv_chunk=16)
     p.flags |= fa.SCHED_FA2_OPS  # two schedules at once
-    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None, None) == -4
     # the FP8 product: streaming schedule only
     p = fa.make_params(1, 1, 1, 128, 64, pv_fp8=True)
     assert fa.attn_schedule(p)["block_n"] == 64
     for sched in ("fa2_ops", "untiled"):
         for kw in (dict(pv_fp8=True), dict(pv_mxfp4=True)):
             p = fa.make_params(1, 1, 1, 128, 64, schedule=sched, **kw)
-            assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+            assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None, None) == -4
     p = fa.make_params(1, 1, 1, 128, 64, pv_mxfp4=True)
     assert fa.attn_schedule(p)["block_n"] == 64
     p = fa.make_params(1, 1, 1, 128, 64, pv_fp8=True, pv_mxfp4=True)  # two formats
-    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None, None) == -4
     p = fa.make_params(1, 1, 1, 128, 64)
     p.flags |= fa.PV_FP8_FIXED  # the fixed FP8 scale without the FP8 product
-    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None, None) == -4
     p = fa.make_params(1, 1, 1, 128, 64)
     p.flags |= fa.PV_MX_CEIL  # the MX rule without the MXFP4 product
-    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None) == -4
+    assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None, None) == -4
     p = fa.make_params(1, 1, 1, 128, 64, pv_mxfp4="ceil")
     assert fa.attn_schedule(p)["block_n"] == 64
     with pytest.raises(ValueError):
