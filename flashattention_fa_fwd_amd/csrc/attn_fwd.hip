@@ -34,7 +34,8 @@
 // FP8 variant of the P̄V product (the pages leave open how the bias behaves
 // with fewer mantissa bits: [R] "Open questions"): P̄ * 2^k and V are rounded
 // to OCP E4M3 (v_cvt_pk_fp8_f32, round to nearest even) and multiplied on
-// v_mfma_f32_32x32x16_fp8_fp8 with the same operand layout; the accumulator
+// the scaled 64-product instruction (E4M3 formats, unit scales; operands in
+// the bf16 path's key order, the four 16-key groups in sequence); the accumulator
 // holds 2^k Ō, exact scaling through every fp32 and bf16 rounding, and the
 // scale is taken out at the end.  k is per row and per step: 7 -
 // floor((r - m) log2 e), which puts the row's largest P̄ = exp(r - m) in
