@@ -37,6 +37,9 @@ class _Problem(ctypes.Structure):
     ]
 
 
+_ORC_VERSION = 2  # the struct layouts below match oracle.h at this version
+
+
 class _Schedule(ctypes.Structure):
     _fields_ = [
         ("block_n", ctypes.c_int32), ("round_n", ctypes.c_int32),
@@ -131,6 +134,9 @@ def lib():
         u8p, i32p = P(ctypes.c_uint8), P(ctypes.c_int32)
         pp, sp = P(_Problem), P(_Schedule)
         L.orc_version.restype = ctypes.c_int
+        if L.orc_version() != _ORC_VERSION:
+            raise ImportError(f"{_LIB_PATH} is version {L.orc_version()}, this binding expects "
+                              f"{_ORC_VERSION}: rebuild it (oracle.build())")
         L.orc_bf16_from_f32.argtypes = [ctypes.c_float]
         L.orc_bf16_from_f32.restype = ctypes.c_uint16
         L.orc_bf16_from_f64.argtypes = [ctypes.c_double]

@@ -17,7 +17,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORC_VERSION 1
+#define ORC_VERSION 2  /* bump with every change to a struct shared with Python */
 #define U24 5.9604644775390625e-08 /* 2^-24: unit roundoff of binary32 */
 
 int orc_version(void) { return ORC_VERSION; }
