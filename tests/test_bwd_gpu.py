@@ -379,3 +379,33 @@ def test_step_replays_from_a_hip_graph():
         torch.cuda.synchronize()
         for n, a, b in zip(names, ref, outs()):
             assert torch.equal(a, b), (r, n)
+
+
+def test_dk_column_sums_follow_the_delta_error():
+    """Σ_j dK_j = α Σ_i (Σ_j dS_ij) Q_i vanishes in exact arithmetic (each
+    row of dS sums to zero).  With delta from the bf16 O the dS row sums
+    are minus the delta error, so Σ_j dK_j = -α Σ_i Δδ_i Q_i: the kernel's
+    dK column sums must match that prediction (from the two modes' delta
+    outputs) down to the rounding floor (bf16 dK, fp32 sums) that the
+    rowsum(dP∘P) mode shows on its own, and that floor must sit well below
+    the default's column sums."""
+    x = make("gpt2s")
+    wl = x["workload"]
+    _, b = _fwd_bwd_dsum(x, "beta", "do_o")
+    _, bp = _fwd_bwd_dsum(x, "beta", "dp_p")
+    q = dev(x["q"]).double()
+    g = wl.heads_q // wl.heads_kv
+    ddelta = (b["delta"] - bp["delta"]).double()                      # [B, Hq, N]
+    pred = -wl.alpha * torch.einsum("bhn,bhnd->bhd", ddelta, q)      # per query head
+    pred = pred.reshape(wl.batch, wl.heads_kv, g, -1).sum(2)         # summed over the group
+    colsum = b["dk"].double().sum(2)                                  # [B, Hkv, d]
+    colsum_dp = bp["dk"].double().sum(2)
+    scale = b["dk"].double().abs().sum(2)
+    err = ((colsum - pred).abs() / scale).mean().item()
+    base = (pred.abs() / scale).mean().item()
+    dp = (colsum_dp.abs() / scale).mean().item()
+    report("dK column sums (relative to sum|dK|)", delta_lp=f"{(colsum.abs() / scale).mean().item():.2e}",
+           predicted=f"{base:.2e}", residual_vs_prediction=f"{err:.2e}", delta_dp=f"{dp:.2e}")
+    lp = (colsum.abs() / scale).mean().item()
+    assert err < 1.5 * dp, (err, dp)
+    assert lp > 2.0 * dp, (lp, dp)
