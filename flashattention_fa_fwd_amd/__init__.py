@@ -42,6 +42,14 @@ class AttnError(RuntimeError):
         self.code = code
 
 
+class Strides(ctypes.Structure):
+    """Element strides (batch, head, row) of one tensor; zeros = dense."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("row", ctypes.c_int64)]
+
+
+_TENSORS = ("q", "k", "v", "o", "do", "dq", "dk", "dv")
+
+
 class Params(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
@@ -49,7 +57,7 @@ class Params(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("beta", ctypes.c_float), ("tie_eps", ctypes.c_float),
         ("shift_eps", ctypes.c_float), ("flags", ctypes.c_uint32),
-    ]
+    ] + [(f"{n}_stride", Strides) for n in _TENSORS]
 
 
 _lib = None
@@ -118,22 +126,42 @@ def _params_from(q, k, **kw) -> Params:
     return make_params(B, Hq, k.shape[1], N, d, **kw)
 
 
-def _check(name, t, dtype, shape=None, device=None):
+def _check(name, t, dtype, shape=None, device=None, strided=False):
     """The library reads and writes through raw device pointers sized from
     the parameters: every tensor must have exactly the expected dtype, shape
-    and layout, on the device of q."""
+    and layout, on the device of q.  The [B,H,N,d] operands may be strided
+    views (head_dim contiguous, strides multiples of 8 elements, checked
+    again by the library); everything else must be contiguous."""
     if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
         raise TypeError(f"{name} must be a {dtype} tensor on a HIP device")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if strided:
+        if t.dim() != 4 or t.stride(-1) != 1 or any(s < 0 or s % 8 for s in t.stride()[:3]):
+            raise ValueError(f"{name} must be [batch, heads, seqlen, head_dim] with head_dim "
+                             f"contiguous and other strides multiples of 8, not {t.stride()}")
+        if t.stride(2) < t.shape[3] and t.shape[2] > 1:
+            raise ValueError(f"{name}: rows overlap (row stride {t.stride(2)} < head_dim)")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _check_bf16(name, t, shape=None, device=None):
-    _check(name, t, torch.bfloat16, shape, device)
+    _check(name, t, torch.bfloat16, shape, device, strided=True)
+
+
+def _set_strides(p: Params, **tensors) -> Params:
+    """A copy of p with the element strides of the given [B,H,N,d] tensors
+    (dense tensors get the dense strides; the library accepts both)."""
+    p2 = Params.from_buffer_copy(p)
+    for n, t in tensors.items():
+        if t is None:
+            continue
+        sb, sh, sn, _ = t.stride()
+        setattr(p2, f"{n}_stride", Strides(sb, sh, sn))
+    return p2
 
 
 def _stream(stream, device=None):
@@ -165,7 +193,9 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
              shift_eps=2.0 ** -5, obar_fp32=False, softmax_scale=None, schedule="stream",
              pv_fp8=False, pv_mxfp4=False, return_obar=False, return_row_max=False, out=None,
              stream=None):
-    """Guarded forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16.  schedule:
+    """Guarded forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 (strided views
+    with head_dim contiguous are passed as they are, e.g. head-transposed
+    views of a fused QKV projection; outputs are allocated dense).  schedule:
     "stream" (the streaming kernel), "fa2_ops" or "untiled" (see make_params);
     pv_fp8: P̄V in FP8 E4M3 (streaming kernel only): True/"row" or "fixed";
     pv_mxfp4: P̄V in MXFP4 (streaming kernel only).
@@ -182,7 +212,7 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
                      schedule=schedule, pv_fp8=pv_fp8, pv_mxfp4=pv_mxfp4)
     res = out if out is not None else {}
     if "o" not in res:
-        res["o"] = torch.empty_like(q)
+        res["o"] = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
         res["row_m"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
         res["row_l"] = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
         res["row_flags"] = torch.empty((B, Hq, N), dtype=torch.uint8, device=dev)
@@ -199,6 +229,7 @@ def attn_fwd(q, k, v, *, causal=True, guard="beta", beta=2.0, tie_eps=1e-3,
         _check("obar", res["obar"], torch.float32 if obar_fp32 else torch.bfloat16, q.shape, dev)
     if res.get("row_max") is not None:
         _check("row_max", res["row_max"], torch.float32, rows, dev)
+    p = _set_strides(p, q=q, k=k, v=v, o=res["o"])
     _call("attn_fwd", lib().attn_fwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(res["o"]), _ptr(res["row_m"]),
         _ptr(res["row_l"]), _ptr(res["row_flags"]), _ptr(res.get("obar")), _ptr(res.get("row_max")),
@@ -229,9 +260,9 @@ def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=
                      shift_eps=shift_eps, softmax_scale=softmax_scale, delta=delta)
     res = out if out is not None else {}
     if "dq" not in res:
-        res["dq"] = torch.empty_like(q)
-        res["dk"] = torch.empty_like(k)
-        res["dv"] = torch.empty_like(v)
+        res["dq"] = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        res["dk"] = torch.empty(k.shape, dtype=torch.bfloat16, device=dev)
+        res["dv"] = torch.empty(k.shape, dtype=torch.bfloat16, device=dev)
         res["delta"] = torch.empty(rows, dtype=torch.float32, device=dev)
     if row_dsum and "row_dsum" not in res:
         res["row_dsum"] = torch.empty(rows, dtype=torch.float32, device=dev)
@@ -241,6 +272,7 @@ def attn_bwd(q, k, v, o, dout, row_m, row_l, *, causal=True, guard="beta", beta=
     _check("delta", res["delta"], torch.float32, rows, dev)
     if row_dsum:
         _check("row_dsum", res["row_dsum"], torch.float32, rows, dev)
+    p = _set_strides(p, q=q, k=k, v=v, o=o, do=dout, dq=res["dq"], dk=res["dk"], dv=res["dv"])
     _call("attn_bwd", lib().attn_bwd(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
         _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["delta"]),
@@ -262,6 +294,7 @@ def attn_bwd_dkdv(p: Params, q, k, v, dout, row_m, row_l, delta, dk, dv, stream=
         _check_bf16(n_, t, sh, dev)
     for n_, t in (("row_m", row_m), ("row_l", row_l), ("delta", delta)):
         _check(n_, t, torch.float32, rows, dev)
+    p = _set_strides(p, q=q, k=k, v=v, do=dout, dk=dk, dv=dv)
     _call("attn_bwd_dkdv", lib().attn_bwd_dkdv(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(row_m), _ptr(row_l),
         _ptr(delta), _ptr(dk), _ptr(dv), _stream(stream, dev)))
@@ -280,6 +313,7 @@ def attn_bwd_dq(p: Params, q, k, v, o, dout, row_m, row_l, dq, delta, row_dsum=N
         _check(n_, t, torch.float32, rows, dev)
     if row_dsum is not None:
         _check("row_dsum", row_dsum, torch.float32, rows, dev)
+    p = _set_strides(p, q=q, k=k, v=v, o=o, do=dout, dq=dq)
     _call("attn_bwd_dq", lib().attn_bwd_dq(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(row_m), _ptr(row_l),
         _ptr(dq), _ptr(delta), _ptr(row_dsum), _stream(stream, dev)))

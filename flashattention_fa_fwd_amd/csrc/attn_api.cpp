@@ -17,6 +17,47 @@ float scale_of(const attn_params* p) {
   return (float)(1.0 / std::sqrt((double)p->head_dim));
 }
 
+// The layout of one tensor with `heads` heads from its strides ({0, 0, 0}:
+// dense).  Returns ATTN_OK or the error code of attn.h's stride rules.
+int layout_of(const attn_params* p, const attn_strides& s, int heads, attn::Layout* out) {
+  const int64_t d = p->head_dim, n = p->seqlen;
+  attn_strides t = s;
+  if (t.batch == 0 && t.head == 0 && t.row == 0) {
+    t.row = d;
+    t.head = n * d;
+    t.batch = (int64_t)heads * n * d;
+  }
+  if (t.batch < 0 || t.head < 0 || t.row < 0) return ATTN_E_UNSUPPORTED;
+  if (t.batch % 8 != 0 || t.head % 8 != 0 || t.row % 8 != 0) return ATTN_E_UNSUPPORTED;
+  if (t.row < d) return ATTN_E_UNSUPPORTED;
+  // one head's rows, and the rows a tile copy reads past the end (zeros),
+  // are addressed with 32-bit byte offsets
+  if ((double)(n + 256) * (double)t.row * 2.0 >= 2147483648.0) return ATTN_E_SHAPE;
+  const double last = (double)(p->batch - 1) * t.batch + (double)(heads - 1) * t.head +
+                      (double)(n - 1) * t.row + (double)d;
+  if (last > 9.0e15) return ATTN_E_SHAPE;
+  if (out) {
+    out->sb = t.batch;
+    out->sh = t.head;
+    out->sn = (int)t.row;
+  }
+  return ATTN_OK;
+}
+
+int check_layouts(const attn_params* p) {
+  const attn_strides* q_like[] = {&p->q_stride, &p->o_stride, &p->do_stride, &p->dq_stride};
+  const attn_strides* kv_like[] = {&p->k_stride, &p->v_stride, &p->dk_stride, &p->dv_stride};
+  for (const attn_strides* s : q_like) {
+    const int rc = layout_of(p, *s, p->heads_q, nullptr);
+    if (rc) return rc;
+  }
+  for (const attn_strides* s : kv_like) {
+    const int rc = layout_of(p, *s, p->heads_kv, nullptr);
+    if (rc) return rc;
+  }
+  return ATTN_OK;
+}
+
 int check_params(const attn_params* p) {
   if (!p) return ATTN_E_NULL;
   if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->seqlen <= 0 ||
@@ -41,11 +82,12 @@ int check_params(const attn_params* p) {
   if (g == ATTN_GUARD_BETA && !(p->beta > 1.0f && std::isfinite(p->beta))) return ATTN_E_PARAM;
   if (!(p->tie_eps >= 0.0f && std::isfinite(p->tie_eps))) return ATTN_E_PARAM;
   if (g == ATTN_GUARD_EPS && !(p->shift_eps > 0.0f && std::isfinite(p->shift_eps))) return ATTN_E_PARAM;
-  // rows * head_dim must fit the kernels' index arithmetic, and one head's
-  // rows (in bytes) a 32-bit buffer range
+  // rows * head_dim must fit the kernels' index arithmetic; the strides
+  // (one head's rows within a 32-bit byte range) are checked per tensor
   const double elems = (double)p->batch * p->heads_q * p->seqlen * p->head_dim;
   if (elems > 9.0e15) return ATTN_E_SHAPE;
-  if ((double)p->seqlen * p->head_dim * 2.0 >= 2147483648.0) return ATTN_E_SHAPE;
+  const int lrc = check_layouts(p);
+  if (lrc) return lrc;
   // a launch covers at most 2^32 - 1 work-items: 256-thread workgroups of
   // 128 query rows (forward, dQ) or keys (dK/dV, fewer heads)
   const double groups = (double)p->batch * p->heads_q * ((p->seqlen + 127) / 128);
@@ -83,6 +125,15 @@ attn::BwdArgs bwd_args(const attn_params* p, const void* q, const void* k, const
   a.group = p->heads_q / p->heads_kv;
   a.alpha = scale_of(p);
   a.c1 = a.alpha * attn::kLog2e;
+  // validated by check_params
+  layout_of(p, p->q_stride, p->heads_q, &a.lq);
+  layout_of(p, p->k_stride, p->heads_kv, &a.lk);
+  layout_of(p, p->v_stride, p->heads_kv, &a.lv);
+  layout_of(p, p->o_stride, p->heads_q, &a.lo);
+  layout_of(p, p->do_stride, p->heads_q, &a.ldo);
+  layout_of(p, p->dq_stride, p->heads_q, &a.ldq);
+  layout_of(p, p->dk_stride, p->heads_kv, &a.ldk);
+  layout_of(p, p->dv_stride, p->heads_kv, &a.ldv);
   return a;
 }
 
@@ -102,7 +153,7 @@ const char* attn_strerror(int code) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULL: return "a required pointer is NULL";
     case ATTN_E_SHAPE: return "invalid shape (non-positive size, heads_q not a multiple of heads_kv, or a head too large)";
-    case ATTN_E_UNSUPPORTED: return "unsupported head_dim (64 or 128) or misaligned tensor pointer";
+    case ATTN_E_UNSUPPORTED: return "unsupported head_dim (64 or 128), misaligned tensor pointer or unsupported strides";
     case ATTN_E_PARAM: return "invalid parameter (beta, tie_eps, shift_eps, scale or flags)";
     case ATTN_E_HIP: return "the HIP runtime rejected a kernel launch";
     default: return "unknown error code";
@@ -161,6 +212,10 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.shift_eps = p->shift_eps;
   a.pv_fixed_scale = (p->flags & ATTN_PV_FP8_FIXED) != 0;
   a.pv_mx_ceil = (p->flags & ATTN_PV_MX_CEIL) != 0;
+  layout_of(p, p->q_stride, p->heads_q, &a.lq);  // validated by check_params
+  layout_of(p, p->k_stride, p->heads_kv, &a.lk);
+  layout_of(p, p->v_stride, p->heads_kv, &a.lv);
+  layout_of(p, p->o_stride, p->heads_q, &a.lo);
   const bool causal = (p->flags & ATTN_CAUSAL) != 0, obar_f32 = (p->flags & ATTN_OBAR_FP32) != 0;
   if (p->flags & ATTN_SCHED_MASK)
     return hip_status(attn::launch_fwd_block(a, p->head_dim, causal, guard_of(p->flags), obar_f32,

@@ -79,9 +79,10 @@ __device__ __forceinline__ void dkdv_load(const BwdArgs& a, int hq, int q0, int 
     stat[1] = a.row_l[r];
     stat[2] = a.delta[r];
   }
-  const size_t hoff = ((size_t)(b * a.Hq + hq) * a.N) * D;
-  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.q + hoff, a.N, D), q0, wave, lane, Qs);
-  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.dout + hoff, a.N, D), q0, wave, lane, dOs);
+  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.q + a.lq.head(b, hq), a.N, a.lq.sn, D), q0, a.lq.sn,
+                                  wave, lane, Qs);
+  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.dout + a.ldo.head(b, hq), a.N, a.ldo.sn, D), q0,
+                                  a.ldo.sn, wave, lane, dOs);
 }
 
 // Write a step's row statistics to its stage (threads 0..31, rows q0 + tid).
@@ -218,11 +219,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void bwd_dkdv_kernel(Bwd
   const int k0 = kblk * BN;
   const int wk0 = k0 + 32 * wave;     // this wave's first key
   const int key = wk0 + l32;          // the key this lane owns in S/dP
-  const size_t kvoff = ((size_t)(b * a.Hkv + hk) * N) * D;
 
   // the workgroup's K and V rows: B operands of S = Q K^T and dP = dO V^T
-  dma_tile<D, BN, kWaves>(head_desc(a.k + kvoff, N, D), k0, wave, lane, Ks);
-  dma_tile<D, BN, kWaves>(head_desc(a.v + kvoff, N, D), k0, wave, lane, Vs);
+  dma_tile<D, BN, kWaves>(head_desc(a.k + a.lk.head(b, hk), N, a.lk.sn, D), k0, a.lk.sn, wave, lane, Ks);
+  dma_tile<D, BN, kWaves>(head_desc(a.v + a.lv.head(b, hk), N, a.lv.sn, D), k0, a.lv.sn, wave, lane, Vs);
 
   f32x16 dk[FB], dv[FB];
 #pragma unroll
@@ -290,9 +290,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void bwd_dkdv_kernel(Bwd
     for (int i = 0; i < 16; ++i) {
       const int kr = wk0 + 8 * (i >> 2) + 4 * half + (i & 3);
       if (kr < N) {
-        const size_t off = kvoff + (size_t)kr * D + 32 * f + l32;
-        a.dk[off] = bf16_bits(a.alpha * dk[f][i]);
-        a.dv[off] = bf16_bits(dv[f][i]);
+        const int col = 32 * f + l32;
+        a.dk[a.ldk.head(b, hk) + (size_t)kr * a.ldk.sn + col] = bf16_bits(a.alpha * dk[f][i]);
+        a.dv[a.ldv.head(b, hk) + (size_t)kr * a.ldv.sn + col] = bf16_bits(dv[f][i]);
       }
     }
 }
@@ -317,8 +317,8 @@ __device__ __forceinline__ void dq_step(
   constexpr int FB = D / 32;
   const int N = a.N;
   if (more) {
-    dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, ks_next);
-    dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, vs_next);
+    dma_tile<D, BN, kWaves>(rk, j0 + BN, a.lk.sn, wave, lane, ks_next);
+    dma_tile<D, BN, kWaves>(rv, j0 + BN, a.lv.sn, wave, lane, vs_next);
   }
   // a wave whose rows all lie above this block's first key has nothing here
   if (wave_live && !(CAUSAL && j0 > q0 + 31)) {
@@ -404,8 +404,8 @@ __device__ __forceinline__ void dq_delta_step(
   constexpr int NT = D / kMfmaK;
   const int N = a.N;
   if (more) {
-    dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, ks_next);
-    dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, vs_next);
+    dma_tile<D, BN, kWaves>(rk, j0 + BN, a.lk.sn, wave, lane, ks_next);
+    dma_tile<D, BN, kWaves>(rv, j0 + BN, a.lv.sn, wave, lane, vs_next);
   }
   if (wave_live && !(CAUSAL && j0 > q0 + 31)) {
     f32x16 sv[2], dp[2];
@@ -471,10 +471,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int hk = hq / a.group;
   const int q0 = mb * kDqRows + wave * 32;
   const int qrow = q0 + l32;
-  const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
-  const size_t kvoff = ((size_t)(b * a.Hkv + hk) * N) * D;
-  const i32x4 rk = head_desc(a.k + kvoff, N, D);
-  const i32x4 rv = head_desc(a.v + kvoff, N, D);
+  const i32x4 rk = head_desc(a.k + a.lk.head(b, hk), N, a.lk.sn, D);
+  const i32x4 rv = head_desc(a.v + a.lv.head(b, hk), N, a.lv.sn, D);
+  const uint16_t* __restrict__ Qh = a.q + a.lq.head(b, hq);
+  const uint16_t* __restrict__ dOh = a.dout + a.ldo.head(b, hq);
 
   // Q and dO rows of this lane's row as B operands: [16t + 8*half + 0..7]
   bf16x8 qf[NT], gf[NT];
@@ -482,8 +482,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int t = 0; t < NT; ++t) {
     uint4 qr = make_uint4(0, 0, 0, 0), gr = make_uint4(0, 0, 0, 0);
     if (qrow < N) {
-      qr = *(const uint4*)(a.q + qoff + (size_t)qrow * D + 16 * t + 8 * half);
-      gr = *(const uint4*)(a.dout + qoff + (size_t)qrow * D + 16 * t + 8 * half);
+      qr = *(const uint4*)(Qh + (size_t)qrow * a.lq.sn + 16 * t + 8 * half);
+      gr = *(const uint4*)(dOh + (size_t)qrow * a.ldo.sn + 16 * t + 8 * half);
     }
     qf[t] = __builtin_bit_cast(bf16x8, qr);
     gf[t] = __builtin_bit_cast(bf16x8, gr);
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       uint4 orow = make_uint4(0, 0, 0, 0);
-      if (qrow < N) orow = *(const uint4*)(a.o + qoff + (size_t)qrow * D + 16 * t + 8 * half);
+      if (qrow < N) orow = *(const uint4*)(a.o + a.lo.head(b, hq) + (size_t)qrow * a.lo.sn + 16 * t + 8 * half);
       const uint4 grow = __builtin_bit_cast(uint4, gf[t]);
       const uint32_t ow[4] = {orow.x, orow.y, orow.z, orow.w};
       const uint32_t gw[4] = {grow.x, grow.y, grow.z, grow.w};
@@ -539,8 +539,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   if constexpr (DELTA_DP) {
     // first sweep: delta = rowsum(dP∘P) over the keys the row sees
-    dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
-    dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
+    dma_tile<D, BN, kWaves>(rk, 0, a.lk.sn, wave, lane, Ks[0]);
+    dma_tile<D, BN, kWaves>(rv, 0, a.lv.sn, wave, lane, Vs[0]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     float acc = 0.0f;
     for (int j0 = 0; j0 < kend; j0 += BN) {
@@ -558,8 +558,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
-  dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
+  dma_tile<D, BN, kWaves>(rk, 0, a.lk.sn, wave, lane, Ks[0]);
+  dma_tile<D, BN, kWaves>(rv, 0, a.lv.sn, wave, lane, Vs[0]);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   float dsum = 0.0f;
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // ---- dQ = bf16(alpha * dQ): lane = row, register i of block f = feature
   // 32f + 8(i/4) + 4*half + i%4
   if (qrow >= N) return;
-  uint16_t* drow = a.dq + qoff + (size_t)qrow * D;
+  uint16_t* drow = a.dq + a.ldq.head(b, hq) + (size_t)qrow * a.ldq.sn;
 #pragma unroll
   for (int f = 0; f < FB; ++f)
 #pragma unroll

@@ -52,15 +52,16 @@ __device__ __forceinline__ int qidx(int r, int col) {  // col % 4 == 0
   return r * D + ((((col >> 3) ^ qswz<D>(r))) << 3) + (col & 7);
 }
 
-// Buffer resource (gfx9 layout) of one head's rows: n*d bf16 from base;
-// offsets at or past n*d*2 bytes read as zeros.
+// Buffer resource (gfx9 layout) of one head's rows: n rows of d bf16, sn
+// elements apart, from base; offsets at or past ((n-1)*sn + d)*2 bytes read
+// as zeros (row n and later: sn >= d).
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 head_desc(const uint16_t* base, int n, int d) {
+__device__ __forceinline__ i32x4 head_desc(const uint16_t* base, int n, int sn, int d) {
   const uint64_t a = (uint64_t)base;
   // uniform by construction; readfirstlane keeps it in scalar registers
   return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
                __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
-               __builtin_amdgcn_readfirstlane(n * d * 2), kBufferWord3};
+               __builtin_amdgcn_readfirstlane(((n - 1) * sn + d) * 2), kBufferWord3};
 }
 
 // One buffer-to-LDS load of 16 bytes a lane: lane i's bytes land at LDS
@@ -81,13 +82,13 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
   return (uint32_t)(uintptr_t)(lds_u16*)p;
 }
 
-// Copy rows [r0, r0 + ROWS) of a row-major [n, D] bf16 array into a
-// swizzled LDS tile: a wave's 64 lanes fill 1 KiB of the tile in lane order
-// (16 bytes a lane), each lane fetching the global chunk that belongs at its
-// tile position.  Rows past n lie outside the buffer and read as zeros.
-// Wave w of NW takes its share of the 1 KiB pieces.
+// Copy rows [r0, r0 + ROWS) of a [n, D] bf16 array with row stride sn
+// (elements) into a swizzled LDS tile: a wave's 64 lanes fill 1 KiB of the
+// tile in lane order (16 bytes a lane), each lane fetching the global chunk
+// that belongs at its tile position.  Rows past n lie outside the buffer and
+// read as zeros.  Wave w of NW takes its share of the 1 KiB pieces.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(i32x4 desc, int r0, int w, int lane, uint16_t* tile) {
+__device__ __forceinline__ void dma_tile(i32x4 desc, int r0, int sn, int w, int lane, uint16_t* tile) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int PIECES = ROWS * CPR / 64;    // 1 KiB pieces per tile
   static_assert(PIECES % NW == 0, "tile / wave split");
@@ -97,7 +98,7 @@ __device__ __forceinline__ void dma_tile(i32x4 desc, int r0, int w, int lane, ui
     const int p = piece * 64 + lane;          // chunk position in the tile
     const int row = p / CPR;
     const int c = (p % CPR) ^ qswz<D>(row);   // logical chunk stored there
-    const int voff = ((r0 + row) * D + 8 * c) * 2;
+    const int voff = ((r0 + row) * sn + 8 * c) * 2;
     lds_dma16(desc, __builtin_amdgcn_readfirstlane(lds_addr(tile + piece * 512)), voff);
   }
 }

@@ -149,17 +149,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
   const int qrow = q0 + l32;
 
   const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
-  const size_t kvoff = ((size_t)(b * a.Hkv + hk) * N) * D;
-  const uint16_t* __restrict__ Q = a.q + qoff;
-  const uint16_t* __restrict__ K = a.k + kvoff;
-  const uint16_t* __restrict__ V = a.v + kvoff;
+  // Ō output and row vectors: dense; Q, K, V, O: the caller's strides
+  const uint16_t* __restrict__ Q = a.q + a.lq.head(b, hq);
 
   // Q fragment as the B operand: lane holds Q[qrow][16t + 8*half + 0..7]
   bf16x8 qf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (qrow < N) raw = *(const uint4*)(Q + (size_t)qrow * D + 16 * t + 8 * half);
+    if (qrow < N) raw = *(const uint4*)(Q + (size_t)qrow * a.lq.sn + 16 * t + 8 * half);
     qf[t] = __builtin_bit_cast(bf16x8, raw);
   }
 
@@ -178,7 +176,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
   const int kend = CAUSAL ? min(N, (mb + 1) * kFwdBlockM) : N;
   const bool wave_live = q0 < N;
 
-  const i32x4 rk = head_desc(a.k + kvoff, N, D), rv = head_desc(a.v + kvoff, N, D);
+  const i32x4 rk = head_desc(a.k + a.lk.head(b, hk), N, a.lk.sn, D),
+             rv = head_desc(a.v + a.lv.head(b, hk), N, a.lv.sn, D);
+  const int ksn = a.lk.sn, vsn = a.lv.sn;
   // per-lane LDS offsets: K rows as the A operand of S^T (key row 32kb + l32,
   // chunk 2t + half); V^T as the A operand of O^T through the transpose read
   // (keys 16t + trow and 16t + 8 + trow, features 32f + 16(g16&1) + ...)
@@ -241,8 +241,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
     }
   };
 
-  dma_tile<D, BN, kWaves>(rk, 0, wave, lane, Ks[0]);
-  dma_tile<D, BN, kWaves>(rv, 0, wave, lane, Vs[0]);
+  dma_tile<D, BN, kWaves>(rk, 0, ksn, wave, lane, Ks[0]);
+  dma_tile<D, BN, kWaves>(rv, 0, vsn, wave, lane, Vs[0]);
   int j0 = 0;
   for (; j0 < jc; j0 += BN) {
     const int cur = (j0 / BN) & 1;
@@ -253,8 +253,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
     __syncthreads();
     const bool more = j0 + BN < kend;
     if (more) {
-      dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, Ks[cur ^ 1]);
-      dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, Vs[cur ^ 1]);
+      dma_tile<D, BN, kWaves>(rk, j0 + BN, ksn, wave, lane, Ks[cur ^ 1]);
+      dma_tile<D, BN, kWaves>(rv, j0 + BN, vsn, wave, lane, Vs[cur ^ 1]);
     }
     const uint16_t* ks = Ks[cur];
     const uint16_t* vs = Vs[cur];
@@ -438,8 +438,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (j0 + BN < kend) {
-      dma_tile<D, BN, kWaves>(rk, j0 + BN, wave, lane, Ks[cur ^ 1]);
-      dma_tile<D, BN, kWaves>(rv, j0 + BN, wave, lane, Vs[cur ^ 1]);
+      dma_tile<D, BN, kWaves>(rk, j0 + BN, ksn, wave, lane, Ks[cur ^ 1]);
+      dma_tile<D, BN, kWaves>(rv, j0 + BN, vsn, wave, lane, Vs[cur ^ 1]);
     }
     // low-precision products: the waves still computing need this wave's share
     if constexpr (PV_FP8) convert_v(Vs[cur]);
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
         for (int i = 0; i < 16; ++i) quo[f][i] = oacc[f][i] / ltot;
     }
   }
-  uint16_t* orow = a.o + qoff + (size_t)qrow * D;
+  uint16_t* orow = a.o + a.lo.head(b, hq) + (size_t)qrow * a.lo.sn;
 #pragma unroll
   for (int f = 0; f < FB; ++f)
 #pragma unroll

@@ -64,15 +64,15 @@ __global__ __launch_bounds__(kThreads) void fwd_block_kernel(FwdArgs a) {
   const int q0 = mb * kFwdBlockM + wave * 32;
   const int qrow = q0 + l32;
   const size_t qoff = ((size_t)(b * a.Hq + hq) * N) * D;
-  const size_t kvoff = ((size_t)(b * a.Hkv + hk) * N) * D;
-  const uint16_t* __restrict__ Q = a.q + qoff;
+  // Ō output and row vectors: dense; Q, K, V, O: the caller's strides
+  const uint16_t* __restrict__ Q = a.q + a.lq.head(b, hq);
 
   // Q fragment as the B operand of S^T = K Q^T: lane holds Q[qrow][16t + 8*half + 0..7]
   bf16x8 qf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (qrow < N) raw = *(const uint4*)(Q + (size_t)qrow * D + 16 * t + 8 * half);
+    if (qrow < N) raw = *(const uint4*)(Q + (size_t)qrow * a.lq.sn + 16 * t + 8 * half);
     qf[t] = __builtin_bit_cast(bf16x8, raw);
   }
   f32x16 oacc[FB], bacc[FB];
@@ -90,7 +90,9 @@ __global__ __launch_bounds__(kThreads) void fwd_block_kernel(FwdArgs a) {
   // tiles this wave computes: under the causal mask its rows see no key at
   // or past q0 + 32
   const int wend = !wave_live ? 0 : (CAUSAL ? min(kend, q0 + 32) : kend);
-  const i32x4 rk = head_desc(a.k + kvoff, N, D), rv = head_desc(a.v + kvoff, N, D);
+  const i32x4 rk = head_desc(a.k + a.lk.head(b, hk), N, a.lk.sn, D),
+             rv = head_desc(a.v + a.lv.head(b, hk), N, a.lv.sn, D);
+  const int ksn = a.lk.sn, vsn = a.lv.sn;
   int ka_off[2][NT];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -129,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void fwd_block_kernel(FwdArgs a) {
   // one tile into LDS: every wave is done with the previous one first
   auto load = [&](int j0, bool with_v) {
     __syncthreads();
-    dma_tile<D, BN, kWaves>(rk, j0, wave, lane, Ks);
-    if (with_v) dma_tile<D, BN, kWaves>(rv, j0, wave, lane, Vs);
+    dma_tile<D, BN, kWaves>(rk, j0, ksn, wave, lane, Ks);
+    if (with_v) dma_tile<D, BN, kWaves>(rv, j0, vsn, wave, lane, Vs);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   };
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void fwd_block_kernel(FwdArgs a) {
   // ---- epilogue: O = bf16(Ō / ℓ); row outputs
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (qrow >= N) return;
-  uint16_t* orow = a.o + qoff + (size_t)qrow * D;
+  uint16_t* orow = a.o + a.lo.head(b, hq) + (size_t)qrow * a.lo.sn;
 #pragma unroll
   for (int f = 0; f < FB; ++f)
 #pragma unroll

@@ -26,6 +26,16 @@ constexpr int kFwdOpsBlockN = 512;
 // Products per matrix instruction along every contraction.
 constexpr int kMfmaK = 16;
 
+// Element strides of one tensor: batch and head (64-bit), row (32-bit: one
+// head's rows are addressed with 32-bit byte offsets); head_dim stride 1.
+struct Layout {
+  int64_t sb, sh;
+  int sn;
+  __device__ __forceinline__ size_t head(int b, int h) const {
+    return (size_t)((int64_t)b * sb + (int64_t)h * sh);
+  }
+};
+
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -42,6 +52,7 @@ struct FwdArgs {
   float beta, tie_eps, shift_eps;
   int pv_fixed_scale;  // FP8 product: 1 = operand scale fixed at 2^8
   int pv_mx_ceil;      // MXFP4 product: 1 = block scale from ceil(log2 amax)
+  Layout lq, lk, lv, lo;
 };
 
 struct BwdArgs {
@@ -59,6 +70,7 @@ struct BwdArgs {
   uint16_t* dv;
   int B, Hq, Hkv, N, group;
   float alpha, c1;
+  Layout lq, lk, lv, lo, ldo, ldq, ldk, ldv;
 };
 
 // Workgroup order on the 8 XCDs (each with its own L2): the hardware hands

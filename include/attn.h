@@ -12,9 +12,24 @@
  * Each entry point below names the passage that defines it.
  *
  * Conventions shared by every entry point
- *   - Tensors are dense, row-major [batch][heads][seqlen][head_dim] with
- *     head_dim contiguous; Q, O, dO, dQ have heads_q heads, K, V, dK, dV have
- *     heads_kv heads.  Per-row vectors are [batch][heads_q][seqlen].
+ *   - A tensor is indexed [batch][heads][seqlen][head_dim] with head_dim
+ *     contiguous; Q, O, dO, dQ have heads_q heads, K, V, dK, dV have heads_kv
+ *     heads.  Element (b, h, n, f) of tensor X lives at
+ *     X + b*X_stride.batch + h*X_stride.head + n*X_stride.row + f (elements),
+ *     so head-transposed views of a projection output ([batch][seqlen]
+ *     [heads][head_dim], or one third of a fused [batch][seqlen][3][heads]
+ *     [head_dim] QKV output, as in the GPT-2 attention layers the pages
+ *     train: [R] "Core idea" -> method, paper §3.1) are passed without a
+ *     copy.  A stride triple of zeros selects the dense layout (batch =
+ *     heads*seqlen*head_dim, head = seqlen*head_dim, row = head_dim).
+ *     Per-row vectors (row_m, row_l, row_flags, delta, row_max, row_dsum)
+ *     and the optional Ō output are always dense [batch][heads_q][seqlen]
+ *     (x head_dim).
+ *   - Strides: every stride >= 0 and a multiple of 8 elements (16 bytes);
+ *     row >= head_dim; (seqlen + 256) * row * 2 < 2^31 (one head's rows,
+ *     in bytes, addressed with 32-bit offsets).  Output tensors (o, dq, dk,
+ *     dv) must not overlap each other or any input; inputs may share memory
+ *     (q, k and v may be views of one buffer).
  *   - Every pointer is a device pointer owned by the caller; the library
  *     neither allocates nor frees, keeps no state between calls, never
  *     synchronises and never prints.  Tensor pointers must be 16-byte
@@ -36,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 10
+#define ATTN_ABI_VERSION 11
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -66,12 +81,20 @@ extern "C" {
 #define ATTN_OK 0
 #define ATTN_E_NULL (-1)        /* a required pointer is NULL                   */
 #define ATTN_E_SHAPE (-2)       /* non-positive size, heads_q % heads_kv != 0,
-                                   seqlen*head_dim*2 >= 2^31, or more than
-                                   2^24 - 1 workgroups of 128 rows
+                                   (seqlen+256)*row_stride*2 >= 2^31, or more
+                                   than 2^24 - 1 workgroups of 128 rows
                                    (batch*heads_q*ceil(seqlen/128))          */
-#define ATTN_E_UNSUPPORTED (-3) /* head_dim not 64/128, misaligned pointer      */
+#define ATTN_E_UNSUPPORTED (-3) /* head_dim not 64/128, misaligned pointer,
+                                   stride negative, not a multiple of 8
+                                   elements, or a row stride < head_dim      */
 #define ATTN_E_PARAM (-4)       /* bad beta/tie_eps/shift_eps/flags/scale       */
 #define ATTN_E_HIP (-6)         /* the HIP runtime refused a launch             */
+
+/* Element strides of one [batch][heads][seqlen][head_dim] tensor (the
+ * head_dim stride is 1).  {0, 0, 0} selects the dense layout. */
+typedef struct {
+  int64_t batch, head, row;
+} attn_strides;
 
 typedef struct {
   int32_t batch;     /* > 0                                                  */
@@ -86,6 +109,9 @@ typedef struct {
   uint32_t flags;    /* ATTN_CAUSAL | one ATTN_GUARD_* | ATTN_OBAR_FP32 |
                         ATTN_DELTA_DP | one ATTN_SCHED_* | ATTN_PV_FP8 (+
                         ATTN_PV_FP8_FIXED) or ATTN_PV_MXFP4                  */
+  /* layouts of the tensors (see the conventions above); zero = dense        */
+  attn_strides q_stride, k_stride, v_stride, o_stride;     /* attn_fwd, attn_bwd */
+  attn_strides do_stride, dq_stride, dk_stride, dv_stride; /* attn_bwd          */
 } attn_params;
 
 /*
@@ -101,8 +127,9 @@ typedef struct {
  * ℓ <- exp(m_old - m) ℓ + sum exp(t - m) in fp32.  Unless ATTN_OBAR_FP32, Ō
  * is rounded to bf16 after every round_n keys and after the row's last
  * block.  Finally O = bf16(Ō/ℓ).
- *   q [B,Hq,N,d] bf16, k/v [B,Hkv,N,d] bf16                (in)
- *   o [B,Hq,N,d] bf16                                       (out)
+ *   q [B,Hq,N,d] bf16, k/v [B,Hkv,N,d] bf16                (in; q_stride,
+ *                                                  k_stride, v_stride)
+ *   o [B,Hq,N,d] bf16                                       (out; o_stride)
  *   row_m [B,Hq,N] fp32: the final shift m                  (out, required)
  *   row_l [B,Hq,N] fp32: ℓ relative to row_m                (out, required)
  *   row_flags [B,Hq,N] u8: ATTN_ROW_* bits                  (out, required)
@@ -156,8 +183,10 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v,
  * (delta computed from the bf16 O, paper §3.2).  The guard is carried by
  * recomputing P = exp(t - row_m) / row_l with the stored shift ([R] the fix:
  * the backward is otherwise unchanged).
- *   q, k, v, o (bf16), dout [B,Hq,N,d] bf16, row_m, row_l from attn_fwd (in)
- *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d] bf16                  (out)
+ *   q, k, v, o (bf16; q/k/v/o_stride), dout [B,Hq,N,d] bf16 (do_stride),
+ *   row_m, row_l from attn_fwd                              (in)
+ *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d] bf16                  (out; dq/dk/
+ *                                                  dv_stride)
  *   delta [B,Hq,N] fp32 = rowsum(dO∘O)                      (out, required)
  * With ATTN_DELTA_DP, delta = rowsum(dP∘P) instead: the pages' other form
  * of the same quantity, which never reads the bf16 O ([R] method, paper

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 10
+    assert fa.attn_abi_version() == 11
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -175,3 +175,30 @@ def test_binding_rejects_host_and_mistyped_tensors():
     p = fa.make_params(1, 1, 1, 64, 64)
     with pytest.raises(TypeError):
         fa.attn_bwd_dkdv(p, q, q, q, q, m, m, m, q, q)
+
+
+def test_stride_rules(L):
+    """Per-tensor strides: zeros are the dense layout; negative strides,
+    strides that are not multiples of 8 elements, overlapping rows and rows
+    beyond a 32-bit byte range are refused before anything is enqueued."""
+    B, H, N, d = 2, 3, 100, 64
+    ok = fa.make_params(B, H, H, N, d)
+    assert _fwd(L, ok) != -3 and fa.attn_schedule(ok)["block_n"] == 64
+    fused = fa._set_strides(ok)
+    # one third of a fused [B, N, 3, H, d] projection output, head-transposed
+    for n in ("q", "k", "v"):
+        setattr(fused, f"{n}_stride", fa.Strides(N * 3 * H * d, d, 3 * H * d))
+    fused.o_stride = fa.Strides(N * H * d, d, H * d)  # O written as [B, N, H, d]
+    assert fa.attn_schedule(fused)["block_n"] == 64
+    cases = [
+        ("q", fa.Strides(-8, d, 3 * H * d), -3),
+        ("k", fa.Strides(N * H * d, 4, d), -3),          # head stride not a multiple of 8
+        ("v", fa.Strides(N * H * d, d, 60), -3),         # row stride not a multiple of 8
+        ("o", fa.Strides(N * H * d, d, 56), -3),         # rows overlap (56 < 64)
+        ("dk", fa.Strides(N * H * d, d, 1 << 24), -2),   # (N + 256) rows past 2^31 bytes
+    ]
+    for name, st, code in cases:
+        p = fa._set_strides(ok)
+        setattr(p, f"{name}_stride", st)
+        assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None, None) == code, name
+        assert _fwd(L, p) == code, name
