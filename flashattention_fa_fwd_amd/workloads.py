@@ -7,7 +7,10 @@ path's tests/benchmark and the CPU oracle receive exactly these arrays.
 Workloads (shapes taken from the pages' models; the data is synthetic):
   * ``tiny``      B=1, H=1, N=128, d=64, causal.  Q, K ~ N(0,1); V features
                   0..31 ~ N(-0.5,1) (negative-dominated), 32..63 ~ N(0,1);
-                  10% of query rows get a planted exact repeated maximum.
+                  10% of query rows get a planted exact repeated maximum
+                  (seed 1014: of the seeds 1001..1040 with a tie rate near 10%, the one
+                  whose bf16 Ō has the fewest elements the oracle cannot
+                  certify).
   * ``gpt2s``     GPT-2 Small attention layer: B=16, H=12, N=1024, d=64,
                   causal.  Q, K ~ N(0, 1.5^2); V = mu[b,h,f] + N(0,1) with
                   mu ~ U(-1,1); key 0 is an attention sink (+4 logits); 5% of
@@ -30,14 +33,19 @@ on every query's scaled logit.
 A planted tie for query row i: pick two distinct visible keys a and b (not
 the sink), copy K[a] into K[b] bit for bit, and add lambda*K[a] to Q[i]
 (lambda = plant_logit / (alpha * d * var_q_k)), which lifts both keys about
-plant_logit above the row's typical logit -- far enough (16-20) that every
-other P̄ of the row is tiny, the attention-sink regime in which the pages
-locate the biased rounding (P̄ = 1 exactly at the repeated maximum and a
-small same-sign residual from the rest).  The two keys then have identical scores in
-any arithmetic.  A near tie additionally moves one feature of K[b] by one
-bf16 step, in a feature where that changes the scaled logit by 1e-5..5e-4.
-Duplicated keys also touch other rows, so the achieved tie rate is whatever
-the oracle's flags report, not the planted fraction.
+plant_logit above the row's typical logit.  The named configurations use a
+lift of 3.5-4 standard deviations of the row's logits (tiny 3.5, GPT-2 8,
+Llama 4, stress 56): where a natural row maximum falls, so the pair is the
+row maximum in most planted rows without dominating the row.  The ``_sink``
+study workloads lift the pair 16-20 logits, the attention-sink regime in
+which the pages locate the biased rounding (P̄ = 1 exactly at the repeated
+maximum and a small same-sign residual from the rest).  The two keys have
+identical scores in any arithmetic.  A near tie additionally moves one
+feature of K[b] by one bf16 step, in a feature where that changes the
+scaled logit by 1e-5..5e-4.  Duplicated keys also touch other rows, so the
+achieved tie rate is whatever the oracle's flags report, not the planted
+fraction.  This module never computes a score: which key is a row's
+maximum is left to the lift.
 """
 from __future__ import annotations
 
@@ -94,21 +102,37 @@ class Workload:
 
 
 WORKLOADS = {
+    # the configurations as stated: the planted pair sits about 3.5-4 standard
+    # deviations of the row's logits above the typical logit, i.e. where a
+    # natural maximum of the row falls, so it is the row maximum without
+    # dominating the row
     "tiny": Workload("tiny", 1, 1, 1, 128, 64, True, 1.0, 1.0, "split", -0.5,
-                     0.0, 0.10, 0.0, 16.0, 1001,
+                     0.0, 0.10, 0.0, 3.5, 1014,
                      "single head, causal, N=128, d=64"),
     "gpt2s": Workload("gpt2s", 16, 12, 12, 1024, 64, True, 1.5, 1.5, "mu_uniform", 0.0,
-                      4.0, 0.05, 0.0, 20.0, 1002,
+                      4.0, 0.05, 0.0, 8.0, 1002,
                       "GPT-2 Small attention layer B=16 H=12 N=1024 d=64 causal"),
     "gpt2m": Workload("gpt2m", 8, 16, 16, 1024, 64, True, 1.5, 1.5, "mu_uniform", 0.0,
-                      4.0, 0.20, 0.0, 20.0, 1003,
+                      4.0, 0.20, 0.0, 8.0, 1003,
                       "GPT-2 Medium attention layer B=8 H=16 N=1024 d=64 causal"),
     "llama8b": Workload("llama8b", 1, 32, 8, 8192, 128, True, 1.0, 1.0, "const", -0.3,
-                        6.0, 0.02, 0.0, 16.0, 1004,
+                        6.0, 0.02, 0.0, 4.0, 1004,
                         "Llama-3.1-8B GQA attention B=1 Hq=32 Hkv=8 N=8192 d=128 causal"),
     "stress": Workload("stress", 4, 8, 8, 4096, 128, False, 4.0, 4.0, "const", 0.0,
-                       0.0, 0.30, 0.5, 60.0, 1005,
+                       0.0, 0.30, 0.5, 56.0, 1005,
                        "large-logit stress B=4 H=8 N=4096 d=128 non-causal"),
+    # study variants in the attention-sink regime where the pages locate the
+    # biased rounding: the planted pair 16-20 logits above the row, so every
+    # other P̄ of a tie row is tiny (same shapes and distributions otherwise)
+    "tiny_sink": Workload("tiny_sink", 1, 1, 1, 128, 64, True, 1.0, 1.0, "split", -0.5,
+                          0.0, 0.10, 0.0, 16.0, 1001,
+                          "single head, causal, N=128, d=64, ties lifted 16 logits"),
+    "gpt2s_sink": Workload("gpt2s_sink", 16, 12, 12, 1024, 64, True, 1.5, 1.5, "mu_uniform", 0.0,
+                           4.0, 0.05, 0.0, 20.0, 1002,
+                           "GPT-2 Small attention layer B=16 H=12 N=1024 d=64 causal, ties lifted 20 logits"),
+    "gpt2m_sink": Workload("gpt2m_sink", 8, 16, 16, 1024, 64, True, 1.5, 1.5, "mu_uniform", 0.0,
+                           4.0, 0.20, 0.0, 20.0, 1003,
+                           "GPT-2 Medium attention layer B=8 H=16 N=1024 d=64 causal, ties lifted 20 logits"),
 }
 
 

@@ -160,6 +160,14 @@ def lib():
                                   ctypes.c_int32, f64p, f64p, f64p, f64p, ctypes.c_int32]
         L.orc_bwd_rows_emu.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
                                        f64p, ctypes.c_int32, f64p, f64p, ctypes.c_int32]
+        for nm in ("orc_chain_bound", "orc_chain_bound_mx"):
+            getattr(L, nm).argtypes = [ctypes.POINTER(_Schedule), ctypes.c_double, f64p, ctypes.c_int32]
+            getattr(L, nm).restype = ctypes.c_double
+        L.orc_chain_bound_fp8.argtypes = [ctypes.POINTER(_Schedule), ctypes.c_double, f64p, i32p,
+                                          ctypes.c_int32, ctypes.c_int32]
+        L.orc_chain_bound_fp8.restype = ctypes.c_double
+        L.orc_bwd_kv_keys.argtypes = [pp, u16p, u16p, u16p, u16p, ctypes.c_int32, f64p, ctypes.c_int32,
+                                      f64p, f64p, f64p, ctypes.c_int32]
         L.orc_delta_dp_rows_f64.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
                                             f64p, ctypes.c_int32]
         L.orc_dsum_rows_f64.argtypes = [pp, u16p, u16p, u16p, u16p, i32p, i32p, ctypes.c_int32,
@@ -185,7 +193,7 @@ def lib():
             getattr(L, fn).restype = ctypes.c_int
         for name in ("orc_fwd_f64", "orc_bwd_f64", "orc_bwd_rows_f64", "orc_row_stats",
                      "orc_obar_f64", "orc_fwd_emu", "orc_bwd_emu", "orc_bwd_rows_emu",
-                     "orc_fwd_emu_rows", "orc_delta_dp_rows_f64", "orc_dsum_rows_f64"):
+                     "orc_fwd_emu_rows", "orc_delta_dp_rows_f64", "orc_dsum_rows_f64", "orc_bwd_kv_keys"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -406,6 +414,27 @@ def bwd_emu(p: Problem, q, k, v, dout, o_in=None, round_ops=True, kv_heads=None,
     return dict(delta=delta, dq=dq, dk=dk, dv=dv)
 
 
+def bwd_kv_keys(p: Problem, q, k, v, dout, kv_head, o_in=None, round_ops=False, nthreads=None):
+    """FP64 backward of one KV head, parallel over rows and key blocks: delta
+    [g, N] of its g query heads and dk, dv [N, d] of its keys.  o_in [g, N, d]
+    and round_ops as in bwd_emu (the method's rounding points)."""
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    g = p.heads_q // p.heads_kv
+    N, d = q.shape[-2], q.shape[-1]
+    oi = None if o_in is None else np.ascontiguousarray(np.asarray(o_in, np.float64))
+    if oi is not None:
+        assert oi.shape == (g, N, d)
+    delta = np.zeros((g, N), np.float64)
+    dk = np.zeros((N, d), np.float64); dv = np.zeros((N, d), np.float64)
+    pc = p.c()
+    _check(lib().orc_bwd_kv_keys(ctypes.byref(pc), _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                 _ptr(v, ctypes.c_uint16), _ptr(dout, ctypes.c_uint16), int(kv_head),
+                                 _ptr(oi, ctypes.c_double), int(bool(round_ops)),
+                                 _ptr(delta, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                                 _ptr(dv, ctypes.c_double), _threads(nthreads)), "orc_bwd_kv_keys")
+    return dict(delta=delta, dk=dk, dv=dv)
+
+
 def bwd_rows_emu(p: Problem, q, k, v, dout, qheads, rows, o_in=None, round_ops=True, nthreads=None):
     q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
     qh = np.ascontiguousarray(np.asarray(qheads, dtype=np.int32))
@@ -494,3 +523,27 @@ def fwd_emu(p: Problem, sched: Schedule, q, k, v, heads=None, nthreads=None):
                              _ptr(fc, ctypes.c_uint8), _ptr(ex, ctypes.c_uint8), _threads(nthreads)),
            "orc_fwd_emu")
     return dict(obar=ob, obar_cert=oc, obar_dev=od, o=o, m=m, l=l, flags=fl, flag_cert=fc, ex=ex)
+
+
+def chain_bound(sched: Schedule, c0: float, terms) -> float:
+    """Bound on |kernel sum - exact c0 + sum(terms)| for a chain of bf16
+    matrix instructions of sched.chunk products (oracle.c, chain_bound)."""
+    t = np.ascontiguousarray(np.asarray(terms, np.float64))
+    sc = sched.c()
+    return lib().orc_chain_bound(ctypes.byref(sc), float(c0), _ptr(t, ctypes.c_double), int(t.size))
+
+
+def chain_bound_fp8(sched: Schedule, c0: float, terms, esum, shift=0) -> float:
+    """The same for FP8 E4M3 products (esum: exponent sums of the operands)."""
+    t = np.ascontiguousarray(np.asarray(terms, np.float64))
+    e = np.ascontiguousarray(np.asarray(esum, np.int32))
+    sc = sched.c()
+    return lib().orc_chain_bound_fp8(ctypes.byref(sc), float(c0), _ptr(t, ctypes.c_double),
+                                     _ptr(e, ctypes.c_int32), int(t.size), int(shift))
+
+
+def chain_bound_mx(sched: Schedule, c0: float, terms) -> float:
+    """The same for one scaled FP4 matrix instruction."""
+    t = np.ascontiguousarray(np.asarray(terms, np.float64))
+    sc = sched.c()
+    return lib().orc_chain_bound_mx(ctypes.byref(sc), float(c0), _ptr(t, ctypes.c_double), int(t.size))

@@ -156,6 +156,25 @@ int orc_bwd_rows_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
                      const int32_t* rows, int32_t n, const double* o_in, int32_t round_ops,
                      double* delta, double* dq, int32_t nthreads);
 
+/* Error bounds of the kernel's accumulation chains (oracle.c, chain_bound*):
+ * c0 + sum(terms) summed by matrix instructions of sc->chunk (bf16) or
+ * sc->pv_chunk (FP8: terms are products of E4M3 operands scaled by 2^shift,
+ * esum their exponent sums; MXFP4: one instruction) products each. */
+double orc_chain_bound(const orc_schedule* sc, double c0, const double* terms, int32_t n);
+double orc_chain_bound_fp8(const orc_schedule* sc, double c0, const double* terms,
+                           const int32_t* esum, int32_t n, int32_t shift);
+double orc_chain_bound_mx(const orc_schedule* sc, double c0, const double* terms, int32_t n);
+
+/* FP64 backward of one KV head (kv_head = b*heads_kv + hk): delta [g, N] for
+ * the group's g query heads, dk and dv [N, d] of its keys; parallel over
+ * rows, then over blocks of keys.  o_in (nullable, [g, N, d]) and round_ops
+ * as in orc_bwd_emu.  Same arithmetic as orc_bwd_f64 / orc_bwd_emu per (i,
+ * j): [R] "Core idea", equations (paper Eq. 1-2). */
+int orc_bwd_kv_keys(const orc_problem* p, const uint16_t* q, const uint16_t* k,
+                    const uint16_t* v, const uint16_t* dout, int32_t kv_head,
+                    const double* o_in, int32_t round_ops, double* delta, double* dk,
+                    double* dv, int32_t nthreads);
+
 /* delta_i = sum_j P_ij dP_ij (exact softmax row P, dP_ij = dO_i . V_j) for
  * single rows: row rows[i] of query head qheads[i]; in double.  [R] method
  * (paper §3.2): the form of delta that does not use the low-precision O. */

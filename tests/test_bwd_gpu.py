@@ -409,3 +409,61 @@ def test_dk_column_sums_follow_the_delta_error():
     lp = (colsum.abs() / scale).mean().item()
     assert err < 1.5 * dp, (err, dp)
     assert lp > 2.0 * dp, (lp, dp)
+
+
+@pytest.mark.parametrize("guard", ["beta", "none"])
+def test_llama8b_whole_kv_head_dk_dv(guard):
+    """N = 8192, d = 128, 4 query heads per KV head: dK and dV of every key
+    of KV head 0 (summed over its 4 query heads) and delta of those heads
+    against the FP64 backward, with the method's own floor from the replay
+    at its rounding points (delta from the oracle's emulated bf16 O)."""
+    x = make("llama8b")
+    wl = x["workload"]
+    p = problem(wl, guard)
+    _, b = _fwd_bwd(x, guard)
+    g = wl.heads_q // wl.heads_kv
+    kvh = 0
+    ref = orc.bwd_kv_keys(p, x["q"], x["k"], x["v"], x["do"], kvh, nthreads=threads())
+    em = orc.fwd_emu(p, schedule(p, certify=False), x["q"], x["k"], x["v"],
+                     heads=list(range(kvh * g, kvh * g + g)), nthreads=threads())
+    o_in = em["o"].reshape(-1, wl.seqlen, wl.head_dim)[kvh * g:kvh * g + g]
+    rep = orc.bwd_kv_keys(p, x["q"], x["k"], x["v"], x["do"], kvh, o_in=o_in, round_ops=True,
+                          nthreads=threads())
+    shp = (-1, wl.seqlen, wl.head_dim)
+    out = {}
+    for key in ("dk", "dv"):
+        gpu = f32(b[key]).reshape(shp)[kvh]
+        out.update(_check(key, gpu, ref[key], rel_errors(rep[key], ref[key])))
+    de = b["delta"].cpu().numpy().reshape(-1, wl.seqlen)[kvh * g:kvh * g + g]
+    out.update(_check("delta", de, ref["delta"], rel_errors(rep["delta"], ref["delta"])))
+    report(f"bwd llama8b kv head 0 {guard}", **out)
+
+
+@pytest.mark.xfail(strict=False, reason="the method's own rounding points (δ from the bf16 O, bf16 P and "
+                   "dS operands, bf16 outputs) put an exact replay of it above the stated mean bound 2e-3 "
+                   "for dQ, dK and δ; the parity tests bound the kernel by that replay instead")
+def test_stated_tolerance_literally():
+    """The stated acceptance, max rel <= 1e-2 and mean rel <= 2e-3 against
+    FP64 for O, delta, dQ, dK, dV, checked literally at GPT-2 Small (the
+    measured figures are printed whether it passes or not)."""
+    x = make("gpt2s")
+    wl = x["workload"]
+    p = problem(wl, "beta")
+    f, b = _fwd_bwd(x, "beta")
+    kv = [0, 100]
+    ref = orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], kv_heads=kv, nthreads=threads())
+    shp = (-1, wl.seqlen, wl.head_dim)
+    figs, ok = {}, True
+    o64 = ref["o"].reshape(shp)[kv]
+    for key, gpu, r in (("o", f32(f["o"]).reshape(shp)[kv], o64),
+                        ("dq", f32(b["dq"]).reshape(shp)[kv], ref["dq"].reshape(shp)[kv]),
+                        ("dk", f32(b["dk"]).reshape(shp)[kv], ref["dk"].reshape(shp)[kv]),
+                        ("dv", f32(b["dv"]).reshape(shp)[kv], ref["dv"].reshape(shp)[kv]),
+                        ("delta", b["delta"].cpu().numpy().reshape(-1, wl.seqlen)[kv],
+                         ref["delta"].reshape(-1, wl.seqlen)[kv])):
+        mx, mean = rel_errors(gpu, r)
+        met = mx <= MAX_REL and mean <= MEAN_REL
+        ok &= met
+        figs[key] = f"{mx:.2e}/{mean:.2e}{'' if met else ' MISSED'}"
+    report("stated tolerance (max/mean rel) gpt2s beta", **figs)
+    assert ok, figs

@@ -204,8 +204,9 @@ def test_fp8_bias_study():
     """Signed errors on tie rows and the tied keys' weight factor under both
     operand scales; the fixed scale 2^8 underflows every P̄ of rows with a
     large maximum under the beta guard (its shift 2r makes every P̄ at most
-    exp(-r)), the row scale does not."""
-    x = make("gpt2s")
+    exp(-r)), the row scale does not.  Measured in the attention-sink regime
+    (gpt2s_sink: the repeated maximum 20 logits above the row)."""
+    x = make("gpt2s_sink")
     wl = x["workload"]
     heads = list(range(0, 192, 12))
     v8bits = _e4m3_bits(x["v"])
@@ -238,7 +239,7 @@ def test_fp8_bias_study():
                 sel_neg = tie[..., None] & neg[:, None, :]
                 single = ~tie[..., None] & neg[:, None, :]
                 res[(scale, guard, f32_)] = (c, zero_rows)
-                report(f"fp8 bias gpt2s scale={scale} guard={guard} obar={'fp32' if f32_ else 'bf16'}",
+                report(f"fp8 bias gpt2s_sink scale={scale} guard={guard} obar={'fp32' if f32_ else 'bf16'}",
                        tie_key_coef=f"{c:+.4f}", tie_rows=int(tie.sum()), zero_obar_rows=zero_rows,
                        neg=f"{err[sel_neg].mean():+.3e}±{err[sel_neg].std() / np.sqrt(max(sel_neg.sum(), 1)):.1e}",
                        single_neg=f"{err[single].mean():+.3e}±{err[single].std() / np.sqrt(max(single.sum(), 1)):.1e}")

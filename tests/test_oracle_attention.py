@@ -303,7 +303,7 @@ def test_emulated_bias_reproduces_the_pages_finding(orc):
     small constant brings the bias back)."""
     errs = {}
     for seed in range(1001, 1031):
-        x = W.make("tiny", seed=seed)
+        x = W.make("tiny_sink", seed=seed)
         for key, guard, f32 in (("none", orc.GUARD_NONE, False), ("beta", orc.GUARD_BETA, False),
                                 ("eps", orc.GUARD_EPS, False), ("none32", orc.GUARD_NONE, True)):
             err, tie = _signed_error(orc, x, guard, f32)
