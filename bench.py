@@ -4,7 +4,9 @@ on one MI355X.
 
 One step = attn_fwd + attn_bwd (every stage of the path) over one batch of
 synthetic inputs that are resident in device memory before timing starts.
-Prints one JSON line (see the keys below).  The CPU oracle's FP64
+The headline value is measured with cold caches (a 1 GiB buffer written
+before each timed step, outside the timed region); the warm, back-to-back
+figure is reported beside it.  Prints one JSON line (see the keys below).  The CPU oracle's FP64
 forward+backward of the same workload is timed on the host as a baseline.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload gpt2s]
@@ -123,9 +125,41 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters  # ms
 
-    # ---- the timed region: exactly K steps, synchronised on both sides
-    ms_step = timed(step, args.steps, args.warmup)
-    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    # ---- the timed region: exactly K steps with cold caches.  Before each
+    # step a 1 GiB buffer is written (more than the 8 XCDs' L2 and the
+    # last-level cache hold together), so every step reads its inputs from
+    # HBM; HIP events on the launch stream bracket the step alone (the fill
+    # is outside them).  W untimed warm-up steps first; synchronised on both
+    # sides.  ms_per_step = mean over the K steps.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        evs[i][0].record(stream)
+        fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
+        evs[i][1].record(stream)
+        fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], out=bout, **kw)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    cold_steps = [e[0].elapsed_time(e[2]) for e in evs]
+    ms_step = float(np.mean(cold_steps))
+    cold_fwd = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    cold_bwd = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    del flush
+    print(f"[bench] {args.steps} cold steps: mean {ms_step:.4f} ms/step (median {np.median(cold_steps):.4f}); "
+          f"fwd {cold_fwd:.4f}, bwd {cold_bwd:.4f} ms (medians)", file=sys.stderr, flush=True)
+    # the warm figure beside it: K steps back to back (inputs may stay in the
+    # last-level cache from one step to the next)
+    ms_warm = timed(step, args.steps, 3)
+    print(f"[bench] {args.steps} warm steps back to back: {ms_warm:.4f} ms/step", file=sys.stderr, flush=True)
+    # the kernel's own per-row flags of the timed workload
+    fl = fout["row_flags"]
+    flag_counts = {"rows": int(fl.numel()), "tie_rows": int(((fl & 1) != 0).sum().item()),
+                   "zero_denominator_rows": int(((fl & 2) != 0).sum().item()),
+                   "guard_applied_rows": int(((fl & 4) != 0).sum().item())}
 
     # ---- per-kernel durations: each of the step's launches (attn_bwd is its
     # two stages, dQ then dK/dV) repeated back to back between HIP events on
@@ -159,28 +193,6 @@ def main():
     print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_dq {ms_dq:.4f}, bwd_dkdv {ms_dkdv:.4f}; "
           f"fwd with guard={other}: {ms_fwd_other:.4f}; bwd with delta=rowsum(dP*P): "
           f"{ms_bwd_dp:.4f}", file=sys.stderr, flush=True)
-
-    # ---- cold caches: before each step a 1 GiB buffer is written (more than
-    # the 8 XCDs' L2 and the last-level cache hold together), so the step
-    # reads its inputs from HBM; HIP events around the forward and the
-    # backward of each step only (the fill is outside them); medians
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    n_cold = max(20, min(args.steps, 100))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_cold)]
-    for i in range(n_cold):
-        flush.fill_(i & 0xFF)
-        evs[i][0].record(stream)
-        fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
-        evs[i][1].record(stream)
-        fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], out=bout, **kw)
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
-    cold_fwd = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
-    cold_bwd = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-    cold_step = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
-    del flush
-    print(f"[bench] cold caches (median of {n_cold}): step {cold_step:.4f} ms, fwd {cold_fwd:.4f}, "
-          f"bwd {cold_bwd:.4f}", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
@@ -234,9 +246,12 @@ def main():
         "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
         "fwd_ms_variants": variants,
         "bwd_ms_delta": {"rowsum(dO*O)": round(ms_dq + ms_dkdv, 5), "rowsum(dP*P)": round(ms_bwd_dp, 5)},
-        "cold": {"ms_per_step": round(cold_step, 5), "tflops": round(fl_step / (cold_step * 1e-3) / 1e12, 2),
-                 "fwd_ms": round(cold_fwd, 5), "bwd_ms": round(cold_bwd, 5), "steps": n_cold,
-                 "flush_bytes": 1 << 30},
+        "timing": "cold caches: a 1 GiB buffer written before each timed step, HIP events around the step only",
+        "cold": {"fwd_ms_median": round(cold_fwd, 5), "bwd_ms_median": round(cold_bwd, 5),
+                 "step_ms_median": round(float(np.median(cold_steps)), 5), "flush_bytes": 1 << 30},
+        "warm": {"ms_per_step": round(ms_warm, 5), "tflops": round(fl_step / (ms_warm * 1e-3) / 1e12, 2),
+                 "timing": "K steps back to back between two synchronisations"},
+        "row_flags": flag_counts,
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
@@ -260,7 +275,9 @@ def cpu_baseline(x, wl, args):
     to TFLOP/s with the same counted work per head."""
     import oracle as orc
 
-    nthreads = min(16, os.cpu_count() or 1)  # the host share of one GPU
+    # the host share of one GPU: a GPU box allots 16 host threads to each of
+    # its GPUs, whatever os.cpu_count() reports there
+    nthreads = min(16, os.cpu_count() or 1)
     nkv = wl.batch * wl.heads_kv
     heads = list(range(min(args.cpu_heads, nkv) if args.cpu_heads > 0 else nkv))
     p = orc.Problem(wl.batch, wl.heads_q, wl.heads_kv, wl.seqlen, wl.head_dim, wl.causal,
@@ -275,6 +292,7 @@ def cpu_baseline(x, wl, args):
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": min(nthreads, len(heads)),
+        "host_cpus_visible": os.cpu_count(),
         "kind": "oracle",
         "sample": f"FP64 forward+backward of {len(heads)} of {wl.batch * wl.heads_kv} KV heads "
                   f"({len(heads) * g} query heads) of the {wl.name} workload, {dt:.2f} s wall",
