@@ -17,7 +17,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB: another build of the same source (the sanitizer test builds
+# one with AddressSanitizer / UndefinedBehaviorSanitizer)
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 GUARD_NONE, GUARD_BETA, GUARD_EPS = 0, 1, 2
