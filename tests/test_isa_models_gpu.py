@@ -27,6 +27,7 @@ def probe():
     L = ctypes.CDLL(LIB)
     L.probe_mfma_bf16.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int]
     L.probe_exp2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    L.probe_mfma_fp8.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int]
     return L
 
 
@@ -104,3 +105,70 @@ def test_exp2_within_the_oracle_error_and_flush(probe):
     assert rel.max() <= bound
     # results that would be subnormal are flushed to zero (the oracle's ftz model)
     assert np.all(y[ref < 2.0 ** -126 * (1 - 2.0 ** -20)] == 0.0)
+
+
+def _e4m3_bits(x):
+    """E4M3 byte of each (already E4M3-valued) x, from the OCP layout."""
+    x = np.asarray(x, np.float64)
+    out = np.zeros(x.shape, np.uint8)
+    s = (x < 0).astype(np.uint8) << 7
+    ax = np.abs(x)
+    nz = ax > 0
+    e = np.floor(np.log2(np.where(nz, ax, 1.0))).astype(np.int64)
+    sub = nz & (e < -6)
+    norm = nz & ~sub
+    mant_n = np.round((ax / np.exp2(e.astype(np.float64)) - 1.0) * 8).astype(np.int64)
+    out[norm] = ((e[norm] + 7) << 3 | mant_n[norm]).astype(np.uint8)
+    out[sub] = np.round(ax[sub] / 2.0 ** -9).astype(np.uint8)
+    return out | s
+
+
+def _e4m3_exp(x):
+    _, e = np.frexp(np.where(x == 0, 1.0, np.abs(x)))
+    return np.where(x == 0, 0, np.maximum(e - 1, -6))
+
+
+@pytest.mark.parametrize("kind", ["attention", "normal", "subnormal"])
+def test_fp8_matrix_instruction_within_the_oracle_bound(probe, orc, kind):
+    """The 64-product scaled FP8 instruction (E4M3, unit scales) of the FP8
+    P̄V variant against chain_bound_fp8 (without its safety factors)."""
+    rng = np.random.default_rng({"attention": 7, "normal": 8, "subnormal": 9}[kind])
+    n = 48
+    if kind == "attention":
+        a = orc.e4m3_array(np.exp(-rng.uniform(0, 6, (n, 32, 64))) * 2.0 ** 7)
+        b = orc.e4m3_array(rng.normal(rng.uniform(-1, 1, (n, 1, 32)), 1, (n, 64, 32)))
+        c = rng.normal(0, 300, (n, 32, 32))
+    elif kind == "normal":
+        a = orc.e4m3_array(rng.normal(0, 30, (n, 32, 64)))
+        b = orc.e4m3_array(rng.normal(0, 2, (n, 64, 32)))
+        c = rng.normal(0, 50, (n, 32, 32)) * 2.0 ** rng.integers(-8, 8, (n, 1, 1))
+    else:
+        a = orc.e4m3_array(rng.uniform(-1, 1, (n, 32, 64)) * 2.0 ** -6)
+        b = orc.e4m3_array(rng.normal(0, 4, (n, 64, 32)))
+        c = rng.normal(0, 1e-3, (n, 32, 32))
+    c = c.astype(np.float32).astype(np.float64)
+    A = torch.from_numpy(_e4m3_bits(a)).cuda()
+    B = torch.from_numpy(_e4m3_bits(b)).cuda()
+    # the byte layout decodes back to the same values (torch's E4M3 type)
+    assert np.array_equal(A.view(torch.float8_e4m3fn).float().cpu().numpy().astype(np.float64), a)
+    C = torch.from_numpy(c.astype(np.float32)).cuda()
+    D = torch.empty_like(C)
+    assert probe.probe_mfma_fp8(A.data_ptr(), B.data_ptr(), C.data_ptr(), D.data_ptr(), n) == 0
+    torch.cuda.synchronize()
+    d = D.cpu().numpy().astype(np.float64)
+    sched = orc.Schedule(pv_chunk=64, chunk_err=0.5)  # the oracle doubles; 0.5 undoes that
+    worst, n_over = 0.0, 0
+    for w in range(n):
+        prods = a[w][:, None, :] * b[w].T[None, :, :]
+        es = (_e4m3_exp(a[w])[:, None, :] + _e4m3_exp(b[w]).T[None, :, :]).astype(np.int32)
+        for m in range(32):
+            for col in range(32):
+                terms = prods[m, col]
+                exact = math.fsum([c[w, m, col], *terms])
+                err = abs(d[w, m, col] - exact)
+                bound = orc.chain_bound_fp8(sched, c[w, m, col], terms, es[m, col], 0)
+                n_over += err > bound
+                if bound > 0:
+                    worst = max(worst, err / bound)
+    print(f"[isa] fp8 scaled mfma {kind}: worst error / bound = {worst:.3f}, over the bound: {n_over}")
+    assert n_over == 0
