@@ -35,8 +35,9 @@ the sink), copy K[a] into K[b] bit for bit, and add lambda*K[a] to Q[i]
 (lambda = plant_logit / (alpha * d * var_q_k)), which lifts both keys about
 plant_logit above the row's typical logit.  The named configurations use a
 lift of 3.5-4 standard deviations of the row's logits (tiny 3.5, GPT-2 8,
-Llama 4, stress 56): where a natural row maximum falls, so the pair is the
-row maximum in most planted rows without dominating the row.  The ``_sink``
+stress 56), where a natural row maximum falls, or 2 above the sink where the
+sink is the larger (Llama: sink 6, lift 8), so the pair is the row maximum
+in most planted rows without dominating the row.  The ``_sink``
 study workloads lift the pair 16-20 logits, the attention-sink regime in
 which the pages locate the biased rounding (P̄ = 1 exactly at the repeated
 maximum and a small same-sign residual from the rest).  The two keys have
@@ -116,7 +117,7 @@ WORKLOADS = {
                       4.0, 0.20, 0.0, 8.0, 1003,
                       "GPT-2 Medium attention layer B=8 H=16 N=1024 d=64 causal"),
     "llama8b": Workload("llama8b", 1, 32, 8, 8192, 128, True, 1.0, 1.0, "const", -0.3,
-                        6.0, 0.02, 0.0, 4.0, 1004,
+                        6.0, 0.02, 0.0, 8.0, 1004,
                         "Llama-3.1-8B GQA attention B=1 Hq=32 Hkv=8 N=8192 d=128 causal"),
     "stress": Workload("stress", 4, 8, 8, 4096, 128, False, 4.0, 4.0, "const", 0.0,
                        0.0, 0.30, 0.5, 56.0, 1005,

@@ -1,6 +1,6 @@
 // isa_probe.hip -- test infrastructure: runs single gfx950 instructions on
 // caller-chosen operands so that the tests can check the oracle's models of
-// them (bf16 and FP8 matrix instruction accumulation, exponential).  Not part of the
+// them (bf16, FP8 and FP4 matrix instruction accumulation, exponential).  Not part of the
 // library; shares no code with it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -59,6 +59,39 @@ __global__ void mfma_fp8_probe(const uint8_t* a, const uint8_t* b, const float* 
   for (int i = 0; i < 16; ++i) D[(8 * (i / 4) + 4 * kh + i % 4) * 32 + col] = acc[i];
 }
 
+// One v_mfma_scale_f32_32x32x64_f8f6f4 per wave with E2M1 (FP4) operands:
+// a [n][32][64] and b [n][64][32] E2M1 codes (one per byte, low nibble),
+// sa [n][32][2] and sb [n][2][32] E8M0 scale bytes (block h = k / 32 of a
+// row of A or a column of B), c/d [n][32][32] fp32.  Lane l supplies row /
+// column l%32 at k = 32*(l/32) + j in nibble j of its first four words, and
+// the scale of that block.
+__global__ void mfma_fp4_probe(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                               const float* c, float* d) {
+  const int w = blockIdx.x, l = threadIdx.x, col = l & 31, kh = l >> 5;
+  const uint8_t* A = a + (size_t)w * 2048;
+  const uint8_t* B = b + (size_t)w * 2048;
+  const float* C = c + (size_t)w * 1024;
+  float* D = d + (size_t)w * 1024;
+  i32x8 av = {0, 0, 0, 0, 0, 0, 0, 0}, bv = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int q = 0; q < 4; ++q) {
+    uint32_t wa = 0, wb = 0;
+    for (int j = 0; j < 8; ++j) {
+      const int k = 32 * kh + 8 * q + j;
+      wa |= (uint32_t)(A[col * 64 + k] & 15u) << (4 * j);
+      wb |= (uint32_t)(B[k * 32 + col] & 15u) << (4 * j);
+    }
+    av[q] = (int)wa;
+    bv[q] = (int)wb;
+  }
+  const int scale_a = sa[(size_t)w * 64 + col * 2 + kh];
+  const int scale_b = sb[(size_t)w * 64 + kh * 32 + col];
+  f32x16 acc;
+  for (int i = 0; i < 16; ++i) acc[i] = C[(8 * (i / 4) + 4 * kh + i % 4) * 32 + col];
+  // formats 4, 4: E2M1 operands; scale bytes in bits 0..7
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, scale_a, 0, scale_b);
+  for (int i = 0; i < 16; ++i) D[(8 * (i / 4) + 4 * kh + i % 4) * 32 + col] = acc[i];
+}
+
 __global__ void exp2_probe(const float* x, float* y, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = __builtin_amdgcn_exp2f(x[i]);
@@ -75,6 +108,14 @@ extern "C" int probe_mfma_fp8(const void* a, const void* b, const void* c, void*
   if (n <= 0) return 0;
   hipLaunchKernelGGL(mfma_fp8_probe, dim3(n), dim3(64), 0, 0, (const uint8_t*)a, (const uint8_t*)b,
                      (const float*)c, (float*)d);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+extern "C" int probe_mfma_fp4(const void* a, const void* b, const void* sa, const void* sb, const void* c,
+                              void* d, int n) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(mfma_fp4_probe, dim3(n), dim3(64), 0, 0, (const uint8_t*)a, (const uint8_t*)b,
+                     (const uint8_t*)sa, (const uint8_t*)sb, (const float*)c, (float*)d);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -28,6 +28,7 @@ def probe():
     L.probe_mfma_bf16.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int]
     L.probe_exp2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     L.probe_mfma_fp8.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int]
+    L.probe_mfma_fp4.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int]
     return L
 
 
@@ -171,4 +172,53 @@ def test_fp8_matrix_instruction_within_the_oracle_bound(probe, orc, kind):
                 if bound > 0:
                     worst = max(worst, err / bound)
     print(f"[isa] fp8 scaled mfma {kind}: worst error / bound = {worst:.3f}, over the bound: {n_over}")
+    assert n_over == 0
+
+
+E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
+
+
+@pytest.mark.parametrize("kind", ["unit", "attention", "wide"])
+def test_fp4_matrix_instruction_within_the_oracle_bound(probe, orc, kind):
+    """The scaled FP4 instruction of the MXFP4 variant (E2M1 codes, one E8M0
+    scale per row / column and 32-element block) against chain_bound_mx
+    (without its safety factor)."""
+    rng = np.random.default_rng({"unit": 31, "attention": 32, "wide": 33}[kind])
+    n = 48
+    ca = rng.integers(0, 16, (n, 32, 64)).astype(np.uint8)
+    cb = rng.integers(0, 16, (n, 64, 32)).astype(np.uint8)
+    if kind == "unit":
+        sa = np.full((n, 32, 2), 127, np.uint8); sb = np.full((n, 2, 32), 127, np.uint8)
+        c = rng.normal(0, 50, (n, 32, 32))
+    elif kind == "attention":   # P̄-like scales (2^-2 .. 2^-12) times V-like ones
+        sa = rng.integers(115, 126, (n, 32, 2)).astype(np.uint8)
+        sb = rng.integers(124, 128, (n, 2, 32)).astype(np.uint8)
+        c = rng.normal(0, 1, (n, 32, 32))
+    else:
+        sa = rng.integers(100, 150, (n, 32, 2)).astype(np.uint8)
+        sb = rng.integers(100, 150, (n, 2, 32)).astype(np.uint8)
+        c = rng.normal(0, 1, (n, 32, 32)) * 2.0 ** rng.integers(-20, 20, (n, 1, 1))
+    c = c.astype(np.float32).astype(np.float64)
+    a = E2M1[ca] * np.exp2(np.repeat(sa.astype(np.float64) - 127, 32, axis=2))
+    b = E2M1[cb] * np.exp2(np.repeat(sb.astype(np.float64) - 127, 32, axis=1))
+    args = [torch.from_numpy(np.ascontiguousarray(t)).cuda() for t in (ca, cb, sa, sb)]
+    C = torch.from_numpy(c.astype(np.float32)).cuda()
+    D = torch.empty_like(C)
+    assert probe.probe_mfma_fp4(*[t.data_ptr() for t in args], C.data_ptr(), D.data_ptr(), n) == 0
+    torch.cuda.synchronize()
+    d = D.cpu().numpy().astype(np.float64)
+    sched = orc.Schedule(chunk_err=0.5)  # the oracle doubles; 0.5 undoes that
+    worst, n_over = 0.0, 0
+    for w in range(n):
+        prods = a[w][:, None, :] * b[w].T[None, :, :]
+        for m in range(32):
+            for col in range(32):
+                terms = prods[m, col]
+                exact = math.fsum([c[w, m, col], *terms])
+                err = abs(d[w, m, col] - exact)
+                bound = orc.chain_bound_mx(sched, c[w, m, col], terms)
+                n_over += err > bound
+                if bound > 0:
+                    worst = max(worst, err / bound)
+    print(f"[isa] fp4 scaled mfma {kind}: worst error / bound = {worst:.3f}, over the bound: {n_over}")
     assert n_over == 0
