@@ -46,12 +46,14 @@
 // option.  ℓ stays the sum of the fp32 P̄.
 //
 // MXFP4 variant (the other format the pages name there): P̄ and V in E2M1
-// elements with one E8M0 scale per 32 keys, 2^(floor(log2 amax) - 2) of the
-// block's largest magnitude (v_cvt_scalef32_pk_fp4_f32 gives RNE(clamp(v /
-// scale)), measured), on v_mfma_scale_f32_32x32x64_f8f6f4: one instruction
-// per feature block and 64-key step.  Its k index 32h + j (h = lane half)
-// takes, in each lane, the 32 keys that half holds (key offset mod 8 in
-// 4h..4h+3), so those are the blocks, for P̄ and for V alike.
+// elements with one E8M0 scale per block of 32 consecutive keys (keys
+// 32h..32h+31 of a 64-key step), 2^(floor(log2 amax) - 2) of the block's
+// largest magnitude (v_cvt_scalef32_pk_fp4_f32 gives RNE(clamp(v / scale)),
+// measured), on v_mfma_scale_f32_32x32x64_f8f6f4: one instruction per
+// feature block and 64-key step, whose k index 32h + j is key 32h + j and
+// sits in lane half h.  S^T leaves each lane half with every fourth group
+// of four keys of both blocks, so one swap of lane halves (permlane32_swap)
+// gives half h the 32 P̄ of block h; V^T is read key-block by key-block.
 #include "attn_device.h"
 
 namespace attn {
@@ -203,23 +205,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
   const int jc = !wave_live ? 0 : (CAUSAL ? min(kend, q0 + 32) : kend);
 
   // MXFP4 product: this wave's feature blocks of the step's V^T operand,
-  // quantized (per lane: one feature, the 32 keys of its half) into LDS
+  // quantized (per lane: one feature, the 32 consecutive keys of its half's
+  // block) into LDS
   auto convert_mx = [&](const uint16_t* vs) {
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
       if (f % kWaves != wave) continue;  // uniform: static register indices below
-      // V^T, k order 8t + 4e + u: keys 16t + 8e + 4*half + u of feature 32f + l32
+      // V^T in key order: vx[o] = V[32*half + o][32f + l32]; transpose read
+      // t returns keys 32*half + 4t + 0..3
       float vx[32];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint2 v0 = lds_read_tr(vs + ta_off[f][0] + 16 * t * D);
-        const uint2 v1 = lds_read_tr(vs + ta_off[f][1] + 16 * t * D);
-        const uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          vx[8 * t + 2 * q] = __uint_as_float(w[q] << 16);
-          vx[8 * t + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-        }
+      for (int t = 0; t < 8; ++t) {
+        const uint2 w = lds_read_tr(vs + qidx<D>(32 * half + 4 * t + (r16 >> 2), 32 * f + 16 * (g16 & 1) + 4 * (r16 & 3)));
+        vx[4 * t] = __uint_as_float(w.x << 16);
+        vx[4 * t + 1] = __uint_as_float(w.x & 0xffff0000u);
+        vx[4 * t + 2] = __uint_as_float(w.y << 16);
+        vx[4 * t + 3] = __uint_as_float(w.y & 0xffff0000u);
       }
       float amax = 0.0f;
 #pragma unroll
@@ -320,8 +321,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
     if (GUARD == kGuardEps && tie) mn = rt + a.shift_eps;
 
     // ---- rescale by c = exp(m_old - m_new); c = 1 exactly where the shift
-    // did not move (and on the first step), so multiplying unconditionally
-    // changes nothing there and keeps the accumulator in one register set.
+    // did not move (and on the first step), so multiplying by it changes
+    // nothing there and keeps the accumulator in one register set.
     // FP8 product: the operand scale 2^k for this step (r - m <= 0 under
     // every guard, so k >= 7), the accumulator moved to it exactly
     {
@@ -334,10 +335,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
         co = c * pow2i(kn - pk);  // exact: a power of two
         pk = kn;
       }
+      // most steps move no row's shift: then the wave skips the products
+      // (x * 1 = x exactly, denormals included)
+      if (__builtin_amdgcn_ballot_w64(co != 1.0f) != 0) {
 #pragma unroll
-      for (int f = 0; f < FB; ++f)
+        for (int f = 0; f < FB; ++f)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[f][i] *= co;
+          for (int i = 0; i < 16; ++i) oacc[f][i] *= co;
+      }
       m = mn;
     }
     const float psc = PV_FP8 ? pow2i(pk) : 1.0f;
@@ -371,17 +376,28 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
           pf[t][u + 1] = (__bf16)p1;
         }
       }
-    // MXFP4: one block of 32 P̄ per lane (its row, its half's keys)
+    // MXFP4: one block of 32 P̄ per lane, its row's keys 32*half..+31 in
+    // key order.  pmx[i] and pmx[16 + i] hold keys 8(i/4) + 4*half + i%4 of
+    // block 0 and block 1; after the swap of lane halves w[0] and w[1] hold
+    // keys 8(i/4) + i%4 and 8(i/4) + 4 + i%4 of block `half`
     int sbp = 1;
     i32x8 pmb = {0, 0, 0, 0, 0, 0, 0, 0};
     if (PV_MX) {
+      float blk[32];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(pmx[i]), __float_as_uint(pmx[16 + i]), false, false);
+        const int o = 8 * (i >> 2) + (i & 3);
+        blk[o] = __uint_as_float(w[0]);
+        blk[o + 4] = __uint_as_float(w[1]);
+      }
       float amax = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(pmx[j], pmx[j + 1]));
+      for (int j = 0; j < 32; j += 2) amax = fmaxf(amax, fmaxf(blk[j], blk[j + 1]));
       sbp = mx_scale_byte(amax, a.pv_mx_ceil != 0);
       const float xs = __int_as_float(sbp << 23);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pmb[w] = (int)fp4x8(&pmx[8 * w], xs);
+      for (int w = 0; w < 4; ++w) pmb[w] = (int)fp4x8(&blk[8 * w], xs);
     }
 
     // ---- O^T += V^T P̄^T: four steps of 16 keys, in key order (the feature

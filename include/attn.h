@@ -163,10 +163,11 @@ typedef struct {
  *   question for the other format the pages name there.  The operands become
  *   MXFP4 in the OCP MX sense: E2M1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and
  *   negatives) sharing one E8M0 scale X = 2^(floor(log2 amax) - 2) per
- *   block, each element RNE(clamp(v / X, -6, 6)).  A block is 32 of the 64
- *   keys of a streaming step: those at key offsets 0..3 mod 8, or 4..7 mod 8
- *   -- per query row for P̄, per feature for V (over every key of the step
- *   that exists).  The scales are applied inside the scaled matrix
+ *   block, each element RNE(clamp(v / X, -6, 6)).  A block is 32
+ *   consecutive keys, the first or the second half of a 64-key streaming
+ *   step -- per query row for P̄, per feature for V (over every key of the
+ *   block that exists: V's operand serves every query row, so no row's
+ *   causal mask enters its scale).  The scales are applied inside the scaled matrix
  *   instruction; Ō, ℓ and the shift are as in the bf16 path.  With
  *   ATTN_PV_MX_CEIL the scales are 2^(ceil(log2 amax) - 2) instead (amax / X
  *   in (2, 4]: no element saturates; equal to the rule above when amax is a

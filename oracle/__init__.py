@@ -96,7 +96,7 @@ class Schedule:
         False, True / "row" (k per row and block: the row's largest P̄ in
         [128, 256)) or "fixed" (k = 8).
     pv_mxfp4: the P̄V product in MXFP4 (E2M1 elements, one E8M0 scale per 32
-        keys of a 64-key step, the keys split by offset mod 8 below / above 4);
+        consecutive keys: keys 0..31 and 32..63 of a 64-key step);
         True / "floor" (the OCP rule) or "ceil" (scale from ceil(log2 amax)).
     """
     block_n: int = 64

@@ -1405,13 +1405,14 @@ static void emu_head(void* c, int32_t item) {
         l32 = l32 + p32;
       }
       if (sc->pv_mxfp4) {
-        /* MXFP4 operand: the block's keys in two sets of 32 (key offset mod
-         * 8 below or above 4: what each half of a wave holds), each with
-         * the scale 2^(floor(log2 amax) - 2) of its largest P̄ */
+        /* MXFP4 operand: the step's keys in two blocks of 32 consecutive
+         * keys (OCP MX: a block is 32 consecutive elements along the
+         * contraction), each with the scale 2^(floor(log2 amax) - 2) of
+         * its largest P̄ */
         for (int h = 0; h < 2; ++h) {
           double amax = 0.0, rmax = 0.0;
           for (int32_t j = j0; j < j1; ++j)
-            if ((((j - j0) & 7) >> 2) == h) {
+            if (((j - j0) >> 5) == h) {
               amax = fmax(amax, pex[j - j0]);
               rmax = fmax(rmax, prho[j - j0]);
             }
@@ -1425,7 +1426,7 @@ static void emu_head(void* c, int32_t item) {
                              sbf(amax * (1.0 + rmax + 2.0 * U24)) != sbyte);
           if (s_amb) val_cert = 0;
           for (int32_t j = j0; j < j1; ++j) {
-            if ((((j - j0) & 7) >> 2) != h) continue;
+            if (((j - j0) >> 5) != h) continue;
             const double y = pex[j - j0] / X;
             const double pbv = orc_e2m1_round(y) * X;
             if (cert_on && pex[j - j0] > 0.0 &&
@@ -1450,12 +1451,13 @@ static void emu_head(void* c, int32_t item) {
         double vmax = 0.0, amb = 0.0;
         double vx[2] = {1.0, 1.0}; /* MXFP4: V's scales over the step's keys */
         if (sc->pv_mxfp4) {
-          /* every key of the 64-key step that exists (masked ones too: the
-           * kernel quantizes the tile before masking is known) */
+          /* per feature, over every key of the block that exists: V's
+           * operand is one for all query rows, so a row's causal mask
+           * cannot enter its scale */
           const int32_t jt = j0 + bn < N ? j0 + bn : N;
           double va[2] = {0.0, 0.0};
           for (int32_t j = j0; j < jt; ++j) {
-            const int h = ((j - j0) & 7) >> 2;
+            const int h = (j - j0) >> 5;
             va[h] = fmax(va[h], fabs((double)orc_f32_from_bf16(V[(size_t)j * d + f])));
           }
           for (int h = 0; h < 2; ++h)
@@ -1464,7 +1466,7 @@ static void emu_head(void* c, int32_t item) {
         for (int32_t j = j0; j < j1; ++j) {
           double vv = (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
           if (sc->pv_mxfp4) {
-            const double X = vx[((j - j0) & 7) >> 2];
+            const double X = vx[(j - j0) >> 5];
             vv = orc_e2m1_round(vv / X) * X;
           }
           if (sc->pv_fp8) {

@@ -81,8 +81,8 @@ typedef struct {
    * largest P̄ in [128, 256)); 2: k = 8.  0: bf16 operands.                 */
   int32_t pv_fp8;
   /* 1: the P̄V product in MXFP4 -- P̄ and V in E2M1 elements with one E8M0
-   * scale 2^(floor(log2 amax) - 2) per 32 keys (each 64-key step split by
-   * key offset mod 8 below / above 4), one scaled matrix instruction per
+   * scale 2^(floor(log2 amax) - 2) per 32 consecutive keys (keys 0..31 and
+   * 32..63 of each 64-key step), one scaled matrix instruction per
    * step.  Streaming schedule with block_n = 64 only.  2: the scales from
    * ceil(log2 amax) instead of floor.                                      */
   int32_t pv_mxfp4;

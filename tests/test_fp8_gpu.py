@@ -40,15 +40,15 @@ def _e4m3_bits(vbits):
 
 def _mx_bits(vbits, N, d, ceil=False):
     """bf16 bits of V quantized as the MXFP4 product takes it (exact in bf16):
-    per feature, blocks of the 32 keys of a 64-key step at offsets 0..3 or
-    4..7 mod 8, scale 2^(floor(log2 amax) - 2), elements RNE(clamp(v / X))
+    per feature, blocks of 32 consecutive keys (keys 0..31 and 32..63 of a
+    64-key step), scale 2^(floor(log2 amax) - 2), elements RNE(clamp(v / X))
     on the E2M1 grid (numpy's round is half-to-even)."""
     v = W.bits_to_f32(vbits).astype(np.float64).reshape(-1, N, d)
     out = np.zeros_like(v)
     keys = np.arange(N)
     for j0 in range(0, N, 64):
         for h in range(2):
-            idx = keys[(keys >= j0) & (keys < j0 + 64) & (((keys - j0) & 7) >> 2 == h)]
+            idx = keys[(keys >= j0 + 32 * h) & (keys < j0 + 32 * h + 32)]
             blk = v[:, idx, :]
             amax = np.abs(blk).max(axis=1, keepdims=True)
             rnd = np.ceil if ceil else np.floor

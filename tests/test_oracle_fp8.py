@@ -280,8 +280,8 @@ def test_mxfp4_q0_closed_form(orc, guard, rule):
     1/8, 0.969 * 8 = 7.75 saturates to 6: every operand is 0.75, so Ō is 0.75
     sum_j q(V_j) while ℓ = N exp(-2^-5) (O 23 % too small).  With the rule
     rounded up, X = 1/4 and 3.88 rounds to 4: every operand is 1, O 3.2 %
-    too large, as with FP8.  V's blocks: per feature, the 64-key step's keys
-    split by offset mod 8 below / above 4."""
+    too large, as with FP8.  V's blocks: per feature, keys 0..31 and 32..63
+    of the 64-key step."""
     N, d = 40, 64
     g = {"none": orc.GUARD_NONE, "eps": orc.GUARD_EPS}[guard]
     p, q, k, v = _q0_case(orc, N, d, g, 5)
@@ -289,7 +289,7 @@ def test_mxfp4_q0_closed_form(orc, guard, rule):
     vq = np.zeros_like(vf)
     for f in range(d):
         for h in range(2):
-            idx = [j for j in range(N) if ((j & 7) >> 2) == h]
+            idx = [j for j in range(N) if (j >> 5) == h]
             vq[idx, f] = _mx_quant(vf[idx, f], ceil=rule == "ceil")
     pq = 1.0 if guard == "none" or rule == "ceil" else 0.75
     s = orc.Schedule(block_n=64, round_n=512, obar_fp32=True, certify=False, pv_mxfp4=rule)
@@ -320,7 +320,7 @@ def test_mxfp4_single_block_direct(orc):
     vq = np.zeros_like(vf)  # V's blocks span every existing key of the step
     for f in range(d):
         for h in range(2):
-            idx = [j for j in range(N) if ((j & 7) >> 2) == h]
+            idx = [j for j in range(N) if (j >> 5) == h]
             vq[idx, f] = _mx_quant(vf[idx, f])
     checked = 0
     for i in range(N):
@@ -329,7 +329,7 @@ def test_mxfp4_single_block_direct(orc):
         pq = np.zeros_like(pbar)
         ok = True
         for h in range(2):
-            idx = [j for j in range(i + 1) if ((j & 7) >> 2) == h]
+            idx = [j for j in range(i + 1) if (j >> 5) == h]
             if not idx:
                 continue
             amax = pbar[idx].max()
