@@ -33,12 +33,14 @@ HBM_PEAK_GBS = 8000.0
 # bytes: x2.0; WRITE_SIZE all of them: x1.0).  Summary and commands:
 # profiles/bwd_dkdv_gpt2s_hbm_traffic.md.  The figures hold only for the
 # sources of that kernel they were taken on (SHA-256 over the files that
-# define it); otherwise the report says null.
+# define it) and for the workload they were taken on; otherwise the report
+# says null.
 KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd.hip", "attn_device.h", "attn_internal.h")}
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
-        "sources_sha256": "adf437863bdfb53ad269d34120cc708390af91bd7a618a5286543234d46517a2",
-        "fetch_kib": 64693.0, "write_kib": 51407.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "workload": "gpt2s",
+        "sources_sha256": "83b0e9ab459f5a44224d1fe3f0cf7e3295034542d0577b5e8ff5750aca786db5",
+        "fetch_kib": 65244.0, "write_kib": 51394.0, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
@@ -54,9 +56,9 @@ def kernel_sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, workload: str):
     m = MEASURED_TRAFFIC.get(kernel)
-    if m is None or m["sources_sha256"] != kernel_sources_sha256(kernel):
+    if m is None or m["workload"] != workload or m["sources_sha256"] != kernel_sources_sha256(kernel):
         return None
     return int(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]))
 
@@ -259,7 +261,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(dom),  # HBM bytes per launch
+            "traffic": measured_traffic(dom, args.workload),  # HBM bytes per launch
         },
     }
 
