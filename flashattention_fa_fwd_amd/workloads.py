@@ -37,7 +37,9 @@ plant_logit above the row's typical logit.  The named configurations use a
 lift of 3.5-4 standard deviations of the row's logits (tiny 3.5, GPT-2 8,
 stress 56), where a natural row maximum falls, or 2 above the sink where the
 sink is the larger (Llama: sink 6, lift 8), so the pair is the row maximum
-in most planted rows without dominating the row.  The ``_sink``
+in most planted rows without dominating the row.  ``gpt2s_dup``
+duplicates the keys without lifting the rows (the recipe as stated, where a
+pair is a row's maximum only by chance).  The ``_sink``
 study workloads lift the pair 16-20 logits, the attention-sink regime in
 which the pages locate the biased rounding (P̄ = 1 exactly at the repeated
 maximum and a small same-sign residual from the rest).  The two keys have
@@ -122,6 +124,12 @@ WORKLOADS = {
     "stress": Workload("stress", 4, 8, 8, 4096, 128, False, 4.0, 4.0, "const", 0.0,
                        0.0, 0.30, 0.5, 56.0, 1005,
                        "large-logit stress B=4 H=8 N=4096 d=128 non-causal"),
+    # study variant: keys duplicated as the configurations state, with no
+    # lift of the query rows (a pair is a row's maximum only where the
+    # duplicated key happens to be one)
+    "gpt2s_dup": Workload("gpt2s_dup", 16, 12, 12, 1024, 64, True, 1.5, 1.5, "mu_uniform", 0.0,
+                          4.0, 0.05, 0.0, 0.0, 1002,
+                          "GPT-2 Small attention layer B=16 H=12 N=1024 d=64 causal, keys duplicated, no lift"),
     # study variants in the attention-sink regime where the pages locate the
     # biased rounding: the planted pair 16-20 logits above the row, so every
     # other P̄ of a tie row is tiny (same shapes and distributions otherwise)

@@ -54,14 +54,28 @@ def _signed_errors(name, guard, obar_fp32, heads, sched="stream"):
     err = (ob - ob64) / l64[..., None]
     tie = ((st["flags"] & orc.ROW_TIE) != 0).reshape(-1, wl.seqlen)[heads]
     cert = st["flag_cert"].reshape(-1, wl.seqlen)[heads].astype(bool)
-    gpu_tie = ((r["row_flags"].cpu().numpy() & 1) != 0).reshape(-1, wl.seqlen)[heads]
+    gflags = r["row_flags"].cpu().numpy().reshape(-1, wl.seqlen)[heads]
+    gpu_tie = (gflags & orc.ROW_TIE) != 0
     assert np.array_equal(gpu_tie[cert], tie[cert])
+    # rows whose weights all underflowed (ℓ = 0: a tie at a maximum r above
+    # ~88.7 under the beta guard, whose shift 2r puts every weight below
+    # fp32's range), and rows where such a tie was broken later by a larger
+    # key (the rescale exp(2 r_old - r_new) overflows and multiplies the
+    # underflowed ℓ: NaN) carry no rounding bias; they are left out, counted
+    # and reported
+    gl = r["row_l"].float().cpu().numpy().reshape(-1, wl.seqlen)[heads]
+    ok = np.isfinite(gl) & (gl > 0)
+    live = cert & ok
+    nz, nn = int((cert & (gl == 0)).sum()), int((cert & ~np.isfinite(gl)).sum())
+    if nz or nn:
+        report(f"rows left out, {name} guard={guard} obar={'fp32' if obar_fp32 else 'bf16'}",
+               zero_denominator=nz, non_finite=nn, tie_rows=int((tie & cert).sum()))
     # negative-dominated features: V column mean over the keys < 0
     g = wl.heads_q // wl.heads_kv
     vv = W.bits_to_f32(x["v"]).astype(np.float64).reshape(-1, wl.seqlen, wl.head_dim)
     kvh = [(h // wl.heads_q) * wl.heads_kv + (h % wl.heads_q) // g for h in heads]
     neg = vv[kvh].mean(axis=1) < 0  # [heads, d]
-    return err, tie & cert, neg, l64
+    return err, tie & live, ~tie & live, neg, l64
 
 
 def _row_stats(err, sel):
@@ -79,10 +93,10 @@ def _row_stats(err, sel):
 def _measure(name, heads):
     res = {}
     for guard, f32 in (("none", False), ("beta", False), ("eps", False), ("none", True), ("beta", True)):
-        err, tie, neg, _ = _signed_errors(name, guard, f32, heads)
+        err, tie, other, neg, _ = _signed_errors(name, guard, f32, heads)
         sel_neg = tie[..., None] & neg[:, None, :]
         sel_pos = tie[..., None] & ~neg[:, None, :]
-        single = ~tie[..., None] & neg[:, None, :]
+        single = other[..., None] & neg[:, None, :]
         res[(guard, f32)] = dict(neg=_row_stats(err, sel_neg), pos=_row_stats(err, sel_pos),
                                  single=_row_stats(err, single))
     for (guard, f32), d in res.items():
@@ -127,7 +141,7 @@ def test_eps_guard_bias_closed_form():
     name, heads = "gpt2s_sink", list(range(0, 192, 12))
     x = make(name)
     wl = x["workload"]
-    err, tie, neg, l64 = _signed_errors(name, "eps", False, heads)
+    err, tie, _, neg, l64 = _signed_errors(name, "eps", False, heads)
     w_dev = float(np.float32(0.96875)) - float(np.exp(np.float32(-SHIFT_EPS)).astype(np.float64))
     vv = W.bits_to_f32(x["v"]).astype(np.float64)
     pred = np.full(err.shape, np.nan)
@@ -170,7 +184,7 @@ def test_bias_under_other_schedules(sched):
     heads = list(range(0, 192, 12))
     res = {}
     for guard in ("none", "beta"):
-        err, tie, neg, _ = _signed_errors("gpt2s_sink", guard, False, heads, sched)
+        err, tie, _, neg, _ = _signed_errors("gpt2s_sink", guard, False, heads, sched)
         sel_neg = tie[..., None] & neg[:, None, :]
         res[guard] = _row_stats(err, sel_neg)
         report(f"signed error gpt2s_sink schedule={sched} guard={guard}",
@@ -178,3 +192,15 @@ def test_bias_under_other_schedules(sched):
     m, se, n = res["none"]
     assert n > 300 and m < -3 * se
     assert abs(res["beta"][0]) <= 1e-4
+
+
+@pytest.mark.parametrize("name,heads", [("gpt2s_dup", list(range(0, 192, 12))), ("stress", list(range(0, 32, 4)))])
+def test_bias_key_duplication_and_large_logits(name, heads):
+    """Two more inputs, measured and reported: keys duplicated without any
+    lift of the query rows (the recipe as stated; a pair is a row's maximum
+    only where the duplicated key happens to be one), and the large-logit
+    shape (row maxima 30-60, d = 128, non-causal)."""
+    res = _measure(name, heads)
+    assert res[("none", False)]["neg"][2] > 50
+    assert abs(res[("beta", False)]["neg"][0]) <= 1e-4
+    assert abs(res[("none", True)]["neg"][0]) <= 1e-4
