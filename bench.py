@@ -273,12 +273,13 @@ def main():
 
 def cpu_baseline(x, wl, args):
     """The FP64 oracle (forward+backward of softmax attention) on the same
-    workload (or its first --cpu-heads KV heads), all host threads.  Scaled
-    to TFLOP/s with the same counted work per head."""
+    workload (or its first --cpu-heads KV heads) on the host threads one GPU
+    may use (at most 16).  Scaled to TFLOP/s with the same counted work per
+    head."""
     import oracle as orc
 
-    # the host share of one GPU: a GPU box allots 16 host threads to each of
-    # its GPUs, whatever os.cpu_count() reports there
+    # one GPU's share of a shared host is 16 threads, whatever
+    # os.cpu_count() reports; the visible count is printed beside it
     nthreads = min(16, os.cpu_count() or 1)
     nkv = wl.batch * wl.heads_kv
     heads = list(range(min(args.cpu_heads, nkv) if args.cpu_heads > 0 else nkv))
