@@ -1313,7 +1313,9 @@ static void emu_head(void* c, int32_t item) {
       if (have_m && mn != m) {
         if (mn < m) exb |= ORC_EX_SHIFT_DECREASED;
         double cexact = exp((double)m - (double)mn);
-        /* kernel: c = exp2(fl32(fl32(m_old - m_new) * log2e)), then fl32(c * Ō) */
+        /* bound for an fp32 evaluation: the argument (m_old - m_new) log2 e
+         * formed in fp32 and passed to a base-2 exponential of relative
+         * error exp_err, the product c Ō rounded to fp32 */
         double dm2 = fabs((double)m - (double)mn) * log2e;
         double rho_c = log(2.0) * (2.0 * U24 * dm2) + exp_err + m_err + m_err_new;
         /* the same exp flushes a result below the threshold to zero */
@@ -1333,9 +1335,11 @@ static void emu_head(void* c, int32_t item) {
       m = mn;
       m_err = m_err_new;
       have_m = 1;
-      /* FP8 product: the operand scale 2^ks of this block, from the same
-       * fp32 operations as the kernel (row scale), or 2^8 (fixed); ks_amb:
-       * the kernel's r may lie on the other side of an integer step */
+      /* FP8 product: the operand scale 2^ks of this block (row scale), or
+       * 2^8 (fixed).  The row scale is an integer decided by floating
+       * point, so it is taken in the implementation's precision (fp32:
+       * floor(fl32(fl32(r - m) log2 e))); ks_amb: the implementation's r may
+       * lie on the other side of an integer step */
       int ks = 8, ks_amb = 0;
       if (sc->pv_fp8 == 1) {
         const float d2 = (r - mn) * (float)1.44269504088896340736;
@@ -1353,7 +1357,9 @@ static void emu_head(void* c, int32_t item) {
       for (int32_t j = j0; j < j1; ++j) {
         double xe = alpha * sv[j] - (double)m;
         double pbar = exp(xe);
-        /* kernel: P̄ = exp2(fma(s, fl32(alpha log2e), -fl32(m log2e))) */
+        /* bound for an fp32 evaluation: the argument s alpha log2 e - m log2 e
+         * formed in fp32 (one fused step) and passed to a base-2
+         * exponential of relative error exp_err */
         double x2 = xe * log2e;
         double err_x2 = log2e * alpha * sb[j] * (1.0 + U24) + log2e * m_err +
                         U24 * (fabs(alpha * sv[j] * log2e) + fabs((double)m * log2e) + fabs(x2));
