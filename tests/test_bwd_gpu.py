@@ -467,3 +467,35 @@ def test_stated_tolerance_literally():
         figs[key] = f"{mx:.2e}/{mean:.2e}{'' if met else ' MISSED'}"
     report("stated tolerance (max/mean rel) gpt2s beta", **figs)
     assert ok, figs
+
+
+@pytest.mark.xfail(strict=False, reason="the bf16 P and dS operands and the bf16 gradients alone "
+                   "put dQ, dK, dV at 2.1-2.4e-3 mean rel (measured), just above 2e-3")
+@pytest.mark.parametrize("name,kv", [("gpt2s", [0, 100]), ("gpt2m", [3, 77])])
+def test_stated_tolerance_in_the_accurate_modes(name, kv):
+    """The stated acceptance taken literally (max rel <= 1e-2, mean rel <=
+    2e-3 against FP64 for O, delta, dQ, dK, dV) in the method's two accurate
+    modes together: fp32 Ō in the forward ([S] "Key claims" and the QK-Guard
+    abstract) and delta = rowsum(dP∘P) in the backward ([R] method, paper
+    §3.2), which removes the bf16 rounding of Ō and the delta taken from the
+    bf16 O.  What remains are the bf16 P and dS matrix operands and the bf16
+    outputs."""
+    x = make(name)
+    wl = x["workload"]
+    p = problem(wl, "beta")
+    f, b = _fwd_bwd(x, "beta", obar_fp32=True, delta="dp_p")
+    ref = orc.bwd_f64(p, x["q"], x["k"], x["v"], x["do"], kv_heads=kv, nthreads=threads())
+    shp = (-1, wl.seqlen, wl.head_dim)
+    figs, ok = {}, True
+    for key, gpu, r in (("o", f32(f["o"]).reshape(shp)[kv], ref["o"].reshape(shp)[kv]),
+                        ("dq", f32(b["dq"]).reshape(shp)[kv], ref["dq"].reshape(shp)[kv]),
+                        ("dk", f32(b["dk"]).reshape(shp)[kv], ref["dk"].reshape(shp)[kv]),
+                        ("dv", f32(b["dv"]).reshape(shp)[kv], ref["dv"].reshape(shp)[kv]),
+                        ("delta", b["delta"].cpu().numpy().reshape(-1, wl.seqlen)[kv],
+                         ref["delta"].reshape(-1, wl.seqlen)[kv])):
+        mx, mean = rel_errors(gpu, r)
+        met = mx <= MAX_REL and mean <= MEAN_REL
+        ok &= met
+        figs[key] = f"{mx:.2e}/{mean:.2e}{'' if met else ' MISSED'}"
+    report(f"stated tolerance, fp32 Ō and rowsum(dP∘P) (max/mean rel) {name} beta", **figs)
+    assert ok, figs
