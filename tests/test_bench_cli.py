@@ -14,3 +14,21 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2, (r.returncode, r.stderr[-500:])
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_measured_traffic_is_keyed_by_workload_and_sources():
+    """roofline.traffic is reported only for the workload and the kernel
+    sources the counters were taken on (host only: no device is touched)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    m = b.MEASURED_TRAFFIC["bwd_dkdv"]
+    t = b.measured_traffic("bwd_dkdv", m["workload"])
+    if m["sources_sha256"] == b.kernel_sources_sha256("bwd_dkdv"):
+        assert t == int(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]))
+    else:
+        assert t is None
+    for other in ("gpt2m", "llama8b", "stress", "tiny"):
+        assert b.measured_traffic("bwd_dkdv", other) is None
+    assert b.measured_traffic("attn_fwd", m["workload"]) is None
