@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (PV == 0 ? 4 : 3) : 2) void fwd
         co = c * pow2i(kn - pk);  // exact: a power of two
         pk = kn;
       }
-      // most steps move no row's shift: then the wave skips the products
+      // a step that moves no shift of the wave's rows skips the products
       // (x * 1 = x exactly, denormals included)
       if (__builtin_amdgcn_ballot_w64(co != 1.0f) != 0) {
 #pragma unroll
