@@ -1222,360 +1222,477 @@ typedef struct {
   const int32_t *rows_qh, *rows_i; /* row list mode: item = one (head, row) */
 } emu_ctx;
 
+/* Working state of the emulation of one head: buffers for the row's scores,
+ * the step's P̄ operand and Ō with its certification bookkeeping, and the
+ * running values of the row being replayed. */
+typedef struct {
+  const orc_problem* p;
+  const orc_schedule* sc;
+  const uint16_t *Q, *K, *V;
+  int32_t N, d, bn, rn;
+  int cert_on;
+  double exp_err; /* relative error of the implementation's exponential */
+  double under;   /* smallest nonzero result of that exponential */
+  /* one row */
+  double *sv, *sb; /* exact scores and the bounds on the implementation's */
+  float* tv;       /* fp32 scaled logits */
+  /* one step (block of keys), indexed by key - j0 */
+  double* pb;   /* P̄ as the matrix operand */
+  double* pamb; /* how far the implementation's operand may differ */
+  double* pex;  /* exact P̄ (MXFP4: before the block scale is known) */
+  double* prho; /* relative bound on the implementation's P̄ */
+  int* pexp;    /* E4M3 exponents of 2^ks P̄ */
+  int* texp;    /* exponents of the FP8 products */
+  double* terms;
+  /* one feature of Ō: value, bound of the current step, carried deviation,
+   * certified */
+  double *ob, *obb, *odv;
+  uint8_t* oc;
+  /* the row's running state */
+  float r, r2, m, l32;
+  int have_m, dec_cert, val_cert, tie, zero_ambig;
+  double m_err; /* bound on |implementation's shift - m| */
+  double dmax;  /* largest logit error so far */
+  double flush_slack; /* total size of the step's P̄ that may flush to zero */
+  int ks, ks_amb;     /* FP8: operand scale exponent, and whether it is uncertain */
+  uint8_t exb;
+} emu_state;
+
+static const double kLog2eD = 1.4426950408889634;
+
+/* The row's exact scores q_i . k_j, the bounds on the implementation's fp32
+ * scores, and the fp32 scaled logits. */
+static void emu_scores(emu_state* st, int32_t i, int32_t n) {
+  const uint16_t* qi = st->Q + (size_t)i * st->d;
+  for (int32_t j = 0; j < n; ++j) {
+    if (st->cert_on) {
+      st->sv[j] = dot_with_bound(st->sc, qi, st->K + (size_t)j * st->d, st->d, st->terms, &st->sb[j]);
+    } else {
+      st->sv[j] = dot_bf16(qi, st->K + (size_t)j * st->d, st->d);
+      st->sb[j] = 0.0;
+    }
+    st->tv[j] = scaled_logit(st->p, st->sv[j]);
+  }
+}
+
+static void emu_row_start(emu_state* st) {
+  st->r = -INFINITY;
+  st->r2 = -INFINITY;
+  st->m = 0.0f;
+  st->l32 = 0.0f;
+  st->have_m = 0;
+  st->dec_cert = st->cert_on;
+  st->val_cert = st->cert_on;
+  st->tie = 0;
+  st->zero_ambig = 0;
+  st->m_err = 0.0;
+  st->exb = 0;
+  st->dmax = 0.0;
+  for (int32_t f = 0; f < st->d; ++f) {
+    st->ob[f] = 0.0;
+    st->obb[f] = 0.0;
+    st->odv[f] = 0.0;
+    st->oc[f] = (uint8_t)st->cert_on;
+  }
+}
+
+/* 1. Running top two of the scaled logits over keys j0 .. j1-1. */
+static void emu_top_two(emu_state* st, int32_t j0, int32_t j1) {
+  for (int32_t j = j0; j < j1; ++j) {
+    float t = st->tv[j];
+    if (t > st->r) {
+      st->r2 = st->r;
+      st->r = t;
+    } else if (t > st->r2) {
+      st->r2 = t;
+    }
+    double e = logit_error(st->p, st->sv[j], st->sb[j]);
+    if (e > st->dmax) st->dmax = e;
+  }
+}
+
+/* 2. Tie decision and shift after the step; *m_err_new: the bound on the
+ * implementation's shift, which comes from its own r, within dmax of this
+ * one: m = r, r + eps (slope 1), beta r (slope beta) or 0 (no error). */
+static float emu_shift(emu_state* st, double* m_err_new) {
+  const orc_problem* p = st->p;
+  st->tie = tie_test(p, st->r, st->r2);
+  if (st->cert_on && !tie_certain(p, st->r, st->r2, st->dmax)) st->dec_cert = 0;
+  float mn = guard_shift(p, st->r, st->tie);
+  if (st->tie && p->guard == ORC_GUARD_BETA && st->r == 0.0f) st->exb |= ORC_EX_ZERO_MAX_TIE;
+  double slope_m = 1.0;
+  if (st->tie && p->guard == ORC_GUARD_BETA) slope_m = st->r > 0.0f ? (double)p->beta : 0.0;
+  *m_err_new = st->cert_on ? slope_m * st->dmax * (1.0 + 4.0 * U24) : 0.0;
+  return mn;
+}
+
+/* 3a. Rescale the running sums by c = exp(m_old - m_new), then take the new
+ * shift. */
+static void emu_rescale(emu_state* st, float mn, double m_err_new) {
+  if (st->have_m && mn != st->m) {
+    if (mn < st->m) st->exb |= ORC_EX_SHIFT_DECREASED;
+    double cexact = exp((double)st->m - (double)mn);
+    /* bound for an fp32 evaluation: the argument (m_old - m_new) log2 e
+     * formed in fp32 and passed to a base-2 exponential of relative
+     * error exp_err, the product c Ō rounded to fp32 */
+    double dm2 = fabs((double)st->m - (double)mn) * kLog2eD;
+    double rho_c = log(2.0) * (2.0 * U24 * dm2) + st->exp_err + st->m_err + m_err_new;
+    /* the same exp flushes a result below the threshold to zero */
+    if (cexact <= st->under * (1.0 + 4.0 * rho_c)) {
+      if (cexact >= st->under * (1.0 - 4.0 * rho_c)) st->zero_ambig = 1;
+      cexact = (cexact < st->under) ? 0.0 : cexact;
+    }
+    float c32 = (float)cexact;
+    if (isinf(c32)) st->exb |= ORC_EX_RESCALE_OVERFLOW;
+    for (int32_t f = 0; f < st->d; ++f) {
+      st->ob[f] = cexact * st->ob[f];
+      st->obb[f] = st->obb[f] * cexact * (1.0 + rho_c) + fabs(st->ob[f]) * (rho_c + U24);
+      st->odv[f] = st->odv[f] * cexact * (1.0 + rho_c);
+    }
+    st->l32 = c32 * st->l32;
+  }
+  st->m = mn;
+  st->m_err = m_err_new;
+  st->have_m = 1;
+}
+
+/* FP8 product: the operand scale 2^ks of the step (row scale), or 2^8
+ * (fixed).  The row scale is an integer decided by floating point, so it is
+ * taken in the implementation's precision (fp32: floor(fl32(fl32(r - m)
+ * log2 e))); ks_amb: the implementation's r may lie on the other side of an
+ * integer step. */
+static void emu_fp8_scale(emu_state* st) {
+  const orc_problem* p = st->p;
+  st->ks = 8;
+  st->ks_amb = 0;
+  if (st->sc->pv_fp8 != 1) return;
+  const float d2 = (st->r - st->m) * (float)1.44269504088896340736;
+  const float fd = floorf(d2);
+  st->ks = 7 - (int)(fd >= -113.0f ? fd : -113.0f);
+  double slope = p->guard == ORC_GUARD_BETA ? fabs((double)p->beta - 1.0) : 1.0;
+  double slack = 1.01 * slope * kLog2eD * st->dmax +
+                 8.0 * U24 * kLog2eD * (fabs((double)st->r) + fabs((double)st->m));
+  /* where the shift is r itself, r - m = 0 on both sides */
+  if (st->m != st->r && ((double)d2 - (double)fd <= slack || (double)fd + 1.0 - (double)d2 <= slack))
+    st->ks_amb = 1;
+  if (st->ks_amb && st->cert_on) st->val_cert = 0;
+}
+
+static void emu_note_pbar_one(emu_state* st, double pbv) {
+  if (pbv == 1.0) {
+    if (st->tie) st->exb |= ORC_EX_PBAR_ONE_TIED;
+    if (!st->tie) st->exb |= ORC_EX_PBAR_ONE_PRE_TIE;
+  }
+}
+
+/* 3b. P̄ = exp(t - m) for keys j0 .. j1-1 as the matrix operand: rounded to
+ * bf16, or 2^ks P̄ rounded to E4M3 (MXFP4: emu_mx_pbar, once the block
+ * scales are known); 4. the fp32 denominator ℓ, the sum of the fp32 P̄. */
+static void emu_pbar(emu_state* st, int32_t j0, int32_t j1) {
+  const orc_schedule* sc = st->sc;
+  const double alpha = (double)st->p->alpha;
+  const double m = (double)st->m;
+  const double kscale = ldexp(1.0, st->ks);
+  st->flush_slack = 0.0;
+  for (int32_t j = j0; j < j1; ++j) {
+    const int32_t u = j - j0;
+    double xe = alpha * st->sv[j] - m;
+    double pbar = exp(xe);
+    /* bound for an fp32 evaluation: the argument s alpha log2 e - m log2 e
+     * formed in fp32 (one fused step) and passed to a base-2
+     * exponential of relative error exp_err */
+    double x2 = xe * kLog2eD;
+    double err_x2 = kLog2eD * alpha * st->sb[j] * (1.0 + U24) + kLog2eD * st->m_err +
+                    U24 * (fabs(alpha * st->sv[j] * kLog2eD) + fabs(m * kLog2eD) + fabs(x2));
+    double rho = log(2.0) * err_x2 + st->exp_err;
+    double pbv;
+    st->pamb[u] = 0.0;
+    st->pex[u] = pbar < st->under ? 0.0 : pbar;
+    st->prho[u] = rho;
+    if (sc->pv_mxfp4) {
+      pbv = 0.0; /* set by emu_mx_pbar */
+      if (pbar <= st->under * (1.0 + 4.0 * rho)) {
+        st->pex[u] = 0.0;
+        if (pbar >= st->under * (1.0 - 4.0 * rho)) st->zero_ambig = 1;
+        st->flush_slack += 2.0 * pbar;
+      }
+    } else if (pbar <= st->under * (1.0 + 4.0 * rho)) {
+      /* at or below the flush threshold: the implementation gives 0 or a
+       * tiny value; take 0 and count the whole size as uncertainty */
+      pbv = 0.0;
+      if (pbar >= st->under * (1.0 - 4.0 * rho)) st->zero_ambig = 1;
+      st->flush_slack += 2.0 * pbar;
+    } else if (sc->pv_fp8) {
+      /* FP8 operand: P̄ * 2^ks rounded to E4M3, scaled back (exact) */
+      const double ps = pbar * kscale;
+      pbv = orc_e4m3_round(ps) / kscale;
+      if (st->cert_on && orc_e4m3_boundary_distance(ps) <= (rho + 2.0 * U24) * ps) {
+        st->val_cert = 0;
+        st->pamb[u] = orc_e4m3_ulp(ps * (1.0 + rho)) / kscale; /* a neighbour */
+      }
+      /* another scale changes the rounding only among the subnormals */
+      if (st->cert_on && st->ks_amb && ps < 0x1p-5) st->pamb[u] = fmax(st->pamb[u], 0x1p-9 / kscale * 2.0);
+    } else {
+      pbv = (double)orc_f32_from_bf16(orc_bf16_from_f64(pbar));
+      /* a P̄ next to a rounding boundary may take the neighbouring bf16
+       * value in the implementation: that one step, times |V|, joins each
+       * element's bound, so only elements that stay clear of a boundary by
+       * it are certified */
+      if (st->cert_on && orc_bf16_boundary_distance(pbar) <= (rho + 2.0 * U24) * pbar)
+        st->pamb[u] = orc_bf16_ulp(pbar * (1.0 + rho));
+    }
+    st->pexp[u] = pbv != 0.0 ? e4m3_exponent(pbv * kscale) : 0;
+    emu_note_pbar_one(st, pbv);
+    st->pb[u] = pbv;
+    /* 4. fp32 denominator: sum of the fp32 P̄ (sequential order here) */
+    float p32 = (pbar < st->under) ? 0.0f : (float)pbar;
+    st->l32 = st->l32 + p32;
+  }
+}
+
+/* MXFP4 operand: the step's keys in two blocks of 32 consecutive keys (OCP
+ * MX: a block is 32 consecutive elements along the contraction), each with
+ * the scale 2^(floor(log2 amax) - 2) of its largest P̄ (or ceil). */
+static void emu_mx_pbar(emu_state* st, int32_t j0, int32_t j1) {
+  const orc_schedule* sc = st->sc;
+  for (int h = 0; h < 2; ++h) {
+    double amax = 0.0, rmax = 0.0;
+    for (int32_t j = j0; j < j1; ++j)
+      if (((j - j0) >> 5) == h) {
+        amax = fmax(amax, st->pex[j - j0]);
+        rmax = fmax(rmax, st->prho[j - j0]);
+      }
+    int (*sbf)(double) = sc->pv_mxfp4 == 2 ? orc_mx_scale_byte_ceil : orc_mx_scale_byte;
+    const int sbyte = sbf(amax);
+    const double X = ldexp(1.0, sbyte - 127);
+    /* the implementation's amax is within rmax of this one: its scale may
+     * be the neighbouring power of two */
+    const int s_amb = st->cert_on && amax > 0.0 &&
+                      (sbf(amax * (1.0 - rmax - 2.0 * U24)) != sbyte ||
+                       sbf(amax * (1.0 + rmax + 2.0 * U24)) != sbyte);
+    if (s_amb) st->val_cert = 0;
+    for (int32_t j = j0; j < j1; ++j) {
+      const int32_t u = j - j0;
+      if ((u >> 5) != h) continue;
+      const double y = st->pex[u] / X;
+      const double pbv = orc_e2m1_round(y) * X;
+      if (st->cert_on && st->pex[u] > 0.0 &&
+          orc_e2m1_boundary_distance(y) <= (st->prho[u] + 2.0 * U24) * y) {
+        st->val_cert = 0;
+        st->pamb[u] = orc_e2m1_spacing(y * (1.0 + st->prho[u])) * X;
+      }
+      if (s_amb) st->pamb[u] = fmax(st->pamb[u], 4.0 * X);
+      emu_note_pbar_one(st, pbv);
+      st->pb[u] = pbv;
+    }
+  }
+}
+
+/* The step's products P̄_j V_jf for feature f as they enter the sum (V
+ * rounded as the product's format takes it); *vmax: the largest |V|
+ * operand, *amb: how far the operand ambiguity of P̄ can move the sum. */
+static void emu_terms(emu_state* st, int32_t f, int32_t j0, int32_t j1, double* vmax, double* amb) {
+  const orc_schedule* sc = st->sc;
+  const int32_t d = st->d;
+  double vx[2] = {1.0, 1.0}; /* MXFP4: V's scales over the step's keys */
+  if (sc->pv_mxfp4) {
+    /* per feature, over every key of the block that exists: V's operand is
+     * one for all query rows, so a row's causal mask cannot enter its scale */
+    const int32_t jt = j0 + st->bn < st->N ? j0 + st->bn : st->N;
+    double va[2] = {0.0, 0.0};
+    for (int32_t j = j0; j < jt; ++j) {
+      const int h = (j - j0) >> 5;
+      va[h] = fmax(va[h], fabs((double)orc_f32_from_bf16(st->V[(size_t)j * d + f])));
+    }
+    for (int h = 0; h < 2; ++h)
+      vx[h] = ldexp(1.0, (sc->pv_mxfp4 == 2 ? orc_mx_scale_byte_ceil(va[h]) : orc_mx_scale_byte(va[h])) - 127);
+  }
+  *vmax = 0.0;
+  *amb = 0.0;
+  for (int32_t j = j0; j < j1; ++j) {
+    const int32_t u = j - j0;
+    double vv = (double)orc_f32_from_bf16(st->V[(size_t)j * d + f]);
+    if (sc->pv_mxfp4) {
+      const double X = vx[u >> 5];
+      vv = orc_e2m1_round(vv / X) * X;
+    }
+    if (sc->pv_fp8) {
+      vv = orc_e4m3_round(vv); /* the FP8 V operand */
+      st->texp[u] = vv != 0.0 ? st->pexp[u] + e4m3_exponent(vv) : 0;
+    }
+    st->terms[u] = st->pb[u] * vv; /* exact: 8-bit x 8-bit mantissas */
+    *vmax = fmax(*vmax, fabs(vv));
+    *amb += st->pamb[u] * fabs(vv);
+  }
+}
+
+/* 3c, FA2 as tensor operations: the step's own product sum rounded to bf16,
+ * then added to the rescaled Ō and rounded again (every step is a rounding
+ * point); a P̄ next to a rounding boundary may take the neighbouring value,
+ * which moves the step's sum by up to amb. */
+static void emu_obar_block_bf16(emu_state* st, int32_t f, int32_t nt, double vmax, double amb) {
+  dd_t bacc = {0.0, 0.0};
+  for (int32_t j = 0; j < nt; ++j) dd_add(&bacc, st->terms[j]);
+  double bexact = bacc.hi + bacc.lo;
+  double bb = st->cert_on ? chain_bound(st->sc, 0.0, st->terms, nt) + st->flush_slack * vmax + amb : 0.0;
+  uint16_t bh = dd_to_bf16(bacc);
+  double bv = (double)orc_f32_from_bf16(bh);
+  dd_t sum = {0.0, 0.0};
+  dd_add(&sum, st->ob[f]);
+  dd_add(&sum, bv);
+  double sexact = sum.hi + sum.lo;
+  uint16_t hb = dd_to_bf16(sum);
+  const int bsame = st->dec_cert && st->val_cert && orc_bf16_boundary_distance(bexact) > bb;
+  const int same = bsame && orc_bf16_boundary_distance(sexact) > st->obb[f] + 2.0 * U24 * fabs(sexact);
+  if (!same) st->oc[f] = 0;
+  /* deviation of the implementation's Ō from this one: the carried part,
+   * the rescale and the step's own (bb, plus a bf16 step if its rounding
+   * may differ), then a step of the sum's rounding */
+  double dv = st->odv[f] + st->obb[f] + (bsame ? 0.0 : bb + orc_bf16_ulp(fabs(bexact) + bb));
+  st->odv[f] = (same && st->odv[f] == 0.0) ? 0.0 : dv + orc_bf16_ulp(fabs(sexact) + dv);
+  st->ob[f] = (double)orc_f32_from_bf16(hb);
+  st->obb[f] = 0.0;
+}
+
+/* 3c, streaming: Ō <- cŌ + Σ P̄ V in an fp32 accumulator; in bf16 mode the
+ * accumulator is rounded to bf16 at the rounding points. */
+static void emu_obar_stream(emu_state* st, int32_t f, int32_t nt, double vmax, double amb, int round_here) {
+  const orc_schedule* sc = st->sc;
+  /* a P̄ next to a rounding boundary may take the neighbouring value */
+  st->obb[f] += amb;
+  if (st->cert_on)
+    st->obb[f] += (sc->pv_mxfp4 ? chain_bound_mx(sc, st->ob[f], st->terms, nt)
+                   : sc->pv_fp8 ? chain_bound_fp8(sc, st->ob[f], st->terms, st->texp, nt, -st->ks)
+                                : chain_bound(sc, st->ob[f], st->terms, nt)) +
+                  st->flush_slack * vmax;
+  dd_t acc = {0.0, 0.0};
+  dd_add(&acc, st->ob[f]);
+  for (int32_t j = 0; j < nt; ++j) dd_add(&acc, st->terms[j]);
+  double exact = acc.hi + acc.lo;
+  if (round_here) {
+    uint16_t hb = dd_to_bf16(acc);
+    const int same = st->dec_cert && st->val_cert && orc_bf16_boundary_distance(exact) > st->obb[f];
+    if (!same) st->oc[f] = 0;
+    /* both sides round values at most odv + obb apart */
+    double dv = st->odv[f] + st->obb[f];
+    st->odv[f] = (same && st->odv[f] == 0.0) ? 0.0 : dv + orc_bf16_ulp(fabs(exact) + dv);
+    st->ob[f] = (double)orc_f32_from_bf16(hb);
+    st->obb[f] = 0.0;
+  } else {
+    st->ob[f] = exact;
+    st->obb[f] += 0x1p-52 * fabs(exact);
+    if (sc->obar_fp32) st->oc[f] = 0; /* no bit claim in fp32 mode */
+  }
+}
+
+/* The row's outputs: flags and O = RNE_bf16(fl32(Ō / ℓ)). */
+static void emu_row_out(const emu_state* st, const emu_ctx* x, size_t ro) {
+  const orc_problem* p = st->p;
+  uint8_t fl = 0;
+  if (st->tie) fl |= ORC_ROW_TIE;
+  if (st->tie && p->guard != ORC_GUARD_NONE) fl |= ORC_ROW_GUARD_APPLIED;
+  if (st->l32 == 0.0f) fl |= ORC_ROW_ZERO_DENOM;
+  if (x->flags) x->flags[ro] = fl;
+  if (x->flag_cert) x->flag_cert[ro] = (uint8_t)(st->dec_cert && !st->zero_ambig);
+  if (x->ex) x->ex[ro] = st->exb;
+  if (x->m) x->m[ro] = st->m;
+  if (x->l) x->l[ro] = st->l32;
+  for (int32_t f = 0; f < st->d; ++f) {
+    size_t eo = ro * (size_t)st->d + f;
+    if (x->obar) x->obar[eo] = st->ob[f];
+    if (x->obar_cert) x->obar_cert[eo] = st->oc[f];
+    /* bound on |implementation's Ō - this Ō| (certifying runs; infinite
+     * where the shift decision itself is uncertain) */
+    if (x->obar_dev) x->obar_dev[eo] = !st->cert_on ? NAN : st->dec_cert ? st->odv[f] + st->obb[f] : INFINITY;
+    if (x->o) {
+      float q32 = (float)st->ob[f] / st->l32;
+      x->o[eo] = (double)orc_f32_from_bf16(orc_bf16_from_f32(q32));
+    }
+  }
+}
+
 static void emu_head(void* c, int32_t item) {
   emu_ctx* x = (emu_ctx*)c;
   const orc_problem* p = x->p;
   const orc_schedule* sc = x->s;
   int32_t qh = x->heads ? x->heads[item] : item;
-  int32_t N = p->seqlen, d = p->head_dim;
+  const int32_t N = p->seqlen, d = p->head_dim;
   int32_t i_begin = 0, i_end = N;
   if (x->rows_qh) { /* one listed row; outputs indexed by the list position */
     qh = x->rows_qh[item];
     i_begin = x->rows_i[item];
     i_end = i_begin + 1;
   }
-  int32_t bn = sc->block_n > 0 ? sc->block_n : N;
-  int32_t rn = sc->round_n > 0 ? sc->round_n : bn;
-  const int cert_on = sc->certify != 0;
-  const uint16_t* Q = x->q + q_head_offset(p, qh);
-  const uint16_t* K = x->k + kv_head_offset(p, qh);
-  const uint16_t* V = x->v + kv_head_offset(p, qh);
-  const double alpha = (double)p->alpha;
-  const double log2e = 1.4426950408889634;
-  const double exp_err = sc->exp_rel_err > 0 ? sc->exp_rel_err : 4.0 * U24;
-  /* smallest nonzero result of the kernel's exp */
-  const double under = sc->ftz ? 0x1p-126 : 0x1p-149;
-
-  double* sv = (double*)malloc(sizeof(double) * (size_t)N);  /* exact scores   */
-  double* sb = (double*)malloc(sizeof(double) * (size_t)N);  /* their bounds   */
-  float* tv = (float*)malloc(sizeof(float) * (size_t)N);     /* fp32 logits    */
-  double* pb = (double*)malloc(sizeof(double) * (size_t)bn); /* bf16 P̄ values  */
-  double* ob = (double*)malloc(sizeof(double) * (size_t)d);  /* accumulator Ō  */
-  double* obb = (double*)malloc(sizeof(double) * (size_t)d); /* its error bound */
-  double* odv = (double*)malloc(sizeof(double) * (size_t)d); /* carried deviation */
-  double* pamb = (double*)malloc(sizeof(double) * (size_t)bn); /* P̄ ambiguity  */
-  int* pexp = (int*)malloc(sizeof(int) * (size_t)bn);         /* E4M3 exponents */
-  int* texp = (int*)malloc(sizeof(int) * (size_t)bn);
-  double* pex = (double*)malloc(sizeof(double) * (size_t)bn);  /* exact P̄ (MX) */
-  double* prho = (double*)malloc(sizeof(double) * (size_t)bn); /* their bounds */
-  double* terms = (double*)malloc(sizeof(double) * (size_t)(bn > d ? bn : d));
-  uint8_t* oc = (uint8_t*)malloc((size_t)d);
+  emu_state st;
+  memset(&st, 0, sizeof(st));
+  st.p = p;
+  st.sc = sc;
+  st.Q = x->q + q_head_offset(p, qh);
+  st.K = x->k + kv_head_offset(p, qh);
+  st.V = x->v + kv_head_offset(p, qh);
+  st.N = N;
+  st.d = d;
+  st.bn = sc->block_n > 0 ? sc->block_n : N;
+  st.rn = sc->round_n > 0 ? sc->round_n : st.bn;
+  st.cert_on = sc->certify != 0;
+  st.exp_err = sc->exp_rel_err > 0 ? sc->exp_rel_err : 4.0 * U24;
+  st.under = sc->ftz ? 0x1p-126 : 0x1p-149;
+  const int32_t bn = st.bn;
+  st.sv = (double*)malloc(sizeof(double) * (size_t)N);
+  st.sb = (double*)malloc(sizeof(double) * (size_t)N);
+  st.tv = (float*)malloc(sizeof(float) * (size_t)N);
+  st.pb = (double*)malloc(sizeof(double) * (size_t)bn);
+  st.ob = (double*)malloc(sizeof(double) * (size_t)d);
+  st.obb = (double*)malloc(sizeof(double) * (size_t)d);
+  st.odv = (double*)malloc(sizeof(double) * (size_t)d);
+  st.pamb = (double*)malloc(sizeof(double) * (size_t)bn);
+  st.pexp = (int*)malloc(sizeof(int) * (size_t)bn);
+  st.texp = (int*)malloc(sizeof(int) * (size_t)bn);
+  st.pex = (double*)malloc(sizeof(double) * (size_t)bn);
+  st.prho = (double*)malloc(sizeof(double) * (size_t)bn);
+  st.terms = (double*)malloc(sizeof(double) * (size_t)(bn > d ? bn : d));
+  st.oc = (uint8_t*)malloc((size_t)d);
 
   for (int32_t i = i_begin; i < i_end; ++i) {
-    int32_t n = visible(p, i);
-    const uint16_t* qi = Q + (size_t)i * d;
-    for (int32_t j = 0; j < n; ++j) {
-      if (cert_on) {
-        sv[j] = dot_with_bound(sc, qi, K + (size_t)j * d, d, terms, &sb[j]);
-      } else {
-        sv[j] = dot_bf16(qi, K + (size_t)j * d, d);
-        sb[j] = 0.0;
-      }
-      tv[j] = scaled_logit(p, sv[j]);
-    }
-    float r = -INFINITY, r2 = -INFINITY, m = 0.0f, l32 = 0.0f;
-    int have_m = 0, dec_cert = cert_on, val_cert = cert_on, tie = 0, zero_ambig = 0;
-    double m_err = 0.0; /* bound on |kernel's shift - m| */
-    uint8_t exb = 0;
-    double dmax = 0.0;
-    for (int32_t f = 0; f < d; ++f) {
-      ob[f] = 0.0;
-      obb[f] = 0.0;
-      odv[f] = 0.0;
-      oc[f] = (uint8_t)cert_on;
-    }
+    const int32_t n = visible(p, i);
+    emu_scores(&st, i, n);
+    emu_row_start(&st);
     for (int32_t j0 = 0; j0 < n; j0 += bn) {
-      int32_t j1 = j0 + bn < n ? j0 + bn : n;
-      int32_t nt = j1 - j0;
-      /* 1. running top two of the scaled logits */
-      for (int32_t j = j0; j < j1; ++j) {
-        float t = tv[j];
-        if (t > r) {
-          r2 = r;
-          r = t;
-        } else if (t > r2) {
-          r2 = t;
-        }
-        double e = logit_error(p, sv[j], sb[j]);
-        if (e > dmax) dmax = e;
-      }
-      /* 2. tie decision and shift for this block */
-      tie = tie_test(p, r, r2);
-      if (cert_on && !tie_certain(p, r, r2, dmax)) dec_cert = 0;
-      float mn = guard_shift(p, r, tie);
-      if (tie && p->guard == ORC_GUARD_BETA && r == 0.0f) exb |= ORC_EX_ZERO_MAX_TIE;
-      /* the kernel's shift comes from its own r, within dmax of this one:
-       * m = r, r + eps (slope 1), beta r (slope beta) or 0 (no error) */
-      double slope_m = 1.0;
-      if (tie && p->guard == ORC_GUARD_BETA) slope_m = r > 0.0f ? (double)p->beta : 0.0;
-      const double m_err_new = cert_on ? slope_m * dmax * (1.0 + 4.0 * U24) : 0.0;
-      /* 3a. rescale the running sums by c = exp(m_old - m_new) */
-      if (have_m && mn != m) {
-        if (mn < m) exb |= ORC_EX_SHIFT_DECREASED;
-        double cexact = exp((double)m - (double)mn);
-        /* bound for an fp32 evaluation: the argument (m_old - m_new) log2 e
-         * formed in fp32 and passed to a base-2 exponential of relative
-         * error exp_err, the product c Ō rounded to fp32 */
-        double dm2 = fabs((double)m - (double)mn) * log2e;
-        double rho_c = log(2.0) * (2.0 * U24 * dm2) + exp_err + m_err + m_err_new;
-        /* the same exp flushes a result below the threshold to zero */
-        if (cexact <= under * (1.0 + 4.0 * rho_c)) {
-          if (cexact >= under * (1.0 - 4.0 * rho_c)) zero_ambig = 1;
-          cexact = (cexact < under) ? 0.0 : cexact;
-        }
-        float c32 = (float)cexact;
-        if (isinf(c32)) exb |= ORC_EX_RESCALE_OVERFLOW;
-        for (int32_t f = 0; f < d; ++f) {
-          ob[f] = cexact * ob[f];
-          obb[f] = obb[f] * cexact * (1.0 + rho_c) + fabs(ob[f]) * (rho_c + U24);
-          odv[f] = odv[f] * cexact * (1.0 + rho_c);
-        }
-        l32 = c32 * l32;
-      }
-      m = mn;
-      m_err = m_err_new;
-      have_m = 1;
-      /* FP8 product: the operand scale 2^ks of this block (row scale), or
-       * 2^8 (fixed).  The row scale is an integer decided by floating
-       * point, so it is taken in the implementation's precision (fp32:
-       * floor(fl32(fl32(r - m) log2 e))); ks_amb: the implementation's r may
-       * lie on the other side of an integer step */
-      int ks = 8, ks_amb = 0;
-      if (sc->pv_fp8 == 1) {
-        const float d2 = (r - mn) * (float)1.44269504088896340736;
-        const float fd = floorf(d2);
-        ks = 7 - (int)(fd >= -113.0f ? fd : -113.0f);
-        double slope = p->guard == ORC_GUARD_BETA ? fabs((double)p->beta - 1.0) : 1.0;
-        double slack = 1.01 * slope * log2e * dmax + 8.0 * U24 * log2e * (fabs((double)r) + fabs((double)mn));
-        /* where the shift is r itself, r - m = 0 on both sides */
-        if (mn != r && ((double)d2 - (double)fd <= slack || (double)fd + 1.0 - (double)d2 <= slack)) ks_amb = 1;
-        if (ks_amb && cert_on) val_cert = 0;
-      }
-      const double kscale = ldexp(1.0, ks);
-      /* 3b. P̄ = exp(t - m), rounded to bf16 as the matrix operand */
-      double flush_slack = 0.0; /* total size of P̄ that may flush to zero */
-      for (int32_t j = j0; j < j1; ++j) {
-        double xe = alpha * sv[j] - (double)m;
-        double pbar = exp(xe);
-        /* bound for an fp32 evaluation: the argument s alpha log2 e - m log2 e
-         * formed in fp32 (one fused step) and passed to a base-2
-         * exponential of relative error exp_err */
-        double x2 = xe * log2e;
-        double err_x2 = log2e * alpha * sb[j] * (1.0 + U24) + log2e * m_err +
-                        U24 * (fabs(alpha * sv[j] * log2e) + fabs((double)m * log2e) + fabs(x2));
-        double rho = log(2.0) * err_x2 + exp_err;
-        double pbv;
-        pamb[j - j0] = 0.0;
-        pex[j - j0] = pbar < under ? 0.0 : pbar;
-        prho[j - j0] = rho;
-        if (sc->pv_mxfp4) {
-          pbv = 0.0; /* set below, once the block's scales are known */
-          if (pbar <= under * (1.0 + 4.0 * rho)) {
-            pex[j - j0] = 0.0;
-            if (pbar >= under * (1.0 - 4.0 * rho)) zero_ambig = 1;
-            flush_slack += 2.0 * pbar;
-          }
-        } else if (pbar <= under * (1.0 + 4.0 * rho)) {
-          /* at or below the flush threshold: the kernel gives 0 or a tiny
-           * value; take 0 and count the whole size as uncertainty */
-          pbv = 0.0;
-          if (pbar >= under * (1.0 - 4.0 * rho)) zero_ambig = 1;
-          flush_slack += 2.0 * pbar;
-        } else if (sc->pv_fp8) {
-          /* FP8 operand: P̄ * 2^ks rounded to E4M3, scaled back (exact) */
-          const double ps = pbar * kscale;
-          pbv = orc_e4m3_round(ps) / kscale;
-          if (cert_on && orc_e4m3_boundary_distance(ps) <= (rho + 2.0 * U24) * ps) {
-            val_cert = 0;
-            pamb[j - j0] = orc_e4m3_ulp(ps * (1.0 + rho)) / kscale; /* a neighbour */
-          }
-          /* another scale changes the rounding only among the subnormals */
-          if (cert_on && ks_amb && ps < 0x1p-5) pamb[j - j0] = fmax(pamb[j - j0], 0x1p-9 / kscale * 2.0);
-        } else {
-          pbv = (double)orc_f32_from_bf16(orc_bf16_from_f64(pbar));
-          /* a P̄ next to a rounding boundary may take the neighbouring bf16
-           * value in the kernel: that one step, times |V|, joins each
-           * element's bound below, so only elements that stay clear of a
-           * boundary by it are certified */
-          if (cert_on && orc_bf16_boundary_distance(pbar) <= (rho + 2.0 * U24) * pbar)
-            pamb[j - j0] = orc_bf16_ulp(pbar * (1.0 + rho));
-        }
-        pexp[j - j0] = pbv != 0.0 ? e4m3_exponent(pbv * kscale) : 0;
-        if (pbv == 1.0) {
-          if (tie) exb |= ORC_EX_PBAR_ONE_TIED;
-          if (!tie) exb |= ORC_EX_PBAR_ONE_PRE_TIE;
-        }
-        pb[j - j0] = pbv;
-        /* 4. fp32 denominator: sum of the fp32 P̄ (sequential order here) */
-        float p32 = (pbar < under) ? 0.0f : (float)pbar;
-        l32 = l32 + p32;
-      }
-      if (sc->pv_mxfp4) {
-        /* MXFP4 operand: the step's keys in two blocks of 32 consecutive
-         * keys (OCP MX: a block is 32 consecutive elements along the
-         * contraction), each with the scale 2^(floor(log2 amax) - 2) of
-         * its largest P̄ */
-        for (int h = 0; h < 2; ++h) {
-          double amax = 0.0, rmax = 0.0;
-          for (int32_t j = j0; j < j1; ++j)
-            if (((j - j0) >> 5) == h) {
-              amax = fmax(amax, pex[j - j0]);
-              rmax = fmax(rmax, prho[j - j0]);
-            }
-          int (*sbf)(double) = sc->pv_mxfp4 == 2 ? orc_mx_scale_byte_ceil : orc_mx_scale_byte;
-          const int sbyte = sbf(amax);
-          const double X = ldexp(1.0, sbyte - 127);
-          /* the kernel's amax is within rmax of this one: its scale may
-           * be the neighbouring power of two */
-          const int s_amb = cert_on && amax > 0.0 &&
-                            (sbf(amax * (1.0 - rmax - 2.0 * U24)) != sbyte ||
-                             sbf(amax * (1.0 + rmax + 2.0 * U24)) != sbyte);
-          if (s_amb) val_cert = 0;
-          for (int32_t j = j0; j < j1; ++j) {
-            if (((j - j0) >> 5) != h) continue;
-            const double y = pex[j - j0] / X;
-            const double pbv = orc_e2m1_round(y) * X;
-            if (cert_on && pex[j - j0] > 0.0 &&
-                orc_e2m1_boundary_distance(y) <= (prho[j - j0] + 2.0 * U24) * y) {
-              val_cert = 0;
-              pamb[j - j0] = orc_e2m1_spacing(y * (1.0 + prho[j - j0])) * X;
-            }
-            if (s_amb) pamb[j - j0] = fmax(pamb[j - j0], 4.0 * X);
-            if (pbv == 1.0) {
-              if (tie) exb |= ORC_EX_PBAR_ONE_TIED;
-              if (!tie) exb |= ORC_EX_PBAR_ONE_PRE_TIE;
-            }
-            pb[j - j0] = pbv;
-          }
-        }
-      }
-      /* 3c. Ō <- cŌ + sum P̄_bf16 V in an fp32 accumulator; in bf16 mode the
-       * accumulator is rounded to bf16 after every round_n keys and after the
-       * row's last block */
-      const int round_here = !sc->obar_fp32 && ((j1 % rn) == 0 || j1 == n);
+      const int32_t j1 = j0 + bn < n ? j0 + bn : n;
+      emu_top_two(&st, j0, j1);                      /* 1 */
+      double m_err_new;
+      const float mn = emu_shift(&st, &m_err_new);   /* 2 */
+      emu_rescale(&st, mn, m_err_new);               /* 3a */
+      emu_fp8_scale(&st);
+      emu_pbar(&st, j0, j1);                         /* 3b, 4 */
+      if (sc->pv_mxfp4) emu_mx_pbar(&st, j0, j1);
+      /* 3c: rounded after every round_n keys and after the row's last step */
+      const int round_here = !sc->obar_fp32 && ((j1 % st.rn) == 0 || j1 == n);
       for (int32_t f = 0; f < d; ++f) {
-        double vmax = 0.0, amb = 0.0;
-        double vx[2] = {1.0, 1.0}; /* MXFP4: V's scales over the step's keys */
-        if (sc->pv_mxfp4) {
-          /* per feature, over every key of the block that exists: V's
-           * operand is one for all query rows, so a row's causal mask
-           * cannot enter its scale */
-          const int32_t jt = j0 + bn < N ? j0 + bn : N;
-          double va[2] = {0.0, 0.0};
-          for (int32_t j = j0; j < jt; ++j) {
-            const int h = (j - j0) >> 5;
-            va[h] = fmax(va[h], fabs((double)orc_f32_from_bf16(V[(size_t)j * d + f])));
-          }
-          for (int h = 0; h < 2; ++h)
-            vx[h] = ldexp(1.0, (sc->pv_mxfp4 == 2 ? orc_mx_scale_byte_ceil(va[h]) : orc_mx_scale_byte(va[h])) - 127);
-        }
-        for (int32_t j = j0; j < j1; ++j) {
-          double vv = (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
-          if (sc->pv_mxfp4) {
-            const double X = vx[(j - j0) >> 5];
-            vv = orc_e2m1_round(vv / X) * X;
-          }
-          if (sc->pv_fp8) {
-            vv = orc_e4m3_round(vv); /* the FP8 V operand */
-            texp[j - j0] = vv != 0.0 ? pexp[j - j0] + e4m3_exponent(vv) : 0;
-          }
-          terms[j - j0] = pb[j - j0] * vv; /* exact: 8-bit x 8-bit mantissas */
-          vmax = fmax(vmax, fabs(vv));
-          amb += pamb[j - j0] * fabs(vv);
-        }
-        if (sc->block_bf16 && !sc->obar_fp32) {
-          /* the block's own product sum, rounded to bf16, then added to the
-           * rescaled Ō and rounded again (every block is a rounding point);
-           * a P̄ next to a rounding boundary may take the neighbouring value,
-           * which moves this block's sum by up to amb */
-          dd_t bacc = {0.0, 0.0};
-          for (int32_t j = 0; j < nt; ++j) dd_add(&bacc, terms[j]);
-          double bexact = bacc.hi + bacc.lo;
-          double bb = cert_on ? chain_bound(sc, 0.0, terms, nt) + flush_slack * vmax + amb : 0.0;
-          uint16_t bh = dd_to_bf16(bacc);
-          double bv = (double)orc_f32_from_bf16(bh);
-          dd_t sum = {0.0, 0.0};
-          dd_add(&sum, ob[f]);
-          dd_add(&sum, bv);
-          double sexact = sum.hi + sum.lo;
-          uint16_t hb = dd_to_bf16(sum);
-          const int bsame = dec_cert && val_cert && orc_bf16_boundary_distance(bexact) > bb;
-          const int same = bsame && orc_bf16_boundary_distance(sexact) > obb[f] + 2.0 * U24 * fabs(sexact);
-          if (!same) oc[f] = 0;
-          /* deviation of the kernel's Ō from this one: the carried part, the
-           * rescale and the block's own (bb, plus a bf16 step if its
-           * rounding may differ), then a step of the sum's rounding */
-          double dv = odv[f] + obb[f] + (bsame ? 0.0 : bb + orc_bf16_ulp(fabs(bexact) + bb));
-          odv[f] = (same && odv[f] == 0.0) ? 0.0 : dv + orc_bf16_ulp(fabs(sexact) + dv);
-          ob[f] = (double)orc_f32_from_bf16(hb);
-          obb[f] = 0.0;
-          continue;
-        }
-        /* a P̄ next to a rounding boundary may take the neighbouring value */
-        obb[f] += amb;
-        if (cert_on)
-          obb[f] += (sc->pv_mxfp4 ? chain_bound_mx(sc, ob[f], terms, nt)
-                     : sc->pv_fp8 ? chain_bound_fp8(sc, ob[f], terms, texp, nt, -ks)
-                                  : chain_bound(sc, ob[f], terms, nt)) +
-                    flush_slack * vmax;
-        dd_t acc = {0.0, 0.0};
-        dd_add(&acc, ob[f]);
-        for (int32_t j = 0; j < nt; ++j) dd_add(&acc, terms[j]);
-        double exact = acc.hi + acc.lo;
-        if (round_here) {
-          uint16_t hb = dd_to_bf16(acc);
-          const int same = dec_cert && val_cert && orc_bf16_boundary_distance(exact) > obb[f];
-          if (!same) oc[f] = 0;
-          /* both sides round values at most odv + obb apart */
-          double dv = odv[f] + obb[f];
-          odv[f] = (same && odv[f] == 0.0) ? 0.0 : dv + orc_bf16_ulp(fabs(exact) + dv);
-          ob[f] = (double)orc_f32_from_bf16(hb);
-          obb[f] = 0.0;
-        } else {
-          ob[f] = exact;
-          obb[f] += 0x1p-52 * fabs(exact);
-          if (sc->obar_fp32) oc[f] = 0; /* no bit claim in fp32 mode */
-        }
+        double vmax, amb;
+        emu_terms(&st, f, j0, j1, &vmax, &amb);
+        if (sc->block_bf16 && !sc->obar_fp32)
+          emu_obar_block_bf16(&st, f, j1 - j0, vmax, amb);
+        else
+          emu_obar_stream(&st, f, j1 - j0, vmax, amb, round_here);
       }
     }
-    /* end of row: flags and O = RNE_bf16(fl32(Ō / ℓ)) */
-    size_t ro = x->rows_qh ? (size_t)item : (size_t)qh * N + i;
-    uint8_t fl = 0;
-    if (tie) fl |= ORC_ROW_TIE;
-    if (tie && p->guard != ORC_GUARD_NONE) fl |= ORC_ROW_GUARD_APPLIED;
-    if (l32 == 0.0f) fl |= ORC_ROW_ZERO_DENOM;
-    if (x->flags) x->flags[ro] = fl;
-    if (x->flag_cert) x->flag_cert[ro] = (uint8_t)(dec_cert && !zero_ambig);
-    if (x->ex) x->ex[ro] = exb;
-    if (x->m) x->m[ro] = m;
-    if (x->l) x->l[ro] = l32;
-    for (int32_t f = 0; f < d; ++f) {
-      size_t eo = ro * (size_t)d + f;
-      if (x->obar) x->obar[eo] = ob[f];
-      if (x->obar_cert) x->obar_cert[eo] = oc[f];
-      /* bound on |kernel Ō - this Ō| (certifying runs; infinite where the
-       * shift decision itself is uncertain) */
-      if (x->obar_dev) x->obar_dev[eo] = !cert_on ? NAN : dec_cert ? odv[f] + obb[f] : INFINITY;
-      if (x->o) {
-        float q32 = (float)ob[f] / l32;
-        x->o[eo] = (double)orc_f32_from_bf16(orc_bf16_from_f32(q32));
-      }
-    }
+    emu_row_out(&st, x, x->rows_qh ? (size_t)item : (size_t)qh * N + i);
   }
-  free(sv);
-  free(sb);
-  free(tv);
-  free(pb);
-  free(ob);
-  free(obb);
-  free(odv);
-  free(pamb);
-  free(pexp);
-  free(texp);
-  free(pex);
-  free(prho);
-  free(terms);
-  free(oc);
+  free(st.sv);
+  free(st.sb);
+  free(st.tv);
+  free(st.pb);
+  free(st.ob);
+  free(st.obb);
+  free(st.odv);
+  free(st.pamb);
+  free(st.pexp);
+  free(st.texp);
+  free(st.pex);
+  free(st.prho);
+  free(st.terms);
+  free(st.oc);
 }
 
 int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
