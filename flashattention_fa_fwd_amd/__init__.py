@@ -6,7 +6,7 @@ used only to own device memory and to name the current HIP stream.  There is
 no fallback: if the library is missing or fails to load, every call raises.
 
 The functions carry the C ABI's names: attn_fwd, attn_bwd (and its stages
-attn_bwd_dq / attn_bwd_dkdv), attn_schedule,
+attn_bwd_dq / attn_bwd_dkdv), attn_bwd_workspace_bytes, attn_schedule,
 attn_strerror, attn_abi_version.
 """
 from __future__ import annotations
@@ -82,6 +82,8 @@ def lib():
         L.attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for n in ("attn_schedule", "attn_fwd", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq"):
             getattr(L, n).restype = ctypes.c_int
+        L.attn_bwd_workspace_bytes.argtypes = [pp]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -92,6 +94,12 @@ def attn_abi_version() -> int:
 
 def attn_strerror(code: int) -> str:
     return lib().attn_strerror(int(code)).decode()
+
+
+def attn_bwd_workspace_bytes(p: "Params") -> int:
+    """Device scratch attn_bwd needs for these params (always 0 for valid
+    params; (size_t)-1 for params attn_bwd would reject)."""
+    return int(lib().attn_bwd_workspace_bytes(ctypes.byref(_set_strides(p))))
 
 
 def make_params(batch, heads_q, heads_kv, seqlen, head_dim, *, causal=True, guard="beta",

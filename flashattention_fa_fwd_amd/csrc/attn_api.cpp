@@ -160,6 +160,10 @@ const char* attn_strerror(int code) {
   }
 }
 
+size_t attn_bwd_workspace_bytes(const attn_params* p) {
+  return check_params(p) == ATTN_OK ? 0 : (size_t)-1;
+}
+
 int attn_schedule(const attn_params* p, int32_t* block_m, int32_t* block_n, int32_t* round_n,
                   int32_t* chunk, int32_t* block_bf16, int32_t* pv_chunk) {
   const int rc = check_params(p);

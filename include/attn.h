@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 11
+#define ATTN_ABI_VERSION 12
 
 /* attn_params.flags */
 #define ATTN_CAUSAL 0x1u          /* key j visible to query i iff j <= i       */
@@ -227,6 +227,18 @@ int attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* 
 int attn_bwd_dkdv(const attn_params* p, const void* q, const void* k, const void* v,
                   const void* dout, const float* row_m, const float* row_l,
                   const float* delta, void* dk, void* dv, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes -- the device scratch that attn_bwd needs for
+ * these params: 0 for every valid parameter set.  The gradient dQ = dS K
+ * ([R] "Core idea", equations, paper Eq. 1-2) is usually accumulated from
+ * many key blocks into an fp32 workspace; here the dQ kernel finishes each
+ * row's dQ in registers and every output element is written once, so no
+ * workspace exists.  The query lets a caller that sizes a workspace before
+ * the call learn that it needs none.  Returns (size_t)-1 for params that
+ * attn_bwd would reject (the same checks).
+ */
+size_t attn_bwd_workspace_bytes(const attn_params* p);
 
 /*
  * attn_schedule -- the rounding schedule attn_fwd uses for these params, so

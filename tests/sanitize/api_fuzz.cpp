@@ -117,6 +117,8 @@ int main() {
     for (void*& x : ptr) x = (rng() % 40 == 0) ? nullptr : (rng() % 40 == 0 ? (void*)(buf + 8) : P);
     int32_t bm, bn, rn, ch, bb, pc;
     int rc = attn_schedule(&p, &bm, &bn, &rn, &ch, &bb, &pc);
+    // the workspace query agrees with the parameter checks
+    if ((attn_bwd_workspace_bytes(&p) == 0) != (rc == 0)) std::abort();
     rc |= attn_fwd(&p, ptr[0], ptr[1], ptr[2], ptr[3], (float*)ptr[4], (float*)ptr[5], (uint8_t*)ptr[6],
                    rng() % 2 ? ptr[7] : nullptr, rng() % 2 ? (float*)ptr[8] : nullptr, nullptr);
     rc |= attn_bwd(&p, ptr[0], ptr[1], ptr[2], ptr[3], ptr[4], (const float*)ptr[5], (const float*)ptr[6],

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert fa.attn_abi_version() == 11
+    assert fa.attn_abi_version() == 12
     for code in (0, -1, -2, -3, -4, -6):
         assert fa.attn_strerror(code) and fa.attn_strerror(code) != "unknown error code"
     assert fa.attn_strerror(-99) == "unknown error code"
@@ -202,3 +202,15 @@ def test_stride_rules(L):
         setattr(p, f"{name}_stride", st)
         assert L.attn_schedule(ctypes.byref(p), None, None, None, None, None, None) == code, name
         assert _fwd(L, p) == code, name
+
+
+def test_bwd_workspace_query(L):
+    """The backward needs no workspace: 0 for valid params, (size_t)-1 for
+    params the backward would reject."""
+    import ctypes as C
+    for args, kw in (((1, 1, 1, 64, 64), {}), ((2, 8, 2, 1000, 128), dict(causal=False)),
+                     ((16, 12, 12, 1024, 64), dict(delta="dp_p"))):
+        assert fa.attn_bwd_workspace_bytes(fa.make_params(*args, **kw)) == 0
+    bad = fa.make_params(1, 3, 2, 64, 64)   # heads_q not a multiple of heads_kv
+    assert fa.attn_bwd_workspace_bytes(bad) == C.c_size_t(-1).value
+    assert L.attn_bwd_workspace_bytes(None) == C.c_size_t(-1).value
