@@ -33,9 +33,10 @@ HBM_PEAK_GBS = 8000.0
 # bytes: x2.0; WRITE_SIZE all of them: x1.0).  Summary and commands:
 # profiles/bwd_dkdv_gpt2s_hbm_traffic.md.  The figures hold only for the
 # sources of that kernel they were taken on (SHA-256 over the files that
-# define it) and for the workload they were taken on; otherwise the report
-# says null.
-KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd.hip", "attn_device.h", "attn_internal.h")}
+# define it and the build script that sets its compiler flags) and for the
+# workload they were taken on; otherwise the report says null.
+KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd_dkdv.hip", "attn_bwd_common.h", "attn_device.h", "attn_internal.h",
+                               "../build_lib.py")}
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
         "workload": "gpt2s",
