@@ -40,8 +40,8 @@ KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd_dkdv.hip", "attn_bwd_common.h", "attn_d
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
         "workload": "gpt2s",
-        "sources_sha256": "83b0e9ab459f5a44224d1fe3f0cf7e3295034542d0577b5e8ff5750aca786db5",
-        "fetch_kib": 65244.0, "write_kib": 51394.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "1b132e7cb0abe65f4b94171860a637b167af1fe6e03a41e564ed8d758760de78",
+        "fetch_kib": 64478.75, "write_kib": 50637.375, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
