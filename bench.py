@@ -40,8 +40,8 @@ KERNEL_SOURCES = {"bwd_dkdv": ("attn_bwd_dkdv.hip", "attn_bwd_common.h", "attn_d
 MEASURED_TRAFFIC = {
     "bwd_dkdv": {
         "workload": "gpt2s",
-        "sources_sha256": "1b132e7cb0abe65f4b94171860a637b167af1fe6e03a41e564ed8d758760de78",
-        "fetch_kib": 64478.75, "write_kib": 50637.375, "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "b0c728845f4f53e0c53359e1be3bea77e8b317f2184290bdead1477d8ab2cc1b",
+        "fetch_kib": 64693.25, "write_kib": 49368.25, "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 

@@ -52,19 +52,21 @@ template <int D>
 __device__ __forceinline__ void dkdv_load(const BwdArgs& a, int hq, int q0, int b, int wave,
                                           int lane, int tid, uint16_t* Qs, uint16_t* dOs,
                                           float (&stat)[3]) {
-  // statistics first: refilling their registers may wait for the previous
-  // step's loads, which must not include the copies issued below.  Rows
-  // past the end read the last row; bwd_stats_store neutralises them.
+  // the copies first: issued after the statistics' loads, their address
+  // arithmetic can be given a register that one of those loads is still
+  // filling and then waits for it (wave 0 stalled on that every step;
+  // 5 % of the kernel at GPT-2 Small)
+  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.q + a.lq.head(b, hq), a.N, a.lq.sn, D), q0, a.lq.sn,
+                                  wave, lane, Qs);
+  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.dout + a.ldo.head(b, hq), a.N, a.ldo.sn, D), q0,
+                                  a.ldo.sn, wave, lane, dOs);
+  // rows past the end read the last row; bwd_stats_store neutralises them
   if (tid < kBwdBlockM) {
     const size_t r = (size_t)(b * a.Hq + hq) * a.N + min(q0 + tid, a.N - 1);
     stat[0] = a.row_m[r];
     stat[1] = a.row_l[r];
     stat[2] = a.delta[r];
   }
-  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.q + a.lq.head(b, hq), a.N, a.lq.sn, D), q0, a.lq.sn,
-                                  wave, lane, Qs);
-  dma_tile<D, kBwdBlockM, kWaves>(head_desc(a.dout + a.ldo.head(b, hq), a.N, a.ldo.sn, D), q0,
-                                  a.ldo.sn, wave, lane, dOs);
 }
 
 // Write a step's row statistics to its stage (threads 0..31, rows q0 + tid).
@@ -83,7 +85,7 @@ __device__ __forceinline__ void dkdv_step(
     const BwdArgs& a, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const int (&qa_off)[D / kMfmaK],
     const int (&ka_off)[D / kMfmaK], const int (&tb_off)[D / 32][2], const uint16_t* __restrict__ qs,
     const uint16_t* __restrict__ gs, const uint16_t* __restrict__ ks,
-    const uint16_t* __restrict__ vs, const float* __restrict__ slse,
+    const uint16_t* __restrict__ vs, const bf16x8 (&vfr)[D / kMfmaK], const float* __restrict__ slse,
     const float* __restrict__ sdel, uint16_t* __restrict__ qs_next,
     uint16_t* __restrict__ gs_next, bool more, int hq_next, int q0_next, int b, int wave,
     int lane, int tid, float (&stat)[3], int q0, int wk0, int key, int half) {
@@ -106,7 +108,11 @@ __device__ __forceinline__ void dkdv_step(
       const bf16x8 kb = *(const bf16x8*)(&ks[ka_off[t]]);
       const bf16x8 qa = *(const bf16x8*)(&qs[qa_off[t]]);
       sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, sv, 0, 0, 0);
-      const bf16x8 vb = *(const bf16x8*)(&vs[ka_off[t]]);
+      bf16x8 vb;
+      if constexpr (D == 128)
+        vb = vfr[t];
+      else
+        vb = *(const bf16x8*)(&vs[ka_off[t]]);
       const bf16x8 ga = *(const bf16x8*)(&gs[qa_off[t]]);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, dp, 0, 0, 0);
     }
@@ -245,6 +251,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void bwd_dkdv_kernel(Bwd
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if (tid < BM) bwd_stats_store(stat, pf.q0, tid, N, slse[0], sdel[0]);
   pf.next(qstart, N);
+  // d = 128 (one workgroup a CU, registers to spare): the wave's V
+  // fragments are read once and kept in registers; d = 64 keeps them in LDS
+  // (holding them spills at three workgroups a CU)
+  bf16x8 vfr[NT];
+  if constexpr (D == 128) {
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vfr[t] = *(const bf16x8*)(&Vs[ka_off[t]]);
+  }
 
   for (int s = 0; s < total; ++s) {
     const int cur = s & 1;
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void bwd_dkdv_kernel(Bwd
     __syncthreads();
     const bool more = s + 1 < total;
     const int q0_next = pf.q0;
-    dkdv_step<D, CAUSAL>(a, dk, dv, qa_off, ka_off, tb_off, Qs[cur], dOs[cur], Ks, Vs, slse[cur],
+    dkdv_step<D, CAUSAL>(a, dk, dv, qa_off, ka_off, tb_off, Qs[cur], dOs[cur], Ks, Vs, vfr, slse[cur],
                          sdel[cur], Qs[cur ^ 1], dOs[cur ^ 1], more, hq0 + pf.h, pf.q0, b, wave,
                          lane, tid, stat, q0, wk0, key, half);
     pf.next(qstart, N);
