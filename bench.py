@@ -6,8 +6,12 @@ One step = attn_fwd + attn_bwd (every stage of the path) over one batch of
 synthetic inputs that are resident in device memory before timing starts.
 The headline value is measured with cold caches (a 1 GiB buffer written
 before each timed step, outside the timed region); the warm, back-to-back
-figure is reported beside it.  Prints one JSON line (see the keys below).  The CPU oracle's FP64
-forward+backward of the same workload is timed on the host as a baseline.
+figure is reported beside it.  Inside the timed steps the backward is
+called as its two stages (the work of attn_bwd), so that HIP events between
+the launches time each kernel there; the roofline object uses the longest
+kernel's mean duration over those steps.  Prints one JSON line (see the keys
+below).  The CPU oracle's FP64 forward+backward of the same workload is timed
+on the host as a baseline.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload gpt2s]
 """
@@ -133,24 +137,33 @@ def main():
     # last-level cache hold together), so every step reads its inputs from
     # HBM; HIP events on the launch stream bracket the step alone (the fill
     # is outside them).  W untimed warm-up steps first; synchronised on both
-    # sides.  ms_per_step = mean over the K steps.
+    # sides.  ms_per_step = mean over the K steps.  The backward is called as
+    # its two stages (the work of attn_bwd: dQ, then dK/dV) so that events
+    # between the launches give each kernel's duration inside the step.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    delta = bout["delta"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         flush.fill_(i & 0xFF)
         evs[i][0].record(stream)
         fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw)
         evs[i][1].record(stream)
-        fa.attn_bwd(q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], out=bout, **kw)
+        fa.attn_bwd_dq(p, q, k, v, fout["o"], do, fout["row_m"], fout["row_l"], bout["dq"], delta)
         evs[i][2].record(stream)
+        fa.attn_bwd_dkdv(p, q, k, v, do, fout["row_m"], fout["row_l"], delta, bout["dk"], bout["dv"])
+        evs[i][3].record(stream)
     torch.cuda.synchronize()
-    cold_steps = [e[0].elapsed_time(e[2]) for e in evs]
+    cold_steps = [e[0].elapsed_time(e[3]) for e in evs]
     ms_step = float(np.mean(cold_steps))
     cold_fwd = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
-    cold_bwd = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    cold_bwd = float(np.median([e[1].elapsed_time(e[3]) for e in evs]))
+    # each kernel's mean duration over the timed steps
+    in_step = {"attn_fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+               "bwd_dq": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+               "bwd_dkdv": float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))}
     del flush
     print(f"[bench] {args.steps} cold steps: mean {ms_step:.4f} ms/step (median {np.median(cold_steps):.4f}); "
           f"fwd {cold_fwd:.4f}, bwd {cold_bwd:.4f} ms (medians)", file=sys.stderr, flush=True)
@@ -164,10 +177,9 @@ def main():
                    "zero_denominator_rows": int(((fl & 2) != 0).sum().item()),
                    "guard_applied_rows": int(((fl & 4) != 0).sum().item())}
 
-    # ---- per-kernel durations: each of the step's launches (attn_bwd is its
-    # two stages, dQ then dK/dV) repeated back to back between HIP events on
-    # the launch stream, as a kernel trace averages them
-    delta = bout["delta"]
+    # ---- per-kernel durations beside them: each of the step's launches
+    # repeated back to back between HIP events on the launch stream (the
+    # clock under one kernel repeated differs from the mix of the step)
     n_rep = max(20, args.steps)
     ms_fwd = timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fout, **kw), n_rep, 3)
     ms_dq = timed(lambda: fa.attn_bwd_dq(p, q, k, v, fout["o"], do, fout["row_m"], fout["row_l"],
@@ -193,7 +205,9 @@ def main():
         variants[name] = round(timed(lambda: fa.attn_fwd(q, k, v, obar_fp32=args.obar_fp32, out=fo3, **vkw, **kw),
                                      n_rep, 3), 5)
     print(f"[bench] forward variants (ms): {variants}", file=sys.stderr, flush=True)
-    print(f"[bench] fwd {ms_fwd:.4f} ms, bwd_dq {ms_dq:.4f}, bwd_dkdv {ms_dkdv:.4f}; "
+    print(f"[bench] in the timed steps (mean): fwd {in_step['attn_fwd']:.4f} ms, bwd_dq {in_step['bwd_dq']:.4f}, "
+          f"bwd_dkdv {in_step['bwd_dkdv']:.4f}", file=sys.stderr, flush=True)
+    print(f"[bench] back to back: fwd {ms_fwd:.4f} ms, bwd_dq {ms_dq:.4f}, bwd_dkdv {ms_dkdv:.4f}; "
           f"fwd with guard={other}: {ms_fwd_other:.4f}; bwd with delta=rowsum(dP*P): "
           f"{ms_bwd_dp:.4f}", file=sys.stderr, flush=True)
 
@@ -213,10 +227,12 @@ def main():
     fl_bwd = 5 * fl_gemm
     fl_step = fl_fwd + fl_bwd
     value = fl_step / (ms_step * 1e-3) / 1e12
+    # the roofline kernel: the longest of the step's kernels, at its mean
+    # duration inside the timed steps
     kernels = {
-        "attn_fwd": (ms_fwd, fl_fwd),
-        "bwd_dkdv": (ms_dkdv, 4 * fl_gemm),
-        "bwd_dq": (ms_dq, 3 * fl_gemm),
+        "attn_fwd": (in_step["attn_fwd"], fl_fwd),
+        "bwd_dkdv": (in_step["bwd_dkdv"], 4 * fl_gemm),
+        "bwd_dq": (in_step["bwd_dq"], 3 * fl_gemm),
     }
     dom = max(kernels, key=lambda n: kernels[n][0])
     dms, dfl = kernels[dom]
@@ -242,10 +258,12 @@ def main():
             "flops_per_step": fl_step,
         },
         "pct_of_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
-        "fwd_tflops": round(fl_fwd / (ms_fwd * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(fl_bwd / ((ms_dkdv + ms_dq) * 1e-3) / 1e12, 2),
-        "kernel_ms": {"attn_fwd": round(ms_fwd, 5), "bwd_dq": round(ms_dq, 5),
-                      "bwd_dkdv": round(ms_dkdv, 5)},
+        "fwd_tflops": round(fl_fwd / (in_step["attn_fwd"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(fl_bwd / ((in_step["bwd_dkdv"] + in_step["bwd_dq"]) * 1e-3) / 1e12, 2),
+        "kernel_ms": {n: round(t, 5) for n, t in in_step.items()},
+        "kernel_ms_timing": "mean over the K timed steps, HIP events between the step's launches",
+        "kernel_ms_back_to_back": {"attn_fwd": round(ms_fwd, 5), "bwd_dq": round(ms_dq, 5),
+                                   "bwd_dkdv": round(ms_dkdv, 5)},
         "fwd_ms_other_guard": {other: round(ms_fwd_other, 5)},
         "fwd_ms_variants": variants,
         "bwd_ms_delta": {"rowsum(dO*O)": round(ms_dq + ms_dkdv, 5), "rowsum(dP*P)": round(ms_bwd_dp, 5)},
