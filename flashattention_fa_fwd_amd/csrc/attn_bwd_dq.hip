@@ -203,33 +203,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* __restrict__ Qh = a.q + a.lq.head(b, hq);
   const uint16_t* __restrict__ dOh = a.dout + a.ldo.head(b, hq);
 
-  // Q and dO rows of this lane's row as B operands: [16t + 8*half + 0..7]
+  // Every load of the prologue is issued before the first wait (one memory
+  // round trip instead of three): the row's Q and dO fragments (B operands:
+  // [16t + 8*half + 0..7]), its O (for delta), m and ℓ, and the first K/V
+  // tile.  Rows past the end read the last row; nothing of theirs is stored.
+  const int qc = min(qrow, N - 1);
   bf16x8 qf[NT], gf[NT];
+  uint4 orw[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    uint4 qr = make_uint4(0, 0, 0, 0), gr = make_uint4(0, 0, 0, 0);
-    if (qrow < N) {
-      qr = *(const uint4*)(Qh + (size_t)qrow * a.lq.sn + 16 * t + 8 * half);
-      gr = *(const uint4*)(dOh + (size_t)qrow * a.ldo.sn + 16 * t + 8 * half);
-    }
-    qf[t] = __builtin_bit_cast(bf16x8, qr);
-    gf[t] = __builtin_bit_cast(bf16x8, gr);
+    qf[t] = __builtin_bit_cast(bf16x8, *(const uint4*)(Qh + (size_t)qc * a.lq.sn + 16 * t + 8 * half));
+    gf[t] = __builtin_bit_cast(bf16x8, *(const uint4*)(dOh + (size_t)qc * a.ldo.sn + 16 * t + 8 * half));
+    if constexpr (!DELTA_DP)
+      orw[t] = *(const uint4*)(a.o + a.lo.head(b, hq) + (size_t)qc * a.lo.sn + 16 * t + 8 * half);
   }
+  const size_t ridx = (size_t)(b * a.Hq + hq) * N + qc;
+  const float mrow = a.row_m[ridx], lrow = a.row_l[ridx];
+  dma_tile<D, BN, kWaves>(rk, 0, a.lk.sn, wave, lane, Ks[0]);
+  dma_tile<D, BN, kWaves>(rv, 0, a.lv.sn, wave, lane, Vs[0]);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  const float lse2 = row_lse2(mrow, lrow);
   // delta = rowsum(dO∘O) of this lane's row: its 32 features here, the
   // other 32 (d = 64) in lane ^ 32 (every lane returns the full sum)
-  float lse2 = 0.0f, del = 0.0f;
-  if (qrow < N) {
-    const size_t ridx = (size_t)(b * a.Hq + hq) * N + qrow;
-    lse2 = row_lse2(a.row_m[ridx], a.row_l[ridx]);
-  }
+  float del = 0.0f;
   if constexpr (!DELTA_DP) {
     float part = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      uint4 orow = make_uint4(0, 0, 0, 0);
-      if (qrow < N) orow = *(const uint4*)(a.o + a.lo.head(b, hq) + (size_t)qrow * a.lo.sn + 16 * t + 8 * half);
       const uint4 grow = __builtin_bit_cast(uint4, gf[t]);
-      const uint32_t ow[4] = {orow.x, orow.y, orow.z, orow.w};
+      const uint32_t ow[4] = {orw[t].x, orw[t].y, orw[t].z, orw[t].w};
       const uint32_t gw[4] = {grow.x, grow.y, grow.z, grow.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -265,10 +267,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const bool wave_live = q0 < N;
 
   if constexpr (DELTA_DP) {
-    // first sweep: delta = rowsum(dP∘P) over the keys the row sees
-    dma_tile<D, BN, kWaves>(rk, 0, a.lk.sn, wave, lane, Ks[0]);
-    dma_tile<D, BN, kWaves>(rv, 0, a.lv.sn, wave, lane, Vs[0]);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // first sweep: delta = rowsum(dP∘P) over the keys the row sees (its
+    // first tile was copied with the prologue's loads)
     float acc = 0.0f;
     for (int j0 = 0; j0 < kend; j0 += BN) {
       const int cur = (j0 / BN) & 1;
@@ -283,11 +283,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     if (qrow < N && half == 0) a.delta[(size_t)(b * a.Hq + hq) * N + qrow] = del;
     // every wave is done with the last tile before stage 0 is refilled
     __syncthreads();
+    dma_tile<D, BN, kWaves>(rk, 0, a.lk.sn, wave, lane, Ks[0]);
+    dma_tile<D, BN, kWaves>(rv, 0, a.lv.sn, wave, lane, Vs[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
-
-  dma_tile<D, BN, kWaves>(rk, 0, a.lk.sn, wave, lane, Ks[0]);
-  dma_tile<D, BN, kWaves>(rv, 0, a.lv.sn, wave, lane, Vs[0]);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   float dsum = 0.0f;
   for (int j0 = 0; j0 < kend; j0 += BN) {
