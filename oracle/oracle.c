@@ -260,6 +260,16 @@ static int check_problem(const orc_problem* p) {
   return 0;
 }
 
+/* A head list (NULL: every head) names only heads of the problem: each index
+ * in [0, count), count = batch * heads. */
+static int heads_valid(const int32_t* heads, int32_t n, int32_t count) {
+  if (!heads) return 1;
+  if (n < 0) return 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (heads[i] < 0 || heads[i] >= count) return 0;
+  return 1;
+}
+
 typedef struct {
   void (*fn)(void* ctx, int32_t item);
   void* ctx;
@@ -518,11 +528,12 @@ static void fwd64_head(void* c, int32_t item) {
     }
     double* orow = x->o ? x->o + q_head_offset(p, qh) + (size_t)i * d : NULL;
     if (orow) {
-      for (int32_t f = 0; f < d; ++f) {
-        double acc = 0.0;
-        for (int32_t j = 0; j < n; ++j) acc += t[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
-        orow[f] = acc / z;
-      }
+      /* orow[f] = sum_j t[j] V[j][f], each sum in key order j = 0, 1, ...
+       * (the loop runs over V's rows so that it reads them in memory order) */
+      for (int32_t f = 0; f < d; ++f) orow[f] = 0.0;
+      for (int32_t j = 0; j < n; ++j)
+        for (int32_t f = 0; f < d; ++f) orow[f] += t[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+      for (int32_t f = 0; f < d; ++f) orow[f] /= z;
     }
     if (x->lse) x->lse[(size_t)qh * N + i] = mx + log(z);
   }
@@ -535,6 +546,7 @@ int orc_fwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   int rc = check_problem(p);
   if (rc) return rc;
   if (!q || !k || !v) return -1;
+  if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
   fwd64_ctx c = {p, q, k, v, heads, o, lse};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
   run_pool(fwd64_head, &c, n, nthreads);
@@ -599,12 +611,13 @@ static void bwd64_kvhead(void* c, int32_t item) {
         z += P[j];
       }
       for (int32_t j = 0; j < n; ++j) P[j] /= z;
+      /* orow[f] = sum_j P[j] V[j][f] in key order, read row by row */
       for (int32_t f = 0; f < d; ++f) {
-        double acc = 0.0;
-        for (int32_t j = 0; j < n; ++j) acc += P[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
-        orow[f] = acc;
+        orow[f] = 0.0;
         dorow[f] = (double)orc_f32_from_bf16(dO[(size_t)i * d + f]);
       }
+      for (int32_t j = 0; j < n; ++j)
+        for (int32_t f = 0; f < d; ++f) orow[f] += P[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
       size_t rbase = q_head_offset(p, qh) + (size_t)i * d;
       const double* odelta = x->o_in ? x->o_in + rbase : orow;
       double delta = 0.0;
@@ -654,6 +667,7 @@ int orc_bwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   int rc = check_problem(p);
   if (rc) return rc;
   if (!q || !k || !v || !dout) return -1;
+  if (!heads_valid(kv_heads, nkv, p->batch * p->heads_kv)) return -2;
   bwd64_ctx c = {p, q, k, v, dout, kv_heads, o, delta, dq, dk, dv, NULL, 0};
   int32_t n = kv_heads ? nkv : p->batch * p->heads_kv;
   run_pool(bwd64_kvhead, &c, n, nthreads);
@@ -671,6 +685,7 @@ int orc_bwd_emu(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   int rc = check_problem(p);
   if (rc) return rc;
   if (!q || !k || !v || !dout) return -1;
+  if (!heads_valid(kv_heads, nkv, p->batch * p->heads_kv)) return -2;
   bwd64_ctx c = {p, q, k, v, dout, kv_heads, NULL, delta, dq, dk, dv, o_in, round_ops};
   int32_t n = kv_heads ? nkv : p->batch * p->heads_kv;
   run_pool(bwd64_kvhead, &c, n, nthreads);
@@ -841,12 +856,13 @@ static void bwdrow_item(void* c, int32_t item) {
   for (int32_t j = 0; j < n; ++j) P[j] /= z;
   double* orow = x->o + (size_t)item * d;
   double* dqrow = x->dq + (size_t)item * d;
+  /* orow[f] = sum_j P[j] V[j][f] in key order, read row by row */
   for (int32_t f = 0; f < d; ++f) {
-    double acc = 0.0;
-    for (int32_t j = 0; j < n; ++j) acc += P[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
-    orow[f] = acc;
+    orow[f] = 0.0;
     dqrow[f] = 0.0;
   }
+  for (int32_t j = 0; j < n; ++j)
+    for (int32_t f = 0; f < d; ++f) orow[f] += P[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
   const double* odelta = x->o_in ? x->o_in + (size_t)item * d : orow;
   double delta = 0.0;
   for (int32_t f = 0; f < d; ++f) delta += (double)orc_f32_from_bf16(doi[f]) * odelta[f];
@@ -1122,6 +1138,7 @@ int orc_row_stats(const orc_problem* p, const orc_schedule* s, const uint16_t* q
   int rc = check_problem(p);
   if (rc) return rc;
   if (!q || !k) return -1;
+  if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
   stats_ctx c = {p, s, q, k, heads, r, r2, m, flags, flag_cert};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
   run_pool(stats_head, &c, n, nthreads);
@@ -1159,12 +1176,13 @@ static void obar_head(void* c, int32_t item) {
       e[j] = exp(alpha * dot_bf16(Q + (size_t)i * d, K + (size_t)j * d, d) - mi);
       l += e[j];
     }
-    if (x->obar)
-      for (int32_t f = 0; f < d; ++f) {
-        double acc = 0.0;
-        for (int32_t j = 0; j < n; ++j) acc += e[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
-        x->obar[ro * d + f] = acc;
-      }
+    if (x->obar) {
+      /* sum_j e[j] V[j][f] in key order, read row by row */
+      double* ob = x->obar + ro * d;
+      for (int32_t f = 0; f < d; ++f) ob[f] = 0.0;
+      for (int32_t j = 0; j < n; ++j)
+        for (int32_t f = 0; f < d; ++f) ob[f] += e[j] * (double)orc_f32_from_bf16(V[(size_t)j * d + f]);
+    }
     if (x->l) x->l[ro] = l;
   }
   free(e);
@@ -1176,6 +1194,7 @@ int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   int rc = check_problem(p);
   if (rc) return rc;
   if (!q || !k || !v || !m) return -1;
+  if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
   obar_ctx c = {p, q, k, v, m, heads, obar, l};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
   run_pool(obar_head, &c, n, nthreads);
@@ -1705,6 +1724,7 @@ int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
   if (!s || !q || !k || !v) return -1;
   if (s->block_n < 0 || s->round_n < 0) return -4;
   if (s->block_n > 0 && s->round_n > 0 && s->round_n % s->block_n != 0) return -4;
+  if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
   emu_ctx c = {p, s, q, k, v, heads, obar, o, obar_cert, obar_dev, m, l, flags, flag_cert, ex, NULL, NULL};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
   run_pool(emu_head, &c, n, nthreads);

@@ -364,3 +364,28 @@ def test_emulation_rows_match_heads(orc):
     r = orc.fwd_emu_rows(p, sc, x["q"], x["k"], x["v"], np.zeros(5, np.int32), rows)
     assert np.array_equal(r["o"], e["o"][0, 0, rows])
     assert np.array_equal(r["m"], e["m"][0, 0, rows]) and np.array_equal(r["flags"], e["flags"][0, 0, rows])
+
+
+def test_head_lists_outside_the_problem_are_rejected(orc):
+    """Every oracle function that takes a list of heads refuses an index
+    outside [0, batch*heads) before reading anything (no partial output)."""
+    p, q, k, v, do = _rand_problem(orc, 91, B=1, Hq=2, Hkv=1, N=16)
+    sched = orc.Schedule()
+    m = np.zeros((1, 2, 16), np.float32)
+    calls = [
+        lambda h: orc.fwd_f64(p, q, k, v, heads=h),
+        lambda h: orc.fwd_emu(p, sched, q, k, v, heads=h),
+        lambda h: orc.row_stats(p, q, k, sched, heads=h),
+        lambda h: orc.obar_f64(p, q, k, v, m, heads=h),
+    ]
+    for call in calls:
+        call([1])  # the last query head: accepted
+        for bad in ([2], [-1], [0, 2]):
+            with pytest.raises(ValueError):
+                call(bad)
+    for call in (lambda h: orc.bwd_f64(p, q, k, v, do, kv_heads=h),
+                 lambda h: orc.bwd_emu(p, q, k, v, do, kv_heads=h)):
+        call([0])
+        for bad in ([1], [-1]):
+            with pytest.raises(ValueError):
+                call(bad)
