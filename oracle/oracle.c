@@ -307,6 +307,34 @@ static void run_pool(void (*fn)(void*, int32_t), void* ctx, int32_t nitems, int3
   free(args);
 }
 
+/* Work items over (listed head, block of rows).  Rows of a head are
+ * independent in the forward functions below, so a call with few heads (a
+ * single full-size head, say) splits each head into blocks of rows to keep
+ * every thread busy; each row's arithmetic is the same either way. */
+typedef struct {
+  int32_t nblk, rows; /* blocks per head, rows per block */
+} row_split;
+
+static row_split split_rows(int32_t nheads, int32_t N, int32_t nthreads) {
+  row_split r = {1, N};
+  if (nthreads > 1 && nheads > 0 && nheads < 4 * nthreads) {
+    int32_t want = (8 * nthreads + nheads - 1) / nheads;
+    if (want > N) want = N;
+    r.rows = (N + want - 1) / want;
+    r.nblk = (N + r.rows - 1) / r.rows;
+  }
+  return r;
+}
+
+/* Head and row range of work item `item`. */
+static void split_item(row_split r, int32_t item, const int32_t* heads, int32_t N,
+                       int32_t* qh, int32_t* i_begin, int32_t* i_end) {
+  int32_t h = item / r.nblk, b = item % r.nblk;
+  *qh = heads ? heads[h] : h;
+  *i_begin = b * r.rows;
+  *i_end = *i_begin + r.rows < N ? *i_begin + r.rows : N;
+}
+
 /* Pointers to the [N][d] slabs of query head (b, h) and of its KV head.
  * Grouped-query mapping: query head h reads KV head h / (heads_q/heads_kv). */
 static size_t q_head_offset(const orc_problem* p, int32_t qhead) {
@@ -502,19 +530,21 @@ typedef struct {
   const uint16_t *q, *k, *v;
   const int32_t* heads;
   double *o, *lse;
+  row_split rs;
 } fwd64_ctx;
 
 static void fwd64_head(void* c, int32_t item) {
   fwd64_ctx* x = (fwd64_ctx*)c;
   const orc_problem* p = x->p;
-  int32_t qh = x->heads ? x->heads[item] : item;
   int32_t N = p->seqlen, d = p->head_dim;
+  int32_t qh, i_begin, i_end;
+  split_item(x->rs, item, x->heads, N, &qh, &i_begin, &i_end);
   const uint16_t* Q = x->q + q_head_offset(p, qh);
   const uint16_t* K = x->k + kv_head_offset(p, qh);
   const uint16_t* V = x->v + kv_head_offset(p, qh);
   double* t = (double*)malloc(sizeof(double) * (size_t)N);
   double alpha = (double)p->alpha;
-  for (int32_t i = 0; i < N; ++i) {
+  for (int32_t i = i_begin; i < i_end; ++i) {
     int32_t n = visible(p, i);
     double mx = -INFINITY;
     for (int32_t j = 0; j < n; ++j) {
@@ -547,9 +577,9 @@ int orc_fwd_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   if (rc) return rc;
   if (!q || !k || !v) return -1;
   if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
-  fwd64_ctx c = {p, q, k, v, heads, o, lse};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
-  run_pool(fwd64_head, &c, n, nthreads);
+  fwd64_ctx c = {p, q, k, v, heads, o, lse, split_rows(n, p->seqlen, nthreads)};
+  run_pool(fwd64_head, &c, n * c.rs.nblk, nthreads);
   return 0;
 }
 
@@ -1077,6 +1107,7 @@ typedef struct {
   const int32_t* heads;
   float *r, *r2, *m;
   uint8_t *flags, *cert;
+  row_split rs;
 } stats_ctx;
 
 /* Bound on |t_kernel - t| for one key: alpha times the score bound, plus the
@@ -1096,12 +1127,13 @@ static int tie_certain(const orc_problem* p, float r, float r2, double dmax) {
 static void stats_head(void* c, int32_t item) {
   stats_ctx* x = (stats_ctx*)c;
   const orc_problem* p = x->p;
-  int32_t qh = x->heads ? x->heads[item] : item;
   int32_t N = p->seqlen, d = p->head_dim;
+  int32_t qh, i_begin, i_end;
+  split_item(x->rs, item, x->heads, N, &qh, &i_begin, &i_end);
   const uint16_t* Q = x->q + q_head_offset(p, qh);
   const uint16_t* K = x->k + kv_head_offset(p, qh);
   double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
-  for (int32_t i = 0; i < N; ++i) {
+  for (int32_t i = i_begin; i < i_end; ++i) {
     int32_t n = visible(p, i);
     float r = -INFINITY, r2 = -INFINITY;
     double dmax = 0.0;
@@ -1139,9 +1171,9 @@ int orc_row_stats(const orc_problem* p, const orc_schedule* s, const uint16_t* q
   if (rc) return rc;
   if (!q || !k) return -1;
   if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
-  stats_ctx c = {p, s, q, k, heads, r, r2, m, flags, flag_cert};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
-  run_pool(stats_head, &c, n, nthreads);
+  stats_ctx c = {p, s, q, k, heads, r, r2, m, flags, flag_cert, split_rows(n, p->seqlen, nthreads)};
+  run_pool(stats_head, &c, n * c.rs.nblk, nthreads);
   return 0;
 }
 
@@ -1155,19 +1187,21 @@ typedef struct {
   const float* m;
   const int32_t* heads;
   double *obar, *l;
+  row_split rs;
 } obar_ctx;
 
 static void obar_head(void* c, int32_t item) {
   obar_ctx* x = (obar_ctx*)c;
   const orc_problem* p = x->p;
-  int32_t qh = x->heads ? x->heads[item] : item;
   int32_t N = p->seqlen, d = p->head_dim;
+  int32_t qh, i_begin, i_end;
+  split_item(x->rs, item, x->heads, N, &qh, &i_begin, &i_end);
   const uint16_t* Q = x->q + q_head_offset(p, qh);
   const uint16_t* K = x->k + kv_head_offset(p, qh);
   const uint16_t* V = x->v + kv_head_offset(p, qh);
   double* e = (double*)malloc(sizeof(double) * (size_t)N);
   double alpha = (double)p->alpha;
-  for (int32_t i = 0; i < N; ++i) {
+  for (int32_t i = i_begin; i < i_end; ++i) {
     int32_t n = visible(p, i);
     size_t ro = (size_t)qh * N + i;
     double mi = (double)x->m[ro];
@@ -1195,9 +1229,9 @@ int orc_obar_f64(const orc_problem* p, const uint16_t* q, const uint16_t* k,
   if (rc) return rc;
   if (!q || !k || !v || !m) return -1;
   if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
-  obar_ctx c = {p, q, k, v, m, heads, obar, l};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
-  run_pool(obar_head, &c, n, nthreads);
+  obar_ctx c = {p, q, k, v, m, heads, obar, l, split_rows(n, p->seqlen, nthreads)};
+  run_pool(obar_head, &c, n * c.rs.nblk, nthreads);
   return 0;
 }
 
@@ -1239,6 +1273,7 @@ typedef struct {
   float *m, *l;
   uint8_t *flags, *flag_cert, *ex;
   const int32_t *rows_qh, *rows_i; /* row list mode: item = one (head, row) */
+  row_split rs;                     /* otherwise: item = (head, block of rows) */
 } emu_ctx;
 
 /* Working state of the emulation of one head: buffers for the row's scores,
@@ -1634,13 +1669,14 @@ static void emu_head(void* c, int32_t item) {
   emu_ctx* x = (emu_ctx*)c;
   const orc_problem* p = x->p;
   const orc_schedule* sc = x->s;
-  int32_t qh = x->heads ? x->heads[item] : item;
   const int32_t N = p->seqlen, d = p->head_dim;
-  int32_t i_begin = 0, i_end = N;
+  int32_t qh, i_begin, i_end;
   if (x->rows_qh) { /* one listed row; outputs indexed by the list position */
     qh = x->rows_qh[item];
     i_begin = x->rows_i[item];
     i_end = i_begin + 1;
+  } else {
+    split_item(x->rs, item, x->heads, N, &qh, &i_begin, &i_end);
   }
   emu_state st;
   memset(&st, 0, sizeof(st));
@@ -1725,9 +1761,10 @@ int orc_fwd_emu(const orc_problem* p, const orc_schedule* s, const uint16_t* q,
   if (s->block_n < 0 || s->round_n < 0) return -4;
   if (s->block_n > 0 && s->round_n > 0 && s->round_n % s->block_n != 0) return -4;
   if (!heads_valid(heads, nheads, p->batch * p->heads_q)) return -2;
-  emu_ctx c = {p, s, q, k, v, heads, obar, o, obar_cert, obar_dev, m, l, flags, flag_cert, ex, NULL, NULL};
   int32_t n = heads ? nheads : p->batch * p->heads_q;
-  run_pool(emu_head, &c, n, nthreads);
+  emu_ctx c = {p, s, q, k, v, heads, obar, o, obar_cert, obar_dev, m, l, flags, flag_cert, ex, NULL, NULL,
+               split_rows(n, p->seqlen, nthreads)};
+  run_pool(emu_head, &c, n * c.rs.nblk, nthreads);
   return 0;
 }
 
@@ -1746,7 +1783,7 @@ int orc_fwd_emu_rows(const orc_problem* p, const orc_schedule* s, const uint16_t
   }
   orc_schedule s2 = *s;
   s2.certify = 0;
-  emu_ctx c = {p, &s2, q, k, v, NULL, NULL, o, NULL, NULL, m, l, flags, NULL, NULL, qheads, rows};
+  emu_ctx c = {p, &s2, q, k, v, NULL, NULL, o, NULL, NULL, m, l, flags, NULL, NULL, qheads, rows, {1, 0}};
   run_pool(emu_head, &c, n, nthreads);
   return 0;
 }
