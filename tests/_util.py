@@ -79,18 +79,22 @@ def schedule(p: orc.Problem, obar_fp32=False, certify=True, sched="stream", pv_f
 
 
 def check_o(o_gpu, o64, o_emu=None, obar_fp32=True, rows=None):
-    """O against FP64: max rel <= 1e-2 and mean rel <= 2e-3; in bf16-Ō mode
-    the mean bound is max(2e-3, emulation's own mean + 2e-4).  Returns the
-    numbers for the report."""
+    """O against FP64: max rel <= 1e-2 and mean rel <= 2e-3.  In bf16-Ō mode
+    the method's own roundings of Ō (one per 512 keys and one at the row's
+    end) set a floor, taken from the emulation of those roundings on the same
+    rows: the bounds are max(1e-2, 1.25 x the emulation's max) and max(2e-3,
+    the emulation's mean + 2e-4).  The max floor binds only on long rows
+    (N = 16384: about 1.1e-2).  Returns the numbers for the report."""
     sel = (slice(None),) if rows is None else (rows,)
     mx, mean = rel_errors(o_gpu[sel], o64[sel])
     emx = emean = float("nan")
-    bound = MEAN_REL
+    bound, bmax = MEAN_REL, MAX_REL
     if o_emu is not None:
         emx, emean = rel_errors(o_emu[sel], o64[sel])
         if not obar_fp32:
             bound = max(MEAN_REL, emean + MEAN_EXCESS)
-    assert mx <= MAX_REL, ("max rel", mx, "emulation", emx)
+            bmax = max(MAX_REL, 1.25 * emx)
+    assert mx <= bmax, ("max rel", mx, "bound", bmax, "emulation", emx)
     assert mean <= bound, ("mean rel", mean, "bound", bound, "emulation", emean)
     return dict(o_max_rel=f"{mx:.2e}", o_mean_rel=f"{mean:.2e}", emu_max_rel=f"{emx:.2e}",
                 emu_mean_rel=f"{emean:.2e}")
