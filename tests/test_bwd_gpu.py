@@ -88,6 +88,8 @@ SHAPES = [  # B, Hq, Hkv, N, d, causal
     (1, 1, 1, 1, 64, True), (1, 2, 1, 63, 64, True), (2, 4, 2, 65, 64, False),
     (1, 2, 2, 200, 64, True), (1, 4, 1, 257, 128, True), (2, 2, 1, 129, 128, False),
     (1, 1, 1, 384, 64, False), (1, 8, 2, 96, 128, True),
+    # groups of 8 query heads on a KV head (dK, dV summed over all 8)
+    (1, 8, 1, 160, 64, True), (2, 16, 2, 100, 128, False),
 ]
 
 

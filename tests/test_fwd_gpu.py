@@ -74,6 +74,8 @@ SHAPES = [  # B, Hq, Hkv, N, d, causal
     (1, 1, 1, 1, 64, True), (1, 2, 1, 63, 64, True), (2, 4, 2, 65, 64, False),
     (1, 2, 2, 200, 64, True), (1, 4, 1, 257, 128, True), (2, 2, 1, 129, 128, False),
     (1, 1, 1, 384, 64, False), (1, 8, 2, 96, 128, True),
+    # groups of 8 query heads on a KV head
+    (1, 8, 1, 160, 64, True), (2, 16, 2, 100, 128, False),
     # past the 512-key rounding point of the streaming bf16 Ō (rounded after
     # keys 512 and 1024 and at the row's end)
     (1, 2, 1, 1100, 64, True), (1, 2, 2, 1100, 128, False), (1, 1, 1, 1537, 64, False),
