@@ -69,3 +69,40 @@ def test_parameters(case, shape):
     out.update(_check("delta", b["delta"].cpu().numpy(), ref["delta"], fl["delta"]))
     report(f"params {_id(case)} {shape}", ties=int((flags & 1).sum()), guarded=int(((flags & 4) != 0).sum()),
            flag_cert=f"{fc.mean():.3f}", obar_cert=f"{cert.mean():.3f}", **out)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["d64-causal", "d128-full"])
+@pytest.mark.parametrize("guard", ["beta", "eps"])
+def test_negative_row_maxima(guard, shape):
+    """Every logit moved down by about 30 (feature d-1 reserved: Q = 1 there
+    and K = bf16(-30/alpha) for every key), so every row maximum is negative:
+    the β guard's tie rows take the shift 0 instead of β·r, the ε guard's
+    r + ε as before.  Flags and certified bf16 Ō bit for bit, O against FP64."""
+    B, Hq, Hkv, N, d, causal = shape
+    wl = W.Workload("negmax", B, Hq, Hkv, N, d, causal, 1.0, 1.0, "const", -0.3, 0.0, 0.1, 0.0, 8.0,
+                    131 + d)
+    x = W.make_custom(wl)
+    one = W.to_bf16_bits(np.ones(1, np.float32))[0]
+    low = W.to_bf16_bits(np.full(1, -30.0 / wl.alpha, np.float32))[0]
+    x["q"][..., d - 1] = one
+    x["k"][..., d - 1] = low
+    p = orc.Problem(B, Hq, Hkv, N, d, causal, GUARD[guard])
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    f = fa.attn_fwd(q, k, v, causal=causal, guard=guard, return_obar=True, return_row_max=True)
+    torch.cuda.synchronize()
+    assert (f["row_max"].cpu().numpy() < 0).all()
+    e = orc.fwd_emu(p, schedule(p), x["q"], x["k"], x["v"], nthreads=threads())
+    o64, _ = orc.fwd_f64(p, x["q"], x["k"], x["v"], nthreads=threads())
+    flags = f["row_flags"].cpu().numpy()
+    fc = e["flag_cert"].astype(bool)
+    assert np.array_equal(flags[fc], e["flags"][fc])
+    tie = (flags & 1) != 0
+    assert tie.sum() > 0
+    m = f["row_m"].cpu().numpy()
+    if guard == "beta":
+        assert (m[tie] == 0.0).all()  # shift 0 for a non-positive repeated maximum
+    out = check_o(f32(f["o"]), o64, e["o"], False)
+    cert = e["obar_cert"].astype(bool)
+    assert np.array_equal(bits(f["obar"])[cert], orc.bf16_from_f32(e["obar"].astype(np.float32))[cert])
+    report(f"negative maxima {guard} {shape}", ties=int(tie.sum()), flag_cert=f"{fc.mean():.3f}",
+           obar_cert=f"{cert.mean():.3f}", **out)
